@@ -1,0 +1,301 @@
+"""Float64 CPU oracle of the frame-wise Gated DeltaNet (GDN) recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers or constant tables); both sides receive
+the same seeded inputs and nothing else.
+
+What it computes, and where it comes from
+-----------------------------------------
+The method is defined on the paper.rainbus.top summary of "SANA-WM: Efficient
+Minute-Scale World Modeling with Hybrid Linear Diffusion Transformer":
+
+* section 前置知识, "Gated DeltaNet (GDN)": a D x D state S_t per head with a
+  decay gate gamma_t and a delta-rule correction, updated as
+  S_t = S_{t-1} M_t + U_t;
+* section 方法步骤详情, module 2 ("Memory-Efficient Long-Context"): the scan
+  runs once per latent frame with
+      M_t = gamma_t I - K^_t beta_t K^_t^T,   U_t = V_t beta_t K^_t^T,
+      O_t = S_t Q^_t,
+  and keys are scaled by 1/sqrt(D S) (the sentence is cut off after that);
+* section 技术新颖性, point 1: this is token-wise GDN generalised to one update
+  per whole latent frame; the key scaling keeps ||M_t||_2 <= gamma_t <= 1; for
+  context-parallel training a transition composite C_p and an input composite
+  H_p are combined by a prefix sum that reproduces the single-device result
+  exactly.
+
+Notation (the pages' column form): K^_t, Q^_t are Dk x N (one column per
+token of frame t), V_t and O_t are Dv x N, beta_t is the N x N diagonal of the
+per-token gates, gamma_t is one scalar per frame and head, S is Dv x Dk.
+
+Readings of what the pages leave open (each also listed in the design notes):
+
+* D in 1/sqrt(D S) is the key head dimension Dk and S the number of tokens per
+  frame N, so the default key scale is 1/sqrt(Dk * N);
+* keys and queries arrive already normalised: the oracle applies only the key
+  scale, never a normalisation (the hats are read as "normalised upstream");
+* the decay multiplies only the identity, literally gamma_t I - K^ beta K^^T;
+* the output of frame t uses S_t, the state after frame t's own update;
+* S_0 = 0 unless an initial state is given;
+* ``erase`` is a test-only switch (M_t = gamma_t I - erase * A_t) used to pin
+  the oracle against gated linear attention; the library has no such switch.
+
+Array layout (shared with the library's interface): q, k: [B, L, H, Dk];
+v, o: [B, L, H, Dv]; gamma: [B, T, H]; beta: [B, L, H]; states:
+[B, H, Dv, Dk]; token l = t * N + n (frame-major).  All arithmetic is float64.
+
+Parity is pinned for every function here by the tests in
+``tests/test_oracle_pins.py`` (brute force, closed forms, invariants, finite
+differences); none of them is "parity unpinned".
+"""
+
+import numpy as np
+
+__all__ = [
+    "default_key_scale",
+    "frame_terms",
+    "forward",
+    "step",
+    "backward",
+    "composite_forward",
+]
+
+
+def default_key_scale(dk, n):
+    """Key scale 1/sqrt(D*S) of the GDN recurrence (summary page, 方法步骤详情
+    module 2, and 技术新颖性 point 1), read with D = Dk and S = N."""
+    return 1.0 / np.sqrt(float(dk) * float(n))
+
+
+def _scale(key_scale, dk, n):
+    return float(key_scale) if key_scale else default_key_scale(dk, n)
+
+
+def _shapes(q, k, v, gamma, beta, n):
+    B, L, H, Dk = k.shape
+    Dv = v.shape[-1]
+    if L % n:
+        raise ValueError("sequence length %d is not a whole number of frames of %d" % (L, n))
+    T = L // n
+    if q.shape != (B, L, H, Dk) or v.shape[:3] != (B, L, H):
+        raise ValueError("q/k/v shapes disagree")
+    if gamma.shape != (B, T, H) or beta.shape != (B, L, H):
+        raise ValueError("gate shapes disagree")
+    return B, L, H, Dk, Dv, T
+
+
+def _frame_cols(x, b, t, h, n):
+    """Columns of one frame for one head: x[b, t*N:(t+1)*N, h, :] as D x N."""
+    return np.asarray(x[b, t * n:(t + 1) * n, h, :], dtype=np.float64).T
+
+
+def frame_terms(k, v, beta, n, key_scale=0.0):
+    """Per-frame Gram A_t = K^_t beta_t K^_t^T and write U_t = V_t beta_t K^_t^T
+    (summary page, 方法步骤详情 module 2).
+
+    Returns A [B, H, T, Dk, Dk] and U [B, H, T, Dv, Dk], float64.
+    """
+    B, L, H, Dk = k.shape
+    Dv = v.shape[-1]
+    T = L // n
+    s = _scale(key_scale, Dk, n)
+    A = np.zeros((B, H, T, Dk, Dk))
+    U = np.zeros((B, H, T, Dv, Dk))
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                Kh = s * _frame_cols(k, b, t, h, n)          # K^_t, Dk x N
+                Vt = _frame_cols(v, b, t, h, n)              # V_t,  Dv x N
+                bt = np.asarray(beta[b, t * n:(t + 1) * n, h], dtype=np.float64)
+                # X diag(beta) scales column j of X by beta_j.
+                A[b, h, t] = (Kh * bt) @ Kh.T
+                U[b, h, t] = (Vt * bt) @ Kh.T
+    return A, U
+
+
+def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, erase=1.0,
+            keep=False):
+    """Whole-sequence frame-wise GDN.
+
+    For every (batch, head), in frame order t = 1..T:
+        M_t = gamma_t I - erase * K^_t beta_t K^_t^T
+        U_t = V_t beta_t K^_t^T
+        S_t = S_{t-1} M_t + U_t
+        O_t = S_t Q^_t
+    (summary page: 前置知识 "Gated DeltaNet" for S_t = S_{t-1} M_t + U_t, and
+    方法步骤详情 module 2 for M_t, U_t, O_t and the key scale).
+
+    Returns (o [B, L, H, Dv], state_out [B, H, Dv, Dk]); with keep=True also a
+    dict of the per-frame intermediates A_t, U_t, S_t ([B, H, T, D, D]).
+    """
+    B, L, H, Dk, Dv, T = _shapes(q, k, v, gamma, beta, n)
+    s = _scale(key_scale, Dk, n)
+    o = np.zeros((B, L, H, Dv))
+    state_out = np.zeros((B, H, Dv, Dk))
+    if keep:
+        kept = {"A": np.zeros((B, H, T, Dk, Dk)), "U": np.zeros((B, H, T, Dv, Dk)),
+                "S": np.zeros((B, H, T, Dv, Dk))}
+    eye = np.eye(Dk)
+    for b in range(B):
+        for h in range(H):
+            S = (np.zeros((Dv, Dk)) if state_in is None
+                 else np.asarray(state_in[b, h], dtype=np.float64).copy())
+            for t in range(T):
+                Kh = s * _frame_cols(k, b, t, h, n)
+                Qh = _frame_cols(q, b, t, h, n)
+                Vt = _frame_cols(v, b, t, h, n)
+                bt = np.asarray(beta[b, t * n:(t + 1) * n, h], dtype=np.float64)
+                A = (Kh * bt) @ Kh.T
+                U = (Vt * bt) @ Kh.T
+                M = float(gamma[b, t, h]) * eye - erase * A
+                S = S @ M + U
+                o[b, t * n:(t + 1) * n, h, :] = (S @ Qh).T
+                if keep:
+                    kept["A"][b, h, t] = A
+                    kept["U"][b, h, t] = U
+                    kept["S"][b, h, t] = S
+            state_out[b, h] = S
+    if keep:
+        return o, state_out, kept
+    return o, state_out
+
+
+def step(q, k, v, gamma, beta, state, key_scale=0.0):
+    """Streaming step: advance the carried state by one latent frame.
+
+    The autoregressive / streaming variant carries the GDN state across calls
+    (CSDN explainer section 六 stage 4; summary page limitations). One call is
+    the forward recurrence with T = 1 starting from ``state``: q, k, v are
+    [B, N, H, D], gamma [B, 1, H], beta [B, N, H].  Returns (o, new_state).
+    """
+    n = k.shape[1]
+    return forward(q, k, v, gamma, beta, n, state_in=state, key_scale=key_scale)
+
+
+def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None,
+             key_scale=0.0, erase=1.0):
+    """Reverse-mode gradients of ``forward`` (the pages give no backward; this
+    is the chain rule applied to the module-2 recurrence, step by step).
+
+    With G_t = dL/dS_t (all paths through S_t):
+        G_T      = dO_T Q^_T^T + dS_T(external)
+        G_t      = dO_t Q^_t^T + G_{t+1} M_{t+1}^T
+        dQ^_t    = S_t^T dO_t
+        dM_t     = S_{t-1}^T G_t,    dgamma_t = tr(dM_t),   dA_t = -erase dM_t
+        dV_t     = G_t K^_t beta_t
+        dK^_t    = G_t^T V_t beta_t + (dA_t + dA_t^T) K^_t beta_t
+        dbeta_tn = v_tn^T G_t k^_tn + k^_tn^T dA_t k^_tn
+        dK_t     = s dK^_t              (K^ = s K)
+        dS_0     = G_1 M_1^T
+    Returns dict with dq, dk, dv ([B, L, H, D]), dgamma [B, T, H],
+    dbeta [B, L, H], dstate_in [B, H, Dv, Dk].
+    """
+    B, L, H, Dk, Dv, T = _shapes(q, k, v, gamma, beta, n)
+    s = _scale(key_scale, Dk, n)
+    dq = np.zeros((B, L, H, Dk))
+    dk = np.zeros((B, L, H, Dk))
+    dv = np.zeros((B, L, H, Dv))
+    dgamma = np.zeros((B, T, H))
+    dbeta = np.zeros((B, L, H))
+    dstate_in = np.zeros((B, H, Dv, Dk))
+    eye = np.eye(Dk)
+    for b in range(B):
+        for h in range(H):
+            # Forward sweep, keeping every state and transition.
+            S = (np.zeros((Dv, Dk)) if state_in is None
+                 else np.asarray(state_in[b, h], dtype=np.float64).copy())
+            states = [S]
+            trans = []
+            for t in range(T):
+                Kh = s * _frame_cols(k, b, t, h, n)
+                Vt = _frame_cols(v, b, t, h, n)
+                bt = np.asarray(beta[b, t * n:(t + 1) * n, h], dtype=np.float64)
+                M = float(gamma[b, t, h]) * eye - erase * ((Kh * bt) @ Kh.T)
+                S = S @ M + (Vt * bt) @ Kh.T
+                states.append(S)
+                trans.append(M)
+            # Reverse sweep.
+            carry = (np.zeros((Dv, Dk)) if d_state_out is None
+                     else np.asarray(d_state_out[b, h], dtype=np.float64).copy())
+            for t in reversed(range(T)):
+                sl = slice(t * n, (t + 1) * n)
+                Kh = s * _frame_cols(k, b, t, h, n)
+                Qh = _frame_cols(q, b, t, h, n)
+                Vt = _frame_cols(v, b, t, h, n)
+                dOt = _frame_cols(d_o, b, t, h, n)
+                bt = np.asarray(beta[b, sl, h], dtype=np.float64)
+                S_prev, S_t, M = states[t], states[t + 1], trans[t]
+                G = dOt @ Qh.T + carry                       # dL/dS_t
+                dq[b, sl, h, :] = (S_t.T @ dOt).T
+                dM = S_prev.T @ G
+                dgamma[b, t, h] = np.trace(dM)
+                dA = -erase * dM
+                dv[b, sl, h, :] = ((G @ Kh) * bt).T
+                dKh = (G.T @ Vt) * bt + ((dA + dA.T) @ Kh) * bt
+                dk[b, sl, h, :] = (s * dKh).T
+                dbeta[b, sl, h] = (np.einsum("in,ij,jn->n", Vt, G, Kh)
+                                   + np.einsum("in,ij,jn->n", Kh, dA, Kh))
+                carry = G @ M.T
+            dstate_in[b, h] = carry
+    return {"dq": dq, "dk": dk, "dv": dv, "dgamma": dgamma, "dbeta": dbeta,
+            "dstate_in": dstate_in}
+
+
+def composite_forward(q, k, v, gamma, beta, n, chunk, state_in=None,
+                      key_scale=0.0, erase=1.0):
+    """Forward through the transition / input composites of the context-
+    parallel scheme (summary page, 技术新颖性 point 1).
+
+    Frames are cut into consecutive chunks of ``chunk`` frames (the last one
+    may be shorter), standing in for the devices of context parallelism.
+    Each chunk p first builds, independently of every other chunk,
+        C_p = M_{first} ... M_{last}                 (transition composite)
+        H_p : H <- H M_t + U_t from H = 0           (input composite)
+    so that S_out(p) = S_in(p) C_p + H_p.  A prefix over the chunks then gives
+    every chunk's incoming state, S_in(p) = S_out(p-1), and each chunk replays
+    its frames from that state to produce its outputs.
+
+    Returns (o, state_out) like ``forward``.
+    """
+    B, L, H, Dk, Dv, T = _shapes(q, k, v, gamma, beta, n)
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    s = _scale(key_scale, Dk, n)
+    eye = np.eye(Dk)
+    o = np.zeros((B, L, H, Dv))
+    state_out = np.zeros((B, H, Dv, Dk))
+    bounds = [(c, min(c + chunk, T)) for c in range(0, T, chunk)]
+    for b in range(B):
+        for h in range(H):
+            Ms, Us = [], []
+            for t in range(T):
+                Kh = s * _frame_cols(k, b, t, h, n)
+                Vt = _frame_cols(v, b, t, h, n)
+                bt = np.asarray(beta[b, t * n:(t + 1) * n, h], dtype=np.float64)
+                Ms.append(float(gamma[b, t, h]) * eye - erase * ((Kh * bt) @ Kh.T))
+                Us.append((Vt * bt) @ Kh.T)
+            # Per-chunk composites (independent across chunks).
+            comps = []
+            for (t0, t1) in bounds:
+                C = eye.copy()
+                Hc = np.zeros((Dv, Dk))
+                for t in range(t0, t1):
+                    C = C @ Ms[t]
+                    Hc = Hc @ Ms[t] + Us[t]
+                comps.append((C, Hc))
+            # Prefix over chunks: incoming state of every chunk.
+            S = (np.zeros((Dv, Dk)) if state_in is None
+                 else np.asarray(state_in[b, h], dtype=np.float64).copy())
+            incoming = []
+            for (C, Hc) in comps:
+                incoming.append(S)
+                S = S @ C + Hc
+            state_out[b, h] = S
+            # Each chunk replays its frames from its incoming state.
+            for (t0, t1), S_in in zip(bounds, incoming):
+                St = S_in
+                for t in range(t0, t1):
+                    St = St @ Ms[t] + Us[t]
+                    o[b, t * n:(t + 1) * n, h, :] = (St @ _frame_cols(q, b, t, h, n)).T
+    return o, state_out

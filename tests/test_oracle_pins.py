@@ -1,0 +1,438 @@
+"""Pins of the float64 oracle against what the SANA-WM pages and plain
+mathematics fix, independently of the oracle's own code.
+
+Every check here computes its expected value by a different route than the
+oracle's recurrence loop: unrolled products, masked-attention closed forms,
+textbook special cases, algebraic identities or finite differences.  A
+dropped term, a wrong sign, a wrong index or a transposed operand in the
+oracle fails at least one of them (the mutation test at the end plants such
+mistakes and checks exactly that).
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_recurrence_frame_amd import inputs as gin
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand_problem(B, H, T, N, D, seed, gamma_lo=0.5, gamma_hi=1.0, state=True):
+    rng = np.random.default_rng(seed)
+    L = T * N
+    q = rng.standard_normal((B, L, H, D))
+    k = rng.standard_normal((B, L, H, D))
+    v = rng.standard_normal((B, L, H, D))
+    g = rng.uniform(gamma_lo, gamma_hi, (B, T, H))
+    beta = rng.uniform(0.05, 1.0, (B, L, H))
+    s0 = 0.3 * rng.standard_normal((B, H, D, D)) if state else None
+    return q, k, v, g, beta, s0
+
+
+# --------------------------------------------------------------------------
+# P1: brute force with unrolled products.
+# S_t = S_0 Phi(1..t) + sum_{tau<=t} U_tau Phi(tau+1..t), Phi(a..b)=M_a...M_b,
+# with M_t and U_t assembled token by token from outer products.
+# --------------------------------------------------------------------------
+def _brute_force(q, k, v, g, beta, n, s0, s, erase=1.0):
+    B, L, H, D = k.shape
+    T = L // n
+    o = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            Ms, Us = [], []
+            for t in range(T):
+                M = g[b, t, h] * np.eye(D)
+                U = np.zeros((D, D))
+                for j in range(n):
+                    l = t * n + j
+                    kh = s * k[b, l, h]
+                    M -= erase * beta[b, l, h] * np.outer(kh, kh)
+                    U += beta[b, l, h] * np.outer(v[b, l, h], kh)
+                Ms.append(M)
+                Us.append(U)
+
+            def phi(a, c):  # product M_a ... M_c (identity when empty)
+                P = np.eye(D)
+                for i in range(a, c + 1):
+                    P = P @ Ms[i]
+                return P
+
+            for t in range(T):
+                S = (np.zeros((D, D)) if s0 is None else s0[b, h] @ phi(0, t))
+                for tau in range(t + 1):
+                    S = S + Us[tau] @ phi(tau + 1, t)
+                for j in range(n):
+                    l = t * n + j
+                    o[b, l, h] = S @ q[b, l, h]
+    return o
+
+
+@pytest.mark.parametrize("key_scale", [0.0, 0.37])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_p1_brute_force_unrolled(key_scale, with_state):
+    q, k, v, g, beta, s0 = _rand_problem(2, 2, 4, 3, 5, seed=1, state=with_state)
+    s = key_scale or 1.0 / np.sqrt(5 * 3)
+    o, _ = oracle.forward(q, k, v, g, beta, 3, state_in=s0, key_scale=key_scale)
+    ref = _brute_force(q, k, v, g, beta, 3, s0, s)
+    assert np.max(np.abs(o - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_p1_scalar_hand_example():
+    # D = 1, N = 1, key_scale = 1/2 (so k^ = k/2), two frames.
+    # frame 1: k=2 -> k^=1, beta=1/2, gamma=3/4, v=4, q=1, S0=0
+    #   M = 3/4 - 1/2*1 = 1/4 ; U = 1/2*4*1 = 2 ; S1 = 0*1/4 + 2 = 2 ; o1 = 2*1 = 2
+    # frame 2: k=4 -> k^=2, beta=1/4, gamma=1, v=-2, q=3
+    #   M = 1 - 1/4*4 = 0 ; U = 1/4*(-2)*2 = -1 ; S2 = 2*0 - 1 = -1 ; o2 = -3
+    q = np.array([1.0, 3.0]).reshape(1, 2, 1, 1)
+    k = np.array([2.0, 4.0]).reshape(1, 2, 1, 1)
+    v = np.array([4.0, -2.0]).reshape(1, 2, 1, 1)
+    g = np.array([0.75, 1.0]).reshape(1, 2, 1)
+    beta = np.array([0.5, 0.25]).reshape(1, 2, 1)
+    o, st = oracle.forward(q, k, v, g, beta, 1, key_scale=0.5)
+    assert o.ravel().tolist() == [2.0, -3.0]
+    assert st.ravel().tolist() == [-1.0]
+
+
+# --------------------------------------------------------------------------
+# P2: with the delta correction switched off (erase = 0) the recurrence is
+# gated linear attention, whose closed form is a masked attention over all
+# L tokens: full within a frame, decayed by prod_{tau<sigma<=t} gamma_sigma
+# across frames, causal by frame; plus the decayed initial state.
+# --------------------------------------------------------------------------
+def test_p2_gla_closed_form():
+    B, H, T, N, D = 1, 2, 5, 3, 6
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, N, D, seed=2)
+    s = 0.29
+    o, _ = oracle.forward(q, k, v, g, beta, N, state_in=s0, key_scale=s, erase=0.0)
+    L = T * N
+    frame = np.arange(L) // N
+    for b in range(B):
+        for h in range(H):
+            logcum = np.cumsum(np.log(g[b, :, h]))          # log prod_{sigma<=t}
+            # decay(tau -> t) = prod_{tau < sigma <= t} gamma_sigma
+            dec = np.exp(logcum[frame][:, None] - logcum[frame][None, :])
+            mask = (frame[None, :] <= frame[:, None]).astype(float)
+            att = s * (q[b, :, h] @ k[b, :, h].T) * beta[b, :, h][None, :] * dec * mask
+            ref = att @ v[b, :, h] + np.exp(logcum[frame])[:, None] * (q[b, :, h] @ s0[b, h].T)
+            assert np.allclose(o[b, :, h], ref, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P3: erase = 0 and gamma = 1: S_t is the running sum of V beta K^^T.
+# --------------------------------------------------------------------------
+def test_p3_prefix_sum():
+    B, H, T, N, D = 1, 1, 6, 4, 5
+    q, k, v, g, beta, _ = _rand_problem(B, H, T, N, D, seed=3, state=False)
+    g = np.ones_like(g)
+    s = 0.5
+    _, _, kept = oracle.forward(q, k, v, g, beta, N, key_scale=s, erase=0.0, keep=True)
+    per_frame = np.einsum("tnd,tne->tde",
+                          (v[0, :, 0] * beta[0, :, 0, None]).reshape(T, N, D),
+                          s * k[0, :, 0].reshape(T, N, D))
+    assert np.allclose(kept["S"][0, 0], np.cumsum(per_frame, axis=0), rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P3': literally beta = 0: no write and no correction, pure decay of S_0.
+# --------------------------------------------------------------------------
+def test_p3b_beta_zero_pure_decay():
+    B, H, T, N, D = 2, 2, 5, 3, 4
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, N, D, seed=4)
+    beta = np.zeros_like(beta)
+    o, st = oracle.forward(q, k, v, g, beta, N, state_in=s0)
+    decay = np.cumprod(g, axis=1)                                # [B, T, H]
+    for t in range(T):
+        St = decay[:, t, :, None, None] * s0                     # [B, H, D, D]
+        ref = np.einsum("bhij,bnhj->bnhi", St, q[:, t * N:(t + 1) * N])
+        assert np.allclose(o[:, t * N:(t + 1) * N], ref, rtol=1e-13, atol=1e-14)
+    assert np.allclose(st, decay[:, -1, :, None, None] * s0, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P4: one token per frame is the token-wise gated delta rule, written in its
+# error-correcting form S <- gamma S + beta (v - S k^) k^^T; at gamma = 1 it
+# is DeltaNet's (Widrow-Hoff) rule.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("gamma_one", [False, True])
+def test_p4_tokenwise_delta_rule(gamma_one):
+    B, H, T, D = 1, 2, 12, 6
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, 1, D, seed=5)
+    if gamma_one:
+        g = np.ones_like(g)
+    o, st = oracle.forward(q, k, v, g, beta, 1, state_in=s0)   # default s = 1/sqrt(D)
+    s = 1.0 / np.sqrt(D)
+    for h in range(H):
+        S = s0[0, h].copy()
+        for t in range(T):
+            kh = s * k[0, t, h]
+            pred = S @ kh
+            S = g[0, t, h] * S + beta[0, t, h] * np.outer(v[0, t, h] - pred, kh)
+            assert np.allclose(o[0, t, h], S @ q[0, t, h], rtol=1e-12, atol=1e-13)
+        assert np.allclose(st[0, h], S, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P5: exact retrieval.  gamma = 1, beta = 1, key scale 1 and keys orthonormal
+# within each frame: S_t k_n = v_n for every key of frame t, whatever S_{t-1}
+# was, so reading with Q_t = K_t returns V_t exactly.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("N,D", [(1, 4), (3, 8), (8, 8)])
+def test_p5_exact_retrieval(N, D):
+    B, H, T = 2, 2, 5
+    kt, vt = gin.orthonormal_frame_keys(B, H, T, N, D, seed=6, io="fp64")
+    k, v = gin.as_f64(kt), gin.as_f64(vt)
+    g = np.ones((B, T, H))
+    beta = np.ones((B, T * N, H))
+    s0 = np.random.default_rng(6).standard_normal((B, H, D, D))
+    o, _ = oracle.forward(k, k, v, g, beta, N, state_in=s0, key_scale=1.0)
+    assert np.allclose(o, v, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P6: the frame update sums over the frame's tokens, so permuting tokens
+# within a frame permutes the outputs the same way.
+# --------------------------------------------------------------------------
+def test_p6_permutation_within_frame():
+    B, H, T, N, D = 1, 2, 4, 5, 6
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, N, D, seed=7)
+    rng = np.random.default_rng(70)
+    perm = np.concatenate([t * N + rng.permutation(N) for t in range(T)])
+    o, st = oracle.forward(q, k, v, g, beta, N, state_in=s0)
+    op, stp = oracle.forward(q[:, perm], k[:, perm], v[:, perm], g, beta[:, perm], N,
+                             state_in=s0)
+    assert np.allclose(op, o[:, perm], rtol=1e-12, atol=1e-13)
+    assert np.allclose(stp, st, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P7: the context-parallel composites reproduce the sequential result
+# (summary page, 技术新颖性 point 1) for any chunking, ragged tail included.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("chunk", [1, 2, 3, 7])
+def test_p7_composite_equals_sequential(chunk):
+    B, H, T, N, D = 1, 2, 7, 3, 5
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, N, D, seed=8)
+    o, st = oracle.forward(q, k, v, g, beta, N, state_in=s0)
+    oc, stc = oracle.composite_forward(q, k, v, g, beta, N, chunk, state_in=s0)
+    assert np.allclose(oc, o, rtol=1e-12, atol=1e-13)
+    assert np.allclose(stc, st, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P8: linearity.  O is linear in (V, S_0) jointly and in Q; the backward is
+# the adjoint of these linear maps.
+# --------------------------------------------------------------------------
+def test_p8_linearity_and_adjoints():
+    B, H, T, N, D = 1, 2, 5, 4, 6
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, N, D, seed=9)
+    rng = np.random.default_rng(90)
+    v2 = rng.standard_normal(v.shape)
+    s02 = rng.standard_normal(s0.shape)
+    o1, st1 = oracle.forward(q, k, v, g, beta, N, state_in=s0)
+    o2, st2 = oracle.forward(q, k, v2, g, beta, N, state_in=s02)
+    o12, st12 = oracle.forward(q, k, 2 * v - 3 * v2, g, beta, N, state_in=2 * s0 - 3 * s02)
+    assert np.allclose(o12, 2 * o1 - 3 * o2, rtol=1e-11, atol=1e-12)
+    assert np.allclose(st12, 2 * st1 - 3 * st2, rtol=1e-11, atol=1e-12)
+
+    d_o = rng.standard_normal(o1.shape)
+    d_st = rng.standard_normal(st1.shape)
+    gr = oracle.backward(q, k, v, g, beta, N, d_o, state_in=s0, d_state_out=d_st)
+    lhs = np.sum(d_o * o1) + np.sum(d_st * st1)
+    # (V, S_0) -> (O, S_T) is linear: <dO,O> + <dS_T,S_T> = <dV,V> + <dS_0,S_0>
+    assert np.isclose(lhs, np.sum(gr["dv"] * v) + np.sum(gr["dstate_in"] * s0), rtol=1e-11)
+    # Q -> O is linear (S_T does not depend on Q): <dO,O> = <dQ,Q>
+    assert np.isclose(np.sum(d_o * o1), np.sum(gr["dq"] * q), rtol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# P9: the key scaling keeps ||M_t||_2 <= gamma_t <= 1 (summary page,
+# 技术新颖性 point 1) at the real per-head shape with normalised keys; the
+# cut-off sentence of module 2 is read as the trace bound tr(A_t) <= 1.
+# --------------------------------------------------------------------------
+def test_p9_spectral_bound_real_shape():
+    t = gin.make_inputs(B=1, H=1, T=3, N=880, D=112, io="bf16", gamma="uniform", seed=11)
+    k, v, g, beta = (gin.as_f64(t[x]) for x in ("k", "v", "gamma", "beta"))
+    A, _ = oracle.frame_terms(k, v, beta, 880)
+    for tt in range(3):
+        At = A[0, 0, tt]
+        M = g[0, tt, 0] * np.eye(112) - At
+        assert np.linalg.norm(M, 2) <= g[0, tt, 0] * (1 + 1e-12)
+        lam = np.linalg.eigvalsh(At)
+        assert lam.min() >= -1e-15 and np.trace(At) <= 1.0
+
+
+# --------------------------------------------------------------------------
+# P10: backward against central finite differences of the forward, for every
+# input (q, k, v, gamma, beta, S_0), with an external dS_T as well.
+# --------------------------------------------------------------------------
+def _loss(args, d_o, d_st, n, s, erase=1.0):
+    q, k, v, g, beta, s0 = args
+    o, st = oracle.forward(q, k, v, g, beta, n, state_in=s0, key_scale=s, erase=erase)
+    return np.sum(o * d_o) + np.sum(st * d_st)
+
+
+@pytest.mark.parametrize("key_scale", [0.0, 0.45])
+def test_p10_finite_differences_elementwise(key_scale):
+    B, H, T, N, D = 1, 1, 3, 2, 3
+    args = list(_rand_problem(B, H, T, N, D, seed=12))
+    rng = np.random.default_rng(120)
+    d_o = rng.standard_normal(args[2].shape)
+    d_st = rng.standard_normal(args[5].shape)
+    gr = oracle.backward(*args[:5], N, d_o, state_in=args[5], d_state_out=d_st,
+                         key_scale=key_scale)
+    names = ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]
+    h = 1e-6
+    for i, name in enumerate(names):
+        x = args[i]
+        fd = np.zeros_like(x)
+        for idx in itertools.product(*[range(s) for s in x.shape]):
+            old = x[idx]
+            x[idx] = old + h
+            fp = _loss(args, d_o, d_st, N, key_scale)
+            x[idx] = old - h
+            fm = _loss(args, d_o, d_st, N, key_scale)
+            x[idx] = old
+            fd[idx] = (fp - fm) / (2 * h)
+        err = np.max(np.abs(fd - gr[name])) / max(1e-12, np.max(np.abs(fd)))
+        assert err < 1e-7, (name, err)
+
+
+def test_p10_finite_differences_directional_tiny_config():
+    t = gin.make_config("tiny", seed=0, with_do=True, with_dstate=True, with_state=True)
+    args = [gin.as_f64(t[x]) for x in ("q", "k", "v", "gamma", "beta", "state")]
+    d_o, d_st = gin.as_f64(t["d_o"]), gin.as_f64(t["d_state"])
+    N = 4
+    gr = oracle.backward(*args[:5], N, d_o, state_in=args[5], d_state_out=d_st)
+    names = ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]
+    rng = np.random.default_rng(13)
+    h = 1e-6
+    for i, name in enumerate(names):
+        for _ in range(3):
+            dirn = rng.standard_normal(args[i].shape)
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[i] += h * dirn
+            minus[i] -= h * dirn
+            fd = (_loss(plus, d_o, d_st, N, 0.0) - _loss(minus, d_o, d_st, N, 0.0)) / (2 * h)
+            an = np.sum(gr[name] * dirn)
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+# --------------------------------------------------------------------------
+# P11: one call over T frames equals T streaming steps, and equals splitting
+# the sequence anywhere and resuming from the carried state.
+# --------------------------------------------------------------------------
+def test_p11_split_and_resume():
+    B, H, T, N, D = 1, 2, 6, 3, 4
+    q, k, v, g, beta, s0 = _rand_problem(B, H, T, N, D, seed=14)
+    o, st = oracle.forward(q, k, v, g, beta, N, state_in=s0)
+    S = s0
+    outs = []
+    for t in range(T):
+        sl = slice(t * N, (t + 1) * N)
+        ot, S = oracle.step(q[:, sl], k[:, sl], v[:, sl], g[:, t:t + 1], beta[:, sl], S,
+                            key_scale=1.0 / np.sqrt(D * N))
+        outs.append(ot)
+    assert np.allclose(np.concatenate(outs, axis=1), o, rtol=1e-12, atol=1e-13)
+    assert np.allclose(S, st, rtol=1e-12, atol=1e-13)
+    for t0 in range(1, T):
+        a = slice(0, t0 * N)
+        c = slice(t0 * N, T * N)
+        oa, sa = oracle.forward(q[:, a], k[:, a], v[:, a], g[:, :t0], beta[:, a], N,
+                                state_in=s0)
+        oc, sc = oracle.forward(q[:, c], k[:, c], v[:, c], g[:, t0:], beta[:, c], N,
+                                state_in=sa)
+        assert np.allclose(np.concatenate([oa, oc], axis=1), o, rtol=1e-12, atol=1e-13)
+        assert np.allclose(sc, st, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P12 (stability, Figure 6 analogue): without the 1/sqrt(DS) key scaling the
+# transition expands (||M_t||_2 ~ 6.7 at 112 x 880) and the state grows
+# geometrically; with it the state stays bounded.
+# --------------------------------------------------------------------------
+def test_p12_key_scaling_stability():
+    t = gin.make_inputs(B=1, H=1, T=12, N=880, D=112, io="bf16", gamma="uniform", seed=15)
+    q, k, v, g, beta = (gin.as_f64(t[x]) for x in ("q", "k", "v", "gamma", "beta"))
+    _, _, kept1 = oracle.forward(q, k, v, g, beta, 880, key_scale=1.0, keep=True)
+    _, _, kept0 = oracle.forward(q, k, v, g, beta, 880, keep=True)
+    n1 = np.linalg.norm(kept1["S"][0, 0], axis=(1, 2))
+    n0 = np.linalg.norm(kept0["S"][0, 0], axis=(1, 2))
+    assert n1[-1] / n1[5] > 1e3                       # ~3x per frame: geometric blow-up
+    assert n0[-1] < 2 * n0[5] + 1.0                   # bounded
+    M1 = g[0, 0, 0] * np.eye(112) - kept1["A"][0, 0, 0]
+    assert np.linalg.norm(M1, 2) > 3.0
+
+
+# --------------------------------------------------------------------------
+# Shapes fixed by the pages (tests/golden/page_shapes.json, each with its
+# citation) agree with the workload recipes used for parity and timing.
+# --------------------------------------------------------------------------
+def test_workload_shapes_follow_pages():
+    with open(os.path.join(HERE, "golden", "page_shapes.json")) as f:
+        pg = json.load(f)
+    d = pg["model_width"]["value"] // pg["heads"]["value"]
+    assert d == 112
+    frames = pg["video_seconds"]["value"] * pg["fps"]["value"] + 1
+    assert frames == 961
+    latent = 1 + (frames - 1) // pg["temporal_compression"]["value"]
+    mn = gin.CONFIGS["minute"]
+    assert (mn["D"], mn["H"], mn["T"]) == (d, pg["heads"]["value"], latent)
+    assert mn["N"] == pg["latent_grid"]["value"][0] * pg["latent_grid"]["value"][1]
+    assert len(pg["gdn_layers"]["value"]) == 15
+
+
+# --------------------------------------------------------------------------
+# Mutation check: plant plausible mistakes in a copy of the recurrence and
+# confirm the pins above would catch each of them.
+# --------------------------------------------------------------------------
+def _mutant_forward(kind, q, k, v, g, beta, n, s0, s):
+    B, L, H, D = k.shape
+    T = L // n
+    o = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            S = s0[b, h].copy() if s0 is not None else np.zeros((D, D))
+            for t in range(T):
+                sl = slice(t * n, (t + 1) * n)
+                Kh = s * k[b, sl, h].T
+                Vt = v[b, sl, h].T
+                bt = beta[b, sl, h]
+                A = (Kh * bt) @ Kh.T
+                U = (Vt * bt) @ Kh.T
+                if kind == "erase_sign":
+                    M = g[b, t, h] * np.eye(D) + A
+                elif kind == "decay_on_all":
+                    M = g[b, t, h] * (np.eye(D) - A)
+                elif kind == "write_transposed":
+                    U = U.T
+                    M = g[b, t, h] * np.eye(D) - A
+                elif kind == "scale_once":
+                    M = g[b, t, h] * np.eye(D) - A / s
+                else:
+                    M = g[b, t, h] * np.eye(D) - A
+                S_prev = S
+                S = S @ M + U
+                if kind == "output_prev_state":
+                    o[b, sl, h] = (S_prev @ q[b, sl, h].T).T
+                else:
+                    o[b, sl, h] = (S @ q[b, sl, h].T).T
+    return o
+
+
+@pytest.mark.parametrize("kind", ["erase_sign", "decay_on_all", "write_transposed",
+                                  "scale_once", "output_prev_state"])
+def test_pins_catch_planted_mistakes(kind):
+    q, k, v, g, beta, s0 = _rand_problem(1, 1, 4, 3, 5, seed=16)
+    s = 0.37
+    ref = _brute_force(q, k, v, g, beta, 3, s0, s)
+    mut = _mutant_forward(kind, q, k, v, g, beta, 3, s0, s)
+    assert np.max(np.abs(mut - ref)) > 1e-6
+    ok = _mutant_forward("none", q, k, v, g, beta, 3, s0, s)
+    assert np.max(np.abs(ok - ref)) < 1e-12
