@@ -1,0 +1,304 @@
+// Host side of libgdn's C ABI: argument validation, workspace carving and
+// kernel dispatch onto the caller's stream.  See include/gdn.h for the
+// contract of every entry point.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+constexpr int kDefaultChunk = 1;   // sequential scan unless asked otherwise
+
+struct Shape {
+  int64_t B, H, T, N, D, L;
+  int io;            // IO_BF16 / IO_F32
+  int es;            // bytes per io element
+  float s;           // key scale
+  int chunk;         // 1: sequential scan; >= 2: composite chunks
+  int64_t mat;       // bytes of one [B, H, T, D, D] fp32 buffer
+  int64_t parts;     // composite chunks per sequence
+};
+
+gdn_status check_problem(const gdn_problem* p, Shape* sh) {
+  if (!p) return GDN_ERR_NULL_POINTER;
+  if (p->io_dtype != GDN_BF16 && p->io_dtype != GDN_FP32) return GDN_ERR_BAD_DTYPE;
+  if (p->B < 1 || p->H < 1 || p->T < 1 || p->N < 1 || p->Dk < 1 || p->Dv < 1)
+    return GDN_ERR_BAD_SHAPE;
+  if (p->scan_chunk < 0) return GDN_ERR_BAD_SHAPE;
+  if (!isfinite(p->key_scale)) return GDN_ERR_BAD_SHAPE;
+  if (p->Dk != p->Dv || p->Dk % 16 != 0 || p->Dk > 128) return GDN_ERR_UNSUPPORTED;
+  if (p->scan_chunk > 1) return GDN_ERR_UNSUPPORTED;
+  Shape s;
+  s.B = p->B; s.H = p->H; s.T = p->T; s.N = p->N; s.D = p->Dk;
+  s.L = s.T * s.N;
+  // Grid sizes and element offsets must fit the kernels' integer types.
+  if (s.B * s.T * s.H > INT32_MAX || s.B * s.H * 8 > INT32_MAX) return GDN_ERR_BAD_SHAPE;
+  if (s.B * s.L * s.H > (int64_t(1) << 40)) return GDN_ERR_BAD_SHAPE;
+  s.io = p->io_dtype == GDN_BF16 ? IO_BF16 : IO_F32;
+  s.es = p->io_dtype == GDN_BF16 ? 2 : 4;
+  s.s = p->key_scale != 0.f ? p->key_scale : (float)(1.0 / sqrt((double)s.D * (double)s.N));
+  s.chunk = p->scan_chunk == 0 ? kDefaultChunk : p->scan_chunk;
+  if (s.chunk > s.T) s.chunk = (int)s.T;
+  s.mat = s.B * s.H * s.T * s.D * s.D * 4;
+  s.parts = (s.T + s.chunk - 1) / s.chunk;
+  *sh = s;
+  return GDN_OK;
+}
+
+int64_t chunk_bytes(const Shape& s) {
+  return s.chunk > 1 ? 2 * s.B * s.H * s.parts * s.D * s.D * 4 : 0;
+}
+
+int64_t forward_ws(const Shape& s) { return 3 * s.mat + chunk_bytes(s); }
+int64_t backward_ws(const Shape& s) { return 6 * s.mat + chunk_bytes(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+struct Span {
+  const void* p;
+  int64_t n;
+};
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.n <= 0 || b.n <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + (uintptr_t)b.n && b0 < a0 + (uintptr_t)a.n;
+}
+bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
+  for (int i = 0; i < no; ++i)
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+  for (int i = 0; i < no; ++i)
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  return false;
+}
+
+gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// Forward pipeline shared by gdn_forward and gdn_step.
+gdn_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
+                       const float* gamma, const float* beta, const float* state_in,
+                       void* o, float* state_out, void* saved, void* workspace,
+                       hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  float* A = saved ? static_cast<float*>(saved) : reinterpret_cast<float*>(ws);
+  float* S = saved ? reinterpret_cast<float*>(static_cast<char*>(saved) + s.mat)
+                   : reinterpret_cast<float*>(ws + s.mat);
+  float* U = reinterpret_cast<float*>(ws + 2 * s.mat);
+  char* chunk_ws = ws + 3 * s.mat;
+  const int nt = (int)(s.D / 16);
+
+  GramArgs ga{};
+  ga.x0 = k; ga.x1 = v; ga.y = k; ga.w = beta;
+  ga.out0 = A; ga.out1 = U;
+  ga.scale0 = s.s * s.s; ga.scale1 = s.s;
+  ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
+  gdn_status st = hip_status(launch_gram(ga, s.io, nt, 2, stream));
+  if (st != GDN_OK) return st;
+
+  if (s.chunk > 1) {
+    ChunkScanArgs ca{};
+    ca.A = A; ca.U = U; ca.gamma = gamma; ca.z0 = state_in; ca.emit = S; ca.zT = state_out;
+    ca.comp = reinterpret_cast<float*>(chunk_ws);
+    ca.hin = reinterpret_cast<float*>(chunk_ws + s.B * s.H * s.parts * s.D * s.D * 4);
+    ca.B = (int)s.B; ca.H = (int)s.H; ca.T = (int)s.T; ca.chunk = s.chunk;
+    st = hip_status(launch_chunk_scan(ca, nt, stream));
+  } else {
+    ScanArgs sa{};
+    sa.A = A; sa.U = U; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S; sa.zT = state_out;
+    sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
+    st = hip_status(launch_scan(sa, nt, false, stream));
+  }
+  if (st != GDN_OK) return st;
+
+  OutArgs oa{};
+  oa.tok = q; oa.mat = S; oa.out = o;
+  oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
+  return hip_status(launch_output(oa, s.io, nt, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "bad shape or size";
+    case GDN_ERR_BAD_DTYPE: return "unknown io dtype";
+    case GDN_ERR_MISALIGNED: return "a pointer is misaligned (16 bytes; 4 for gates)";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GDN_ERR_UNSUPPORTED: return "unsupported head dimension (need Dk == Dv, multiple of 16, <= 128)";
+    case GDN_ERR_HIP: return "HIP kernel launch failed";
+    case GDN_ERR_ALIASING: return "an output overlaps an input";
+  }
+  return "unknown status";
+}
+
+gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes) {
+  if (!bytes) return GDN_ERR_NULL_POINTER;
+  Shape s;
+  gdn_status st = check_problem(p, &s);
+  if (st != GDN_OK) return st;
+  switch (op) {
+    case GDN_OP_FORWARD: *bytes = (size_t)forward_ws(s); return GDN_OK;
+    case GDN_OP_STEP:
+      if (s.T != 1) return GDN_ERR_BAD_SHAPE;
+      *bytes = (size_t)forward_ws(s);
+      return GDN_OK;
+    case GDN_OP_BACKWARD: *bytes = (size_t)backward_ws(s); return GDN_OK;
+  }
+  return GDN_ERR_BAD_SHAPE;
+}
+
+gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes) {
+  if (!bytes) return GDN_ERR_NULL_POINTER;
+  Shape s;
+  gdn_status st = check_problem(p, &s);
+  if (st != GDN_OK) return st;
+  *bytes = (size_t)(2 * s.mat);
+  return GDN_OK;
+}
+
+gdn_status gdn_forward(const gdn_problem* p, const void* q, const void* k, const void* v,
+                       const float* gamma, const float* beta, const float* state_in,
+                       void* o, float* state_out, void* saved, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Shape s;
+  gdn_status st = check_problem(p, &s);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !gamma || !beta || !o || !workspace) return GDN_ERR_NULL_POINTER;
+  const void* ptrs[] = {q, k, v, state_in, o, state_out, saved, workspace};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return GDN_ERR_MISALIGNED;
+  if (!aligned4(gamma) || !aligned4(beta)) return GDN_ERR_MISALIGNED;
+  if ((int64_t)workspace_bytes < forward_ws(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t tok = s.B * s.L * s.H * s.D * s.es;
+  const int64_t stb = s.B * s.H * s.D * s.D * 4;
+  const Span ins[] = {{q, tok}, {k, tok}, {v, tok}, {gamma, s.B * s.T * s.H * 4},
+                      {beta, s.B * s.L * s.H * 4}, {state_in, stb}};
+  const Span outs[] = {{o, tok}, {saved, saved ? 2 * s.mat : 0},
+                       {workspace, (int64_t)workspace_bytes}};
+  if (any_overlap(outs, 3, ins, 6)) return GDN_ERR_ALIASING;
+  if (state_out) {
+    const Span so[] = {{state_out, stb}};
+    if (any_overlap(so, 1, outs, 3)) return GDN_ERR_ALIASING;
+    if (state_out != state_in && any_overlap(so, 1, ins, 6)) return GDN_ERR_ALIASING;
+  }
+  return run_forward(s, q, k, v, gamma, beta, state_in, o, state_out, saved, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_step(const gdn_problem* p, const void* q, const void* k, const void* v,
+                    const float* gamma, const float* beta, float* state, void* o,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  gdn_status st = check_problem(p, &s);
+  if (st != GDN_OK) return st;
+  if (s.T != 1) return GDN_ERR_BAD_SHAPE;
+  if (!state) return GDN_ERR_NULL_POINTER;
+  return gdn_forward(p, q, k, v, gamma, beta, state, o, state, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, const void* v,
+                        const float* gamma, const float* beta, const float* state_in,
+                        const void* d_o, const float* d_state_out, const void* saved,
+                        void* dq, void* dk, void* dv, float* dgamma, float* dbeta,
+                        float* d_state_in, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  Shape s;
+  gdn_status st = check_problem(p, &s);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !gamma || !beta || !d_o || !dq || !dk || !dv || !dgamma || !dbeta ||
+      !workspace)
+    return GDN_ERR_NULL_POINTER;
+  const void* ptrs[] = {q, k, v, state_in, d_o, d_state_out, saved,
+                        dq, dk, dv, d_state_in, workspace};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return GDN_ERR_MISALIGNED;
+  const void* gates[] = {gamma, beta, dgamma, dbeta};
+  for (const void* x : gates)
+    if (!aligned4(x)) return GDN_ERR_MISALIGNED;
+  if ((int64_t)workspace_bytes < backward_ws(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t tok = s.B * s.L * s.H * s.D * s.es;
+  const int64_t stb = s.B * s.H * s.D * s.D * 4;
+  const Span ins[] = {{q, tok}, {k, tok}, {v, tok}, {gamma, s.B * s.T * s.H * 4},
+                      {beta, s.B * s.L * s.H * 4}, {state_in, stb}, {d_o, tok},
+                      {d_state_out, stb}, {saved, saved ? 2 * s.mat : 0}};
+  const Span outs[] = {{dq, tok}, {dk, tok}, {dv, tok}, {dgamma, s.B * s.T * s.H * 4},
+                       {dbeta, s.B * s.L * s.H * 4}, {d_state_in, stb},
+                       {workspace, (int64_t)workspace_bytes}};
+  if (any_overlap(outs, 7, ins, 9)) return GDN_ERR_ALIASING;
+
+  hipStream_t stream_ = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int nt = (int)(s.D / 16);
+  const float* A;
+  const float* S;
+  if (saved) {
+    A = static_cast<const float*>(saved);
+    S = reinterpret_cast<const float*>(static_cast<const char*>(saved) + s.mat);
+  } else {
+    // Recompute A_t and S_t with the forward's own kernels into the
+    // workspace (layout of `saved`), without writing an output.
+    float* A_ = reinterpret_cast<float*>(ws);
+    float* S_ = reinterpret_cast<float*>(ws + s.mat);
+    float* U_ = reinterpret_cast<float*>(ws + 2 * s.mat);
+    GramArgs ga{};
+    ga.x0 = k; ga.x1 = v; ga.y = k; ga.w = beta; ga.out0 = A_; ga.out1 = U_;
+    ga.scale0 = s.s * s.s; ga.scale1 = s.s;
+    ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
+    st = hip_status(launch_gram(ga, s.io, nt, 2, stream_));
+    if (st != GDN_OK) return st;
+    ScanArgs sa{};
+    sa.A = A_; sa.U = U_; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S_; sa.zT = nullptr;
+    sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
+    st = hip_status(launch_scan(sa, nt, false, stream_));
+    if (st != GDN_OK) return st;
+    A = A_;
+    S = S_;
+  }
+  float* X = reinterpret_cast<float*>(ws + 3 * s.mat);
+  float* G = reinterpret_cast<float*>(ws + 4 * s.mat);
+  float* W = reinterpret_cast<float*>(ws + 5 * s.mat);
+
+  // X_t = dO_t Q^_t^T, the frame's own contribution to dLoss/dS_t.
+  GramArgs gx{};
+  gx.x0 = d_o; gx.x1 = nullptr; gx.y = q; gx.w = nullptr; gx.out0 = X; gx.out1 = nullptr;
+  gx.scale0 = 1.f; gx.scale1 = 0.f;
+  gx.B = (int)s.B; gx.H = (int)s.H; gx.T = (int)s.T; gx.N = (int)s.N;
+  st = hip_status(launch_gram(gx, s.io, nt, 1, stream_));
+  if (st != GDN_OK) return st;
+
+  // Reverse scan: G_t = X_t + G_{t+1} M_{t+1}^T, dS_0 = G_1 M_1^T.
+  ScanArgs ra{};
+  ra.A = A; ra.U = X; ra.gamma = gamma; ra.z0 = d_state_out; ra.emit = G; ra.zT = d_state_in;
+  ra.B = (int)s.B; ra.H = (int)s.H; ra.T = (int)s.T;
+  st = hip_status(launch_scan(ra, nt, true, stream_));
+  if (st != GDN_OK) return st;
+
+  DmArgs da{};
+  da.S = S; da.s0 = state_in; da.G = G; da.W = W; da.dgamma = dgamma;
+  da.B = (int)s.B; da.H = (int)s.H; da.T = (int)s.T;
+  st = hip_status(launch_dm(da, nt, stream_));
+  if (st != GDN_OK) return st;
+
+  BwdTokArgs ba{};
+  ba.k = k; ba.v = v; ba.d_o = d_o; ba.beta = beta; ba.S = S; ba.G = G; ba.W = W;
+  ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
+  ba.B = (int)s.B; ba.H = (int)s.H; ba.T = (int)s.T; ba.N = (int)s.N;
+  return hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
+}
+
+}  // extern "C"

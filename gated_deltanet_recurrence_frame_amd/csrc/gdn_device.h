@@ -1,0 +1,107 @@
+// Device-side building blocks for the libgdn kernels (gfx950 / CDNA4).
+//
+// MFMA shapes used (lane l of a 64-wide wave, g = l / 16, i = l % 16):
+//   bf16  v_mfma_f32_16x16x32_bf16: A[m][k] with m = i, k = 8g..8g+7;
+//                                   B[k][n] with k = 8g..8g+7, n = i;
+//   fp32  v_mfma_f32_16x16x4_f32:   A[m][k] with m = i, k = g;
+//                                   B[k][n] with k = g, n = i;
+//   both: C[m][n] with m = 4g + r (r = 0..3 in the four accumulator
+//         registers), n = i.
+// These lane layouts were checked on gfx950 against a host matmul.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+enum IoKind { IO_BF16 = 0, IO_F32 = 1 };
+
+template <int IO> struct Io;
+template <> struct Io<IO_BF16> {
+  typedef uint16_t elem;               // raw bf16 bits
+  static constexpr int bytes = 2;
+  static constexpr int kblock = 32;    // contraction depth of one MFMA
+};
+template <> struct Io<IO_F32> {
+  typedef float elem;
+  static constexpr int bytes = 4;
+  static constexpr int kblock = 4;
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// Eight consecutive bf16 of a row (16 bytes).
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Eight consecutive fp32 values rounded to a bf16 fragment.
+__device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(v[e]);
+  return r;
+}
+
+// Column fragment of a row-major bf16 matrix M in LDS (row stride ld
+// elements): lane (g, i) receives M[k0 + 8g + e][c0 + i], e = 0..7.
+// Uses the gfx950 transposing LDS read: within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte chunk addressed by lane
+// 4j + i / 4 as its element j.  Lane m therefore addresses row
+// k0 + 8g + m / 4 (+4 for the second read), columns c0 + 4 (m % 4) .. +3.
+// Needs (ld * 2) and (c0 * 2) to be multiples of 8 bytes.
+__device__ __forceinline__ bf16x8 lds_col_frag_bf16(const uint16_t* M, int ld, int k0, int c0) {
+  const int l = lane_id();
+  const int g = l >> 4, m = l & 15;
+  const uint16_t* p0 = M + (k0 + 8 * g + (m >> 2)) * ld + c0 + 4 * (m & 3);
+  const uint16_t* p1 = p0 + 4 * ld;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// Block-wide barrier.
+__device__ __forceinline__ void block_sync() { __syncthreads(); }
+
+// XCD-aware work ordering.  Hardware hands consecutive workgroup ids to the
+// 8 XCDs in turn; this maps them so that each XCD receives a contiguous
+// range of work items (neighbouring heads of the same frame share L2 there).
+__device__ __forceinline__ int xcd_item(int id, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = id & 7, local = id >> 3;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
+}  // namespace gdn

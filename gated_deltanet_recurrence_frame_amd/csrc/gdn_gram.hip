@@ -1,0 +1,237 @@
+// Per-frame token contraction ("Gram / write" pass) of the frame-wise GDN.
+//
+// For one (batch b, frame t, head h) the kernel computes, over the N tokens
+// of the frame,
+//     C_r = scale_r * X_r^T diag(w) Y        (D x D, fp32),  r < NR
+// where X_r and Y are the frame's [N, D] token rows of [B, L, H, D] tensors.
+//   forward:  X_0 = K, X_1 = V, Y = K, w = beta, scales s^2 and s, giving
+//             A_t = K^_t beta_t K^_t^T and U_t = V_t beta_t K^_t^T
+//             (summary page, 方法步骤详情 module 2: the delta-rule Gram and
+//             the write term of M_t and U_t);
+//   backward: X_0 = dO, Y = Q, w = 1, scale 1, giving dO_t Q^_t^T, the
+//             frame's own contribution to dLoss/dS_t.
+// All tokens of a frame read the same S_{t-1}, so there is no intra-frame
+// triangular structure: the contraction is a dense D x N x D product.
+//
+// Layout of the work: one workgroup (4 waves) per (b, t, h), XCD-aware
+// ordering so heads of one frame run on one XCD.  Tokens stream through LDS
+// in chunks of CT rows (natural [token][feature] layout, double-buffered,
+// next chunk prefetched into registers while the current one is consumed).
+// Both MFMA operands need a feature's values over consecutive tokens; they
+// are read with the gfx950 transposing LDS read.  The weight w multiplies
+// the X operand in fp32 before rounding to bf16.  Tail tokens of the last
+// chunk re-read the frame's last row and get w = 0, so they add exactly 0.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+template <int IO, int NT, int NR, bool Y_IS_X0>
+struct GramCfg {
+  static constexpr int D = 16 * NT;
+  static constexpr int ES = Io<IO>::bytes;
+  static constexpr int KBK = Io<IO>::kblock;
+  static constexpr int CT = (IO == IO_BF16) ? 64 : 32;     // tokens per chunk
+  static constexpr int NMAT = NR + (Y_IS_X0 ? 0 : 1);       // matrices staged
+  static constexpr int PR = D * ES / 16;                    // 16-byte pieces per row
+  static constexpr int PIECES = NMAT * CT * PR;
+  static constexpr int PPT = (PIECES + 255) / 256;          // pieces per thread
+  static constexpr int MAT_ELEMS = CT * D;
+  static constexpr int STAGE_BYTES = NMAT * MAT_ELEMS * ES + CT * 4;
+  static constexpr int RT = (NR * NT + 3) / 4;              // row tiles per wave
+};
+
+template <int IO, int NT, int NR, bool Y_IS_X0>
+__global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
+  typedef GramCfg<IO, NT, NR, Y_IS_X0> C;
+  typedef typename Io<IO>::elem E;
+  constexpr int D = C::D;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+
+  const int total = a.B * a.T * a.H;
+  const int item = xcd_item(blockIdx.x, total);
+  const int h = item % a.H;
+  const int t = (item / a.H) % a.T;
+  const int b = item / (a.H * a.T);
+  const int N = a.N;
+  const long L = (long)a.T * N;
+  const long row0 = (long)b * L + (long)t * N;   // first token row of the frame
+
+  const E* mats[3] = {static_cast<const E*>(a.x0), static_cast<const E*>(a.x1),
+                      static_cast<const E*>(a.y)};
+  // staged matrix m -> source: 0 -> x0, 1 -> x1 (NR == 2) or y, 2 -> y
+  auto src_of = [&](int m) -> const E* {
+    if (m < NR) return mats[m];
+    return mats[2];
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int g = lane >> 4, li = lane & 15;
+  const int nchunks = (N + C::CT - 1) / C::CT;
+
+  u32x4 pre[C::PPT];
+  float wpre = 0.f;
+
+  auto issue = [&](int c) {
+    const int c0 = c * C::CT;
+#pragma unroll
+    for (int j = 0; j < C::PPT; ++j) {
+      const int p = tid + 256 * j;
+      if (p < C::PIECES) {
+        const int m = p / (C::CT * C::PR);
+        const int r = p % (C::CT * C::PR);
+        int row = r / C::PR;
+        const int pc = r % C::PR;
+        int tok = c0 + row;
+        if (tok >= N) tok = N - 1;
+        const E* src = src_of(m) + ((row0 + tok) * a.H + h) * (long)D + pc * (16 / C::ES);
+        pre[j] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+    if (tid < C::CT) {
+      const int tok = c0 + tid;
+      if (tok < N)
+        wpre = a.w ? a.w[(row0 + tok) * a.H + h] : 1.0f;
+      else
+        wpre = 0.f;
+    }
+  };
+  auto commit = [&](int stage) {
+    char* base = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::PPT; ++j) {
+      const int p = tid + 256 * j;
+      if (p < C::PIECES) {
+        const int m = p / (C::CT * C::PR);
+        const int r = p % (C::CT * C::PR);
+        E* dst = reinterpret_cast<E*>(base) + m * C::MAT_ELEMS + r * (16 / C::ES);
+        *reinterpret_cast<u32x4*>(dst) = pre[j];
+      }
+    }
+    if (tid < C::CT)
+      reinterpret_cast<float*>(base + C::NMAT * C::MAT_ELEMS * C::ES)[tid] = wpre;
+  };
+
+  f32x4 acc[C::RT][NT];
+#pragma unroll
+  for (int j = 0; j < C::RT; ++j)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
+
+  issue(0);
+  commit(0);
+  block_sync();
+
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + 1 < nchunks) issue(c + 1);
+    const char* base = smem + (c & 1) * C::STAGE_BYTES;
+    const E* xs = reinterpret_cast<const E*>(base);
+    const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * C::MAT_ELEMS;
+    const float* ws = reinterpret_cast<const float*>(base + C::NMAT * C::MAT_ELEMS * C::ES);
+
+    if constexpr (IO == IO_BF16) {
+#pragma unroll
+      for (int kb = 0; kb < C::CT / 32; ++kb) {
+        const int k0 = kb * 32;
+        float wv[8];
+        {
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { wv[e] = w0[e]; wv[4 + e] = w1[e]; }
+        }
+        bf16x8 bfr[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          bfr[ct] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(ys), D, k0, ct * 16);
+#pragma unroll
+        for (int j = 0; j < C::RT; ++j) {
+          const int rtg = wave + 4 * j;
+          if (rtg < NR * NT) {
+            const int m = rtg / NT, ft = rtg % NT;
+            bf16x8 af = lds_col_frag_bf16(
+                reinterpret_cast<const uint16_t*>(xs + m * C::MAT_ELEMS), D, k0, ft * 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              af[e] = static_cast<__bf16>(static_cast<float>(af[e]) * wv[e]);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_bf16(af, bfr[ct], acc[j][ct]);
+          }
+        }
+      }
+    } else {
+#pragma unroll 2
+      for (int kb = 0; kb < C::CT / 4; ++kb) {
+        const int k = kb * 4 + g;
+        const float wv = ws[k];
+        float bfr[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * D + ct * 16 + li];
+#pragma unroll
+        for (int j = 0; j < C::RT; ++j) {
+          const int rtg = wave + 4 * j;
+          if (rtg < NR * NT) {
+            const int m = rtg / NT, ft = rtg % NT;
+            const float af =
+                reinterpret_cast<const float*>(xs + m * C::MAT_ELEMS)[k * D + ft * 16 + li] * wv;
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_f32(af, bfr[ct], acc[j][ct]);
+          }
+        }
+      }
+    }
+
+    if (c + 1 < nchunks) commit((c + 1) & 1);
+    block_sync();
+  }
+
+  // Epilogue: C[m][n] lives in lane (g, n) register r with m = 4g + r.
+  const long obase = (((long)b * a.H + h) * a.T + t) * (long)(D * D);
+#pragma unroll
+  for (int j = 0; j < C::RT; ++j) {
+    const int rtg = wave + 4 * j;
+    if (rtg < NR * NT) {
+      const int m = rtg / NT, ft = rtg % NT;
+      float* out = (m == 0 ? a.out0 : a.out1) + obase;
+      const float sc = (m == 0 ? a.scale0 : a.scale1);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          out[(ft * 16 + 4 * g + r) * D + ct * 16 + li] = sc * acc[j][ct][r];
+    }
+  }
+}
+
+template <int IO, int NT>
+static hipError_t launch_gram_nt(const GramArgs& a, int nr, hipStream_t s) {
+  const dim3 grid(a.B * a.T * a.H), block(256);
+  if (nr == 2)
+    hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int IO>
+static hipError_t launch_gram_io(const GramArgs& a, int nt, int nr, hipStream_t s) {
+  switch (nt) {
+    case 1: return launch_gram_nt<IO, 1>(a, nr, s);
+    case 2: return launch_gram_nt<IO, 2>(a, nr, s);
+    case 3: return launch_gram_nt<IO, 3>(a, nr, s);
+    case 4: return launch_gram_nt<IO, 4>(a, nr, s);
+    case 5: return launch_gram_nt<IO, 5>(a, nr, s);
+    case 6: return launch_gram_nt<IO, 6>(a, nr, s);
+    case 7: return launch_gram_nt<IO, 7>(a, nr, s);
+    case 8: return launch_gram_nt<IO, 8>(a, nr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s) {
+  return io == IO_BF16 ? launch_gram_io<IO_BF16>(a, nt, nr, s)
+                       : launch_gram_io<IO_F32>(a, nt, nr, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,157 @@
+/*
+ * libgdn: frame-wise Gated DeltaNet (GDN) token mixer for MI355X (gfx950).
+ *
+ * The operation (paper.rainbus.top summary of "SANA-WM: Efficient
+ * Minute-Scale World Modeling with Hybrid Linear Diffusion Transformer"):
+ *   - section 前置知识, "Gated DeltaNet (GDN)": one D x D state S_t per head,
+ *     S_t = S_{t-1} M_t + U_t;
+ *   - section 方法步骤详情, module 2: the scan advances once per latent frame,
+ *       M_t = gamma_t I - K^_t beta_t K^_t^T,  U_t = V_t beta_t K^_t^T,
+ *       O_t = S_t Q^_t,
+ *     with keys scaled by 1/sqrt(D S) (D = head dim, S = tokens per frame);
+ *   - section 技术新颖性, point 1: the frame-wise scan generalises token-wise
+ *     GDN; transition composites C_p and input composites H_p combine by a
+ *     prefix that reproduces the sequential result exactly.
+ * Column form: K^_t, Q^_t are D x N (a column per token), V_t, O_t are D x N,
+ * beta_t = diag(beta_t1 .. beta_tN), S is Dv x Dk (row i = value dim i).
+ *
+ * Memory layout (row-major, contiguous, frame-major tokens l = t*N + n):
+ *   q, k            [B, L, H, Dk]    io dtype (bf16 or fp32)
+ *   v, o, d_o       [B, L, H, Dv]    io dtype
+ *   gamma           [B, T, H]        fp32   (one decay per frame and head)
+ *   beta            [B, L, H]        fp32   (one write strength per token)
+ *   state_*         [B, H, Dv, Dk]   fp32
+ *   dgamma [B,T,H], dbeta [B,L,H]    fp32
+ * Queries and keys are used as given: the library does not normalise them;
+ * it applies only the key scale.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ *     Nothing synchronises the device.
+ *   - Arguments are validated on the host before any launch.  On a
+ *     validation error nothing is launched, nothing is written, and a
+ *     specific gdn_status is returned.  A failed launch returns
+ *     GDN_ERR_HIP (outputs then undefined).  Device faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.
+ *   - Tensor and workspace pointers must be 16-byte aligned; the gate
+ *     pointers (gamma, beta, dgamma, dbeta) 4-byte aligned.  Outputs must
+ *     not overlap inputs, except where an entry point says so.
+ *   - Reentrant: no mutable global state.
+ *   - Supported shapes: Dk == Dv == D with D a multiple of 16 and <= 128;
+ *     B, H, T, N >= 1; B*H*T and B*L*H must fit in int32.
+ */
+#ifndef LIBGDN_GDN_H
+#define LIBGDN_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_POINTER = 1,        /* a required pointer is NULL            */
+    GDN_ERR_BAD_SHAPE = 2,           /* a size < 1 or inconsistent            */
+    GDN_ERR_BAD_DTYPE = 3,           /* io_dtype not a gdn_dtype              */
+    GDN_ERR_MISALIGNED = 4,          /* a pointer misaligned (16 B; gates 4 B) */
+    GDN_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < required            */
+    GDN_ERR_UNSUPPORTED = 6,         /* D not a multiple of 16, > 128, Dk!=Dv */
+    GDN_ERR_HIP = 7,                 /* a kernel launch failed                */
+    GDN_ERR_ALIASING = 8             /* an output overlaps an input           */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_FP32 = 1 } gdn_dtype;
+
+typedef enum { GDN_OP_FORWARD = 0, GDN_OP_STEP = 1, GDN_OP_BACKWARD = 2 } gdn_op;
+
+typedef struct {
+    int32_t B, H, T, N;   /* batch, heads, latent frames, tokens per frame   */
+    int32_t Dk, Dv;       /* head dims; must be equal                        */
+    int32_t io_dtype;     /* gdn_dtype of q, k, v, o, d_o, dq, dk, dv        */
+    float key_scale;      /* 0 => 1/sqrt(Dk * N), the 1/sqrt(D S) of the
+                             summary page (module 2; novelty point 1)        */
+    int32_t scan_chunk;   /* inter-frame scan: 0 => library default,
+                             1 => sequential over frames,
+                             c >= 2 => composite prefix over chunks of c
+                             frames (novelty point 1); same result up to
+                             rounding order                                  */
+} gdn_problem;
+
+/* Version of this interface (GDN_ABI_VERSION). */
+int gdn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gdn_status_string(int status);
+
+/* Bytes of device workspace the entry point `op` needs for problem `p`
+ * (written to *bytes).  0 is a valid answer.  Validates `p` like the
+ * entry point does. */
+gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes);
+
+/* Bytes of the optional forward->backward buffer `saved` (written to
+ * *bytes).  Layout, fp32: A_t = K^_t beta_t K^_t^T as [B, H, T, Dk, Dk],
+ * followed by the states S_t after every frame as [B, H, T, Dv, Dk]. */
+gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
+
+/* Whole-sequence forward (module 2 recurrence over t = 1..T):
+ *   S_t = S_{t-1} (gamma_t I - K^_t beta_t K^_t^T) + V_t beta_t K^_t^T,
+ *   O_t = S_t Q^_t,  K^ = key_scale * K.
+ *   state_in   S_0; NULL => zero.
+ *   o          output [B, L, H, Dv], io dtype.
+ *   state_out  S_T; NULL => not written; may equal state_in (in place).
+ *   saved      NULL, or gdn_saved_size bytes that receive A_t and S_t for
+ *              gdn_backward.
+ *   workspace  gdn_workspace_size(p, GDN_OP_FORWARD) bytes of scratch. */
+gdn_status gdn_forward(const gdn_problem* p,
+                       const void* q, const void* k, const void* v,
+                       const float* gamma, const float* beta,
+                       const float* state_in,
+                       void* o, float* state_out, void* saved,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Streaming step: advance the carried state by one latent frame
+ * (p->T must be 1), as the chunk-by-chunk autoregressive variant does
+ * (CSDN explainer section 六, stage 4).  `state` [B, H, Dv, Dk] is read as
+ * S_{t-1} and overwritten with S_t; o receives O_t [B, N, H, Dv]. */
+gdn_status gdn_step(const gdn_problem* p,
+                    const void* q, const void* k, const void* v,
+                    const float* gamma, const float* beta,
+                    float* state, void* o,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reverse pass of gdn_forward (the pages give none; chain rule of the
+ * module-2 recurrence).  With G_t = dLoss/dS_t:
+ *   G_T = dO_T Q^_T^T + dS_T,   G_t = dO_t Q^_t^T + G_{t+1} M_{t+1}^T,
+ *   dQ^_t = S_t^T dO_t,  dM_t = S_{t-1}^T G_t,  dgamma_t = tr(dM_t),
+ *   dV_t = G_t K^_t beta_t,
+ *   dK_t = key_scale (G_t^T V_t beta_t - (dM_t + dM_t^T) K^_t beta_t),
+ *   dbeta_tn = v_tn^T G_t k^_tn - k^_tn^T dM_t k^_tn,  dS_0 = G_1 M_1^T.
+ *   state_in     S_0 of the forward; NULL => zero.
+ *   d_o          [B, L, H, Dv] io dtype.
+ *   d_state_out  dLoss/dS_T; NULL => zero.
+ *   saved        the buffer gdn_forward filled for the same inputs, or
+ *                NULL to recompute it inside the workspace.
+ *   dq, dk, dv   io dtype, layouts of q, k, v.  dgamma, dbeta fp32.
+ *   d_state_in   dLoss/dS_0; NULL => not written.
+ *   workspace    gdn_workspace_size(p, GDN_OP_BACKWARD) bytes. */
+gdn_status gdn_backward(const gdn_problem* p,
+                        const void* q, const void* k, const void* v,
+                        const float* gamma, const float* beta,
+                        const float* state_in,
+                        const void* d_o, const float* d_state_out,
+                        const void* saved,
+                        void* dq, void* dk, void* dv,
+                        float* dgamma, float* dbeta, float* d_state_in,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGDN_GDN_H */

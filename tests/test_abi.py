@@ -1,0 +1,98 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/gdn.h declares, and its host-side validation answers without any
+GPU work (every call here fails validation before a launch)."""
+
+import ctypes
+import os
+
+import pytest
+
+from gated_deltanet_recurrence_frame_amd import binding as gb
+
+LIB = gb.LIB_PATH
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libgdn.so is not built; run __graft_entry__.build()")
+    return gb.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = gb.header_functions()
+    assert set(names) == {"gdn_abi_version", "gdn_status_string", "gdn_workspace_size",
+                          "gdn_saved_size", "gdn_forward", "gdn_step", "gdn_backward"}
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the shared object's dynamic symbol table really carries them
+    cdll = ctypes.CDLL(LIB)
+    for n in names:
+        getattr(cdll, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for code in range(9):
+        s = lib.gdn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.gdn_status_string(99).decode() == "unknown status"
+
+
+def _ws(prob, op):
+    n = ctypes.c_size_t(0)
+    code = gb.lib().gdn_workspace_size(ctypes.byref(prob) if prob is not None else None, op,
+                                       ctypes.byref(n))
+    return code, n.value
+
+
+def test_workspace_sizes(lib):
+    B, H, T, N, D = 1, 20, 121, 880, 112
+    p = gb.make_problem(B, H, T, N, D, "bf16")
+    mat = B * H * T * D * D * 4
+    assert _ws(p, gb.GDN_OP_FORWARD) == (0, 3 * mat)
+    assert _ws(p, gb.GDN_OP_BACKWARD) == (0, 6 * mat)
+    assert gb.STATUS[_ws(p, gb.GDN_OP_STEP)[0]] == "GDN_ERR_BAD_SHAPE"     # T != 1
+    p1 = gb.make_problem(B, H, 1, N, D, "bf16")
+    assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 4)
+    assert gb.saved_size(p) == 2 * mat
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, "GDN_ERR_BAD_SHAPE"), ("T", -1, "GDN_ERR_BAD_SHAPE"),
+    ("N", 0, "GDN_ERR_BAD_SHAPE"), ("Dk", 24, "GDN_ERR_UNSUPPORTED"),
+    ("Dk", 144, "GDN_ERR_UNSUPPORTED"), ("Dv", 64, "GDN_ERR_UNSUPPORTED"),
+    ("io_dtype", 5, "GDN_ERR_BAD_DTYPE"), ("scan_chunk", -2, "GDN_ERR_BAD_SHAPE"),
+    ("key_scale", float("nan"), "GDN_ERR_BAD_SHAPE"),
+])
+def test_problem_validation(lib, field, value, status):
+    p = gb.make_problem(1, 2, 4, 8, 32, "bf16")
+    setattr(p, field, value)
+    code, _ = _ws(p, gb.GDN_OP_FORWARD)
+    assert gb.STATUS[code] == status
+
+
+def test_null_and_alignment_checks_before_any_launch(lib):
+    p = gb.make_problem(1, 2, 4, 8, 32, "fp32")
+    vp = ctypes.c_void_p
+    code = lib.gdn_forward(None, *([None] * 10), 0, None)
+    assert gb.STATUS[code] == "GDN_ERR_NULL_POINTER"
+    code = lib.gdn_forward(ctypes.byref(p), *([None] * 10), 0, None)
+    assert gb.STATUS[code] == "GDN_ERR_NULL_POINTER"
+    # fake, never dereferenced addresses: misalignment is caught first
+    good = [vp(0x100000 * (i + 1)) for i in range(10)]
+    bad = list(good)
+    bad[0] = vp(0x100008)
+    code = lib.gdn_forward(ctypes.byref(p), *bad, 1 << 30, None)
+    assert gb.STATUS[code] == "GDN_ERR_MISALIGNED"
+    code = lib.gdn_forward(ctypes.byref(p), *good, 16, None)
+    assert gb.STATUS[code] == "GDN_ERR_WORKSPACE_TOO_SMALL"
+    # the output overlapping an input
+    alias = list(good)
+    alias[6] = alias[0]
+    code = lib.gdn_forward(ctypes.byref(p), *alias, 1 << 30, None)
+    assert gb.STATUS[code] == "GDN_ERR_ALIASING"
+    code = lib.gdn_step(ctypes.byref(p), *([vp(0x1000)] * 8), 0, None)
+    assert gb.STATUS[code] == "GDN_ERR_BAD_SHAPE"                          # T != 1
+    code = lib.gdn_backward(ctypes.byref(p), *([None] * 16), 0, None)
+    assert gb.STATUS[code] == "GDN_ERR_NULL_POINTER"

@@ -1,0 +1,288 @@
+"""GPU parity of libgdn (through its C ABI) against the float64 oracle.
+
+Bars: relative L2 error per output tensor <= 1e-5 when the io dtype is fp32
+and <= 2e-2 when it is bf16.  Inputs come from the shared seeded generator;
+the oracle reads back the exact values the GPU sees (bf16 or fp32, upcast
+to float64).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_recurrence_frame_amd import binding as gb
+from gated_deltanet_recurrence_frame_amd import inputs as gin
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def rel_l2(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    return np.linalg.norm((gpu - ref).ravel()) / (den if den > 0 else 1.0)
+
+
+def to_dev(t):
+    return None if t is None else t.to(DEV).contiguous()
+
+
+def f64(t):
+    return gin.as_f64(t)
+
+
+def run_forward_pair(inp, N, io, key_scale=0.0, scan_chunk=0, with_state=False):
+    d = {k: to_dev(v) for k, v in inp.items()}
+    st = d.get("state") if with_state else None
+    o, so = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, state_in=st,
+                       key_scale=key_scale, scan_chunk=scan_chunk)
+    torch.cuda.synchronize()
+    ro, rs = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                            f64(inp["beta"]), N,
+                            state_in=f64(inp["state"]) if with_state else None,
+                            key_scale=key_scale)
+    return (o.cpu(), so.cpu()), (ro, rs)
+
+
+def check_forward(inp, N, io, **kw):
+    (o, so), (ro, rs) = run_forward_pair(inp, N, io, **kw)
+    eo, es = rel_l2(f64(o), ro), rel_l2(f64(so), rs)
+    print("forward rel_l2: o %.3e state %.3e" % (eo, es))
+    assert np.all(np.isfinite(f64(o)))
+    assert eo <= TOL[io], eo
+    assert es <= TOL[io], es
+    return eo, es
+
+
+# ---------------------------------------------------------------- forward
+def test_forward_tiny_fp32():
+    inp = gin.make_config("tiny", seed=0, with_state=True)
+    check_forward(inp, 4, "fp32")
+    check_forward(inp, 4, "fp32", with_state=True)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [16, 32, 48, 64, 112, 128])
+def test_forward_head_dims_ragged(io, D):
+    # several token chunks with a ragged tail (N = 100), two batches, odd H
+    inp = gin.make_inputs(B=2, H=3, T=5, N=100, D=D, io=io, gamma="uniform", seed=1,
+                          with_state=True)
+    check_forward(inp, 100, io, with_state=True)
+
+
+@pytest.mark.parametrize("N", [1, 3, 16, 37, 64, 65])
+def test_forward_token_counts_fp32(N):
+    inp = gin.make_inputs(B=1, H=2, T=6, N=N, D=112, io="fp32", gamma="sigmoid", seed=2)
+    check_forward(inp, N, "fp32")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_forward_short_clip_bf16(seed):
+    inp = gin.make_config("short", seed=seed)
+    eo, _ = check_forward(inp, 880, "bf16")
+    assert eo < 5e-3          # bf16 rounding of S_t and O only
+
+
+def test_forward_short_clip_fp32_mode():
+    inp = gin.make_config("short", seed=0, io="fp32")
+    check_forward(inp, 880, "fp32")
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_forward_delta_stress(io):
+    # key scale sqrt(Dk/N): the delta correction changes O by O(1), so a
+    # wrong or missing erase term cannot hide under the bf16 tolerance.
+    inp = gin.make_inputs(B=1, H=4, T=21, N=880, D=112, io=io, gamma="uniform", seed=3)
+    ks = float(np.sqrt(112 / 880))
+    check_forward(inp, 880, io, key_scale=ks)
+    # the erase term really matters at this scale
+    ro_off, _ = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                               f64(inp["beta"]), 880, key_scale=ks, erase=0.0)
+    ro_on, _ = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                              f64(inp["beta"]), 880, key_scale=ks)
+    assert rel_l2(ro_off, ro_on) > 0.5
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_exact_retrieval(io):
+    # gamma = 1, beta = 1, key scale 1, keys orthonormal in each frame, Q = K:
+    # every frame reads back its own values exactly (up to input rounding).
+    B, H, T, N, D = 1, 4, 6, 112, 112
+    k, v = gin.orthonormal_frame_keys(B, H, T, N, D, seed=4, io=io)
+    g = torch.ones((B, T, H))
+    beta = torch.ones((B, T * N, H))
+    kd, vd = to_dev(k), to_dev(v)
+    o, _ = gb.forward(kd, kd, vd, to_dev(g), to_dev(beta), N, key_scale=1.0)
+    ro, _ = oracle.forward(f64(k), f64(k), f64(v), f64(g), f64(beta), N, key_scale=1.0)
+    e_or = rel_l2(f64(o.cpu()), ro)
+    e_v = rel_l2(f64(o.cpu()), f64(v))
+    print("exact retrieval: vs oracle %.3e, vs V %.3e" % (e_or, e_v))
+    assert e_or <= TOL[io]
+    assert e_v <= (1e-4 if io == "fp32" else 3e-2)
+
+
+def test_saved_intermediates_fp32():
+    inp = gin.make_inputs(B=1, H=2, T=4, N=50, D=32, io="fp32", gamma="uniform", seed=5,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    o, so, saved = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], 50,
+                              state_in=d["state"], return_saved=True)
+    torch.cuda.synchronize()
+    _, _, kept = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                                f64(inp["beta"]), 50, state_in=f64(inp["state"]), keep=True)
+    sv = saved.view(torch.float32).cpu().numpy().astype(np.float64)
+    n = kept["A"].size
+    assert rel_l2(sv[:n].reshape(kept["A"].shape), kept["A"]) < 1e-5
+    assert rel_l2(sv[n:].reshape(kept["S"].shape), kept["S"]) < 1e-5
+
+
+def test_in_place_state():
+    inp = gin.make_inputs(B=1, H=2, T=3, N=20, D=16, io="fp32", gamma="uniform", seed=6,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    prob = gb.make_problem(1, 2, 3, 20, 16, "fp32")
+    o = torch.empty_like(d["v"])
+    ws = torch.empty(gb.workspace_size(prob, gb.GDN_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    st = d["state"].clone()
+    import ctypes
+    code = gb.lib().gdn_forward(ctypes.byref(prob), gb._p(d["q"]), gb._p(d["k"]), gb._p(d["v"]),
+                                gb._p(d["gamma"]), gb._p(d["beta"]), gb._p(st), gb._p(o),
+                                gb._p(st), None, gb._p(ws), ws.numel(), None)
+    assert code == 0
+    torch.cuda.synchronize()
+    _, rs = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                           f64(inp["beta"]), 20, state_in=f64(inp["state"]))
+    assert rel_l2(f64(st.cpu()), rs) < 1e-5
+
+
+# ------------------------------------------------------------- properties
+def test_deterministic_and_homogeneous_bf16():
+    inp = gin.make_inputs(B=1, H=4, T=7, N=200, D=112, io="bf16", gamma="uniform", seed=7)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    o1, s1 = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], 200)
+    o2, s2 = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], 200)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    # O is linear in V with S_0 = 0 and scaling by 2 commutes with rounding
+    o3, s3 = gb.forward(d["q"], d["k"], 2 * d["v"], d["gamma"], d["beta"], 200)
+    assert torch.equal(o3, 2 * o1) and torch.equal(s3, 2 * s1)
+
+
+def test_permutation_within_frames_fp32():
+    B, H, T, N, D = 1, 2, 4, 48, 32
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io="fp32", gamma="uniform", seed=8)
+    rng = np.random.default_rng(80)
+    perm = torch.from_numpy(np.concatenate([t * N + rng.permutation(N) for t in range(T)]))
+    d = {k: to_dev(v) for k, v in inp.items()}
+    o, s = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N)
+    p = perm.to(DEV)
+    op, sp = gb.forward(d["q"][:, p].contiguous(), d["k"][:, p].contiguous(),
+                        d["v"][:, p].contiguous(), d["gamma"], d["beta"][:, p].contiguous(), N)
+    assert rel_l2(f64(op.cpu()), f64(o[:, p].cpu())) < 1e-5
+    assert rel_l2(f64(sp.cpu()), f64(s.cpu())) < 1e-5
+
+
+# ------------------------------------------------------------------ step
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_step_chain_equals_forward(io):
+    B, H, T, N, D = 1, 3, 9, 130, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=9,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    o_full, s_full = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                                state_in=d["state"])
+    state = d["state"].clone()
+    outs = []
+    for t in range(T):
+        sl = slice(t * N, (t + 1) * N)
+        outs.append(gb.step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                            d["v"][:, sl].contiguous(), d["gamma"][:, t:t + 1].contiguous(),
+                            d["beta"][:, sl].contiguous(), state).clone())
+    torch.cuda.synchronize()
+    o_step = torch.cat(outs, dim=1)
+    # the step path runs the same kernels frame by frame: identical results
+    assert torch.equal(o_step, o_full)
+    assert torch.equal(state, s_full)
+    ro, rs = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                            f64(inp["beta"]), N, state_in=f64(inp["state"]))
+    assert rel_l2(f64(o_step.cpu()), ro) <= TOL[io]
+    assert rel_l2(f64(state.cpu()), rs) <= TOL[io]
+
+
+# -------------------------------------------------------------- backward
+def check_backward(inp, N, io, with_state=True, with_dstate=True, use_saved=False,
+                   key_scale=0.0):
+    d = {k: to_dev(v) for k, v in inp.items()}
+    st = d["state"] if with_state else None
+    dst = d["d_state"] if with_dstate else None
+    saved = None
+    if use_saved:
+        _, _, saved = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                                 state_in=st, key_scale=key_scale, return_saved=True)
+    gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                     state_in=st, d_state_out=dst, saved=saved, key_scale=key_scale)
+    torch.cuda.synchronize()
+    ref = oracle.backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                          f64(inp["beta"]), N, f64(inp["d_o"]),
+                          state_in=f64(inp["state"]) if with_state else None,
+                          d_state_out=f64(inp["d_state"]) if with_dstate else None,
+                          key_scale=key_scale)
+    errs = {}
+    for name in ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]:
+        errs[name] = rel_l2(f64(gr[name].cpu()), ref[name])
+    print("backward rel_l2:", {k: "%.2e" % v for k, v in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL[io], (name, e)
+    return errs
+
+
+def test_backward_tiny_fp32():
+    inp = gin.make_config("tiny", seed=0, with_do=True, with_dstate=True, with_state=True)
+    check_backward(inp, 4, "fp32")
+    check_backward(inp, 4, "fp32", with_state=False, with_dstate=False, use_saved=True)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [16, 64, 112])
+def test_backward_ragged(io, D):
+    inp = gin.make_inputs(B=2, H=3, T=5, N=100, D=D, io=io, gamma="uniform", seed=10,
+                          with_do=True, with_dstate=True, with_state=True)
+    check_backward(inp, 100, io)
+    check_backward(inp, 100, io, use_saved=True)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_backward_delta_stress(io):
+    inp = gin.make_inputs(B=1, H=2, T=12, N=880, D=112, io=io, gamma="uniform", seed=11,
+                          with_do=True, with_dstate=True, with_state=True)
+    check_backward(inp, 880, io, key_scale=float(np.sqrt(112 / 880)))
+
+
+def test_backward_short_clip_bf16():
+    inp = gin.make_config("short", seed=0, with_do=True)
+    check_backward(inp, 880, "bf16", with_state=False, with_dstate=False, use_saved=True)
+
+
+# ---------------------------------------------------- host-side failures
+def test_errors_write_nothing():
+    inp = gin.make_inputs(B=1, H=2, T=3, N=20, D=16, io="fp32", gamma="uniform", seed=12)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    import ctypes
+    prob = gb.make_problem(1, 2, 3, 20, 16, "fp32")
+    need = gb.workspace_size(prob, gb.GDN_OP_FORWARD)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = torch.full_like(d["v"], 7.0)
+    code = gb.lib().gdn_forward(ctypes.byref(prob), gb._p(d["q"]), gb._p(d["k"]), gb._p(d["v"]),
+                                gb._p(d["gamma"]), gb._p(d["beta"]), None, gb._p(o), None, None,
+                                gb._p(ws), need - 1, None)
+    assert gb.STATUS[code] == "GDN_ERR_WORKSPACE_TOO_SMALL"
+    # output aliasing an input
+    code = gb.lib().gdn_forward(ctypes.byref(prob), gb._p(d["q"]), gb._p(d["k"]), gb._p(d["v"]),
+                                gb._p(d["gamma"]), gb._p(d["beta"]), None, gb._p(d["q"]), None,
+                                None, gb._p(ws), need, None)
+    assert gb.STATUS[code] == "GDN_ERR_ALIASING"
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0)
