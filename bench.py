@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of libgdn's frame-wise GDN forward on one MI355X.
+
+One step = one gdn_forward over one GDN layer at the one-minute 720p shape
+(B = 1, 20 heads, D = 112, 121 latent frames x 880 tokens = 106,480 tokens,
+bf16 Q/K/V/O, fp32 gates and state), inputs resident in HBM.  Prints one JSON
+line: tokens/s, the roofline of the dominant kernel (phase times from HIP
+events recorded by the library between its kernels, on the stream they run
+on), and the float64 CPU oracle timed on a bounded sample of the same
+workload.  Extras: forward + backward at the same shape, and 121 streaming
+gdn_step calls.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN tokens/s per layer (20 heads, D=112) at 1-min 720p shape; % MFMA peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+SHAPE = dict(B=1, H=20, D=112, T=121, N=880)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_frame_amd", "csrc")
+KERNEL_SOURCES = {  # kernel -> source files its code depends on
+    "gram": ["gdn_gram.hip", "gdn_device.h", "gdn_internal.h"],
+    "scan": ["gdn_scan.hip", "gdn_device.h", "gdn_internal.h"],
+    "output": ["gdn_output.hip", "gdn_device.h", "gdn_internal.h"],
+}
+
+
+def source_sha(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(kernel, B, H, D, T, N):
+    """Bytes and dense-equivalent FLOPs the method must move / do in one
+    launch of each kernel (inputs read once, outputs written once; the
+    per-frame intermediates A_t, U_t, S_t are not counted)."""
+    tokens = B * T * N
+    heads_frames = B * H * T
+    if kernel == "gram":      # read K, V (bf16) and beta (fp32)
+        return tokens * H * (2 * D * 2 + 4), heads_frames * 2 * (2 * D * D * N)
+    if kernel == "output":    # read Q, write O (bf16)
+        return tokens * H * (2 * D * 2), heads_frames * 2 * D * D * N
+    if kernel == "scan":      # intermediates only
+        return 0, heads_frames * 2 * D * D * D
+    if kernel == "forward":
+        return tokens * H * (4 * D * 2 + 4), heads_frames * (3 * 2 * D * D * N + 2 * D * D * D)
+    raise KeyError(kernel)
+
+
+class HipEvents:
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def elapsed(self, i, j):
+        self.hip.hipEventSynchronize(ctypes.c_void_p(self.ev[j]))
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[i]),
+                                        ctypes.c_void_p(self.ev[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the kernel's current source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = tr.get(kernel)
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s):
+    """The float64 oracle, untouched, on whole heads of the same workload
+    until the time budget is spent; scaled to layer tokens/s."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from gated_deltanet_recurrence_frame_amd import inputs as gin
+    try:
+        from threadpoolctl import threadpool_info
+        cores = sum(p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas") or 1
+    except Exception:
+        cores = 1
+    H, N = SHAPE["H"], SHAPE["N"]
+    done, t_total = 0, 0.0
+    for h in range(H):
+        sl = slice(h, h + 1)
+        q, k, v = (gin.as_f64(inp[x][:, :, sl]) for x in ("q", "k", "v"))
+        g, b = gin.as_f64(inp["gamma"][:, :, sl]), gin.as_f64(inp["beta"][:, :, sl])
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, g, b, N)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    tokens = SHAPE["B"] * SHAPE["T"] * N
+    return {"value": tokens * (done / H) / t_total, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "float64 oracle forward on %d of %d heads (all 121 frames x 880 tokens), "
+                      "%.1f s, scaled by heads to one-layer tokens/s" % (done, H, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--scan-chunk", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_recurrence_frame_amd import binding as gb
+    from gated_deltanet_recurrence_frame_amd import inputs as gin
+
+    dev = torch.device("cuda:0")
+    B, H, D, T, N = (SHAPE[k] for k in ("B", "H", "D", "T", "N"))
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io="bf16", gamma="uniform", seed=0,
+                          with_do=not args.no_extras)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    torch.cuda.synchronize()
+
+    plan = gb.ForwardPlan(B, H, T, N, D, "bf16", dev, scan_chunk=args.scan_chunk)
+    ev = HipEvents(4 * args.steps)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    torch.cuda.synchronize()
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"], events=ev.ev[4 * i:4 * i + 4])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    phases = {"gram": 0.0, "scan": 0.0, "output": 0.0}
+    for i in range(args.steps):
+        phases["gram"] += ev.elapsed(4 * i, 4 * i + 1)
+        phases["scan"] += ev.elapsed(4 * i + 1, 4 * i + 2)
+        phases["output"] += ev.elapsed(4 * i + 2, 4 * i + 3)
+    phases = {k: v / args.steps for k, v in phases.items()}
+    tokens = B * T * N
+    value = tokens / (ms_step * 1e-3)
+
+    dom = max(("gram", "output"), key=lambda k: phases[k])
+    abytes, aflops = algorithmic(dom, B, H, D, T, N)
+    achieved = abytes / (phases[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(dom), "algorithmic_bytes": abytes,
+            "avg_ms": round(phases[dom], 4)}
+    fbytes, fflops = algorithmic("forward", B, H, D, T, N)
+    step_roof = {"bound": "hbm", "achieved": round(fbytes / (ms_step * 1e-3) / 1e9, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(fbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes": fbytes,
+                 "tflops": round(fflops / (ms_step * 1e-3) / 1e12, 2),
+                 "mfma_frac": round(fflops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    extra = {}
+    if not args.no_extras:
+        print("[bench] forward+backward", file=sys.stderr, flush=True)
+        extra["train"] = bench_train(gb, d, B, H, D, T, N, max(3, args.steps // 4))
+        print("[bench] streaming steps", file=sys.stderr, flush=True)
+        extra["stream"] = bench_stream(gb, d, B, H, D, T, N, ev)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdn_forward, one GDN layer at the 1-min 720p latent shape",
+                   "B": B, "H": H, "D": D, "T": T, "N": N, "tokens": tokens,
+                   "io": "bf16", "state": "fp32", "scan_chunk": args.scan_chunk},
+        "roofline": roof,
+        "step_roofline": step_roof,
+        "phases_ms": {k: round(v, 4) for k, v in phases.items()},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_train(gb, d, B, H, D, T, N, steps):
+    import torch
+    plan = gb.ForwardPlan(B, H, T, N, D, "bf16", d["q"].device, saved=True)
+    prob = plan.prob
+    ws = torch.empty(gb.workspace_size(prob, gb.GDN_OP_BACKWARD), dtype=torch.uint8,
+                     device=d["q"].device)
+    grads = None
+
+    def one():
+        nonlocal grads
+        plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+        grads = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                            saved=plan.saved, workspace=ws)
+    one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    tokens = B * T * N
+    nbytes = tokens * H * (7 * D * 2 + 8)       # Q,K,V,dO read; dQ,dK,dV write; beta, dbeta
+    return {"workload": "gdn_forward + gdn_backward (saved A_t, S_t), 1-min shape",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "steps": steps}
+
+
+def bench_stream(gb, d, B, H, D, T, N, ev):
+    import torch
+    dev = d["q"].device
+    state = torch.zeros((B, H, D, D), dtype=torch.float32, device=dev)
+    prob = gb.make_problem(B, H, 1, N, D, "bf16")
+    ws = torch.empty(gb.workspace_size(prob, gb.GDN_OP_STEP), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    frames = [(d["q"][:, t * N:(t + 1) * N], d["k"][:, t * N:(t + 1) * N],
+               d["v"][:, t * N:(t + 1) * N], d["gamma"][:, t:t + 1], d["beta"][:, t * N:(t + 1) * N])
+              for t in range(T)]
+    for f in frames[:3]:
+        gb.step(*f, state, out=o, workspace=ws)
+    state.zero_()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
+    evs[0].record(stream)
+    t0 = time.perf_counter()
+    for t, f in enumerate(frames):
+        gb.step(*f, state, out=o, workspace=ws)
+        evs[t + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat = sorted(evs[t].elapsed_time(evs[t + 1]) for t in range(T))
+    return {"workload": "frame 0 then 120 gdn_step calls (state carried), 880 tokens each",
+            "calls": T, "per_frame_ms_median": round(lat[T // 2], 4),
+            "per_frame_ms_p90": round(lat[int(T * 0.9)], 4),
+            "tokens_per_s": round(B * T * N / wall, 1)}
+
+
+if __name__ == "__main__":
+    main()

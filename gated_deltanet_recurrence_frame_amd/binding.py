@@ -62,6 +62,9 @@ def lib():
     L.gdn_saved_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     L.gdn_forward.restype = ctypes.c_int
     L.gdn_forward.argtypes = [P] + [_VP] * 10 + [ctypes.c_size_t, _VP]
+    L.gdn_forward_events.restype = ctypes.c_int
+    L.gdn_forward_events.argtypes = [P] + [_VP] * 10 + [ctypes.c_size_t, _VP,
+                                                         ctypes.POINTER(_VP)]
     L.gdn_step.restype = ctypes.c_int
     L.gdn_step.argtypes = [P] + [_VP] * 8 + [ctypes.c_size_t, _VP]
     L.gdn_backward.restype = ctypes.c_int
@@ -170,11 +173,17 @@ class ForwardPlan:
                       if saved else None)
         self.device = device
 
-    def __call__(self, q, k, v, gamma, beta, state_in=None):
-        _check(lib().gdn_forward(ctypes.byref(self.prob), _p(q), _p(k), _p(v), _p(gamma),
-                                 _p(beta), _p(state_in), _p(self.o), _p(self.state_out),
-                                 _p(self.saved), _p(self.ws), self.ws.numel(),
-                                 _stream(self.device)), "gdn_forward")
+    def __call__(self, q, k, v, gamma, beta, state_in=None, events=None):
+        """events: None, or 4 raw hipEvent_t handles (ints) recorded around
+        the Gram/write, scan and output kernels (gdn_forward_events)."""
+        args = (ctypes.byref(self.prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
+                _p(state_in), _p(self.o), _p(self.state_out), _p(self.saved), _p(self.ws),
+                self.ws.numel(), _stream(self.device))
+        if events is None:
+            _check(lib().gdn_forward(*args), "gdn_forward")
+        else:
+            ev = (_VP * 4)(*[_VP(int(e)) for e in events])
+            _check(lib().gdn_forward_events(*args, ev), "gdn_forward_events")
         return self.o, self.state_out
 
 

@@ -21,7 +21,8 @@ struct Shape {
   int es;            // bytes per io element
   float s;           // key scale
   int chunk;         // 1: sequential scan; >= 2: composite chunks
-  int64_t mat;       // bytes of one [B, H, T, D, D] fp32 buffer
+  int64_t mat;       // bytes of one [B, H, T] x D x D buffer of the intermediate
+                     // type (bf16 for bf16 io, fp32 for fp32 io)
   int64_t parts;     // composite chunks per sequence
 };
 
@@ -45,18 +46,14 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   s.s = p->key_scale != 0.f ? p->key_scale : (float)(1.0 / sqrt((double)s.D * (double)s.N));
   s.chunk = p->scan_chunk == 0 ? kDefaultChunk : p->scan_chunk;
   if (s.chunk > s.T) s.chunk = (int)s.T;
-  s.mat = s.B * s.H * s.T * s.D * s.D * 4;
+  s.mat = s.B * s.H * s.T * s.D * s.D * s.es;
   s.parts = (s.T + s.chunk - 1) / s.chunk;
   *sh = s;
   return GDN_OK;
 }
 
-int64_t chunk_bytes(const Shape& s) {
-  return s.chunk > 1 ? 2 * s.B * s.H * s.parts * s.D * s.D * 4 : 0;
-}
-
-int64_t forward_ws(const Shape& s) { return 3 * s.mat + chunk_bytes(s); }
-int64_t backward_ws(const Shape& s) { return 6 * s.mat + chunk_bytes(s); }
+int64_t forward_ws(const Shape& s) { return 3 * s.mat; }
+int64_t backward_ws(const Shape& s) { return 6 * s.mat; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
@@ -83,45 +80,50 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
 // Forward pipeline shared by gdn_forward and gdn_step.
+gdn_status record(void* const* events, int i, hipStream_t stream) {
+  if (!events) return GDN_OK;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), stream));
+}
+
 gdn_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                        const float* gamma, const float* beta, const float* state_in,
                        void* o, float* state_out, void* saved, void* workspace,
-                       hipStream_t stream) {
+                       hipStream_t stream, void* const* events = nullptr) {
   char* ws = static_cast<char*>(workspace);
-  float* A = saved ? static_cast<float*>(saved) : reinterpret_cast<float*>(ws);
-  float* S = saved ? reinterpret_cast<float*>(static_cast<char*>(saved) + s.mat)
-                   : reinterpret_cast<float*>(ws + s.mat);
-  float* U = reinterpret_cast<float*>(ws + 2 * s.mat);
-  char* chunk_ws = ws + 3 * s.mat;
+  void* A = saved ? saved : ws;
+  void* S = saved ? static_cast<char*>(saved) + s.mat : ws + s.mat;
+  void* U = ws + 2 * s.mat;
   const int nt = (int)(s.D / 16);
 
   GramArgs ga{};
   ga.x0 = k; ga.x1 = v; ga.y = k; ga.w = beta;
   ga.out0 = A; ga.out1 = U;
+  ga.layout0 = LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
   ga.scale0 = s.s * s.s; ga.scale1 = s.s;
   ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
-  gdn_status st = hip_status(launch_gram(ga, s.io, nt, 2, stream));
+  gdn_status st = record(events, 0, stream);
+  if (st != GDN_OK) return st;
+  st = hip_status(launch_gram(ga, s.io, nt, 2, stream));
+  if (st != GDN_OK) return st;
+  st = record(events, 1, stream);
   if (st != GDN_OK) return st;
 
-  if (s.chunk > 1) {
-    ChunkScanArgs ca{};
-    ca.A = A; ca.U = U; ca.gamma = gamma; ca.z0 = state_in; ca.emit = S; ca.zT = state_out;
-    ca.comp = reinterpret_cast<float*>(chunk_ws);
-    ca.hin = reinterpret_cast<float*>(chunk_ws + s.B * s.H * s.parts * s.D * s.D * 4);
-    ca.B = (int)s.B; ca.H = (int)s.H; ca.T = (int)s.T; ca.chunk = s.chunk;
-    st = hip_status(launch_chunk_scan(ca, nt, stream));
-  } else {
+  {
     ScanArgs sa{};
     sa.A = A; sa.U = U; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S; sa.zT = state_out;
     sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
-    st = hip_status(launch_scan(sa, nt, false, stream));
+    st = hip_status(launch_scan(sa, s.io, nt, false, stream));
   }
+  if (st != GDN_OK) return st;
+  st = record(events, 2, stream);
   if (st != GDN_OK) return st;
 
   OutArgs oa{};
   oa.tok = q; oa.mat = S; oa.out = o;
   oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
-  return hip_status(launch_output(oa, s.io, nt, stream));
+  st = hip_status(launch_output(oa, s.io, nt, stream));
+  if (st != GDN_OK) return st;
+  return record(events, 3, stream);
 }
 
 }  // namespace
@@ -170,10 +172,11 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes) {
   return GDN_OK;
 }
 
-gdn_status gdn_forward(const gdn_problem* p, const void* q, const void* k, const void* v,
-                       const float* gamma, const float* beta, const float* state_in,
-                       void* o, float* state_out, void* saved, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+static gdn_status forward_checked(const gdn_problem* p, const void* q, const void* k,
+                                  const void* v, const float* gamma, const float* beta,
+                                  const float* state_in, void* o, float* state_out, void* saved,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* const* events) {
   Shape s;
   gdn_status st = check_problem(p, &s);
   if (st != GDN_OK) return st;
@@ -196,7 +199,27 @@ gdn_status gdn_forward(const gdn_problem* p, const void* q, const void* k, const
     if (state_out != state_in && any_overlap(so, 1, ins, 6)) return GDN_ERR_ALIASING;
   }
   return run_forward(s, q, k, v, gamma, beta, state_in, o, state_out, saved, workspace,
-                     static_cast<hipStream_t>(stream));
+                     static_cast<hipStream_t>(stream), events);
+}
+
+gdn_status gdn_forward(const gdn_problem* p, const void* q, const void* k, const void* v,
+                       const float* gamma, const float* beta, const float* state_in,
+                       void* o, float* state_out, void* saved, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return forward_checked(p, q, k, v, gamma, beta, state_in, o, state_out, saved, workspace,
+                         workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_forward_events(const gdn_problem* p, const void* q, const void* k,
+                              const void* v, const float* gamma, const float* beta,
+                              const float* state_in, void* o, float* state_out, void* saved,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* events) {
+  if (!events) return GDN_ERR_NULL_POINTER;
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return GDN_ERR_NULL_POINTER;
+  return forward_checked(p, q, k, v, gamma, beta, state_in, o, state_out, saved, workspace,
+                         workspace_bytes, stream, events);
 }
 
 gdn_status gdn_step(const gdn_problem* p, const void* q, const void* k, const void* v,
@@ -244,19 +267,20 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   hipStream_t stream_ = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const int nt = (int)(s.D / 16);
-  const float* A;
-  const float* S;
+  const void* A;
+  const void* S;
   if (saved) {
-    A = static_cast<const float*>(saved);
-    S = reinterpret_cast<const float*>(static_cast<const char*>(saved) + s.mat);
+    A = saved;
+    S = static_cast<const char*>(saved) + s.mat;
   } else {
     // Recompute A_t and S_t with the forward's own kernels into the
     // workspace (layout of `saved`), without writing an output.
-    float* A_ = reinterpret_cast<float*>(ws);
-    float* S_ = reinterpret_cast<float*>(ws + s.mat);
-    float* U_ = reinterpret_cast<float*>(ws + 2 * s.mat);
+    void* A_ = ws;
+    void* S_ = ws + s.mat;
+    void* U_ = ws + 2 * s.mat;
     GramArgs ga{};
     ga.x0 = k; ga.x1 = v; ga.y = k; ga.w = beta; ga.out0 = A_; ga.out1 = U_;
+    ga.layout0 = LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
     ga.scale0 = s.s * s.s; ga.scale1 = s.s;
     ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
     st = hip_status(launch_gram(ga, s.io, nt, 2, stream_));
@@ -264,18 +288,19 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     ScanArgs sa{};
     sa.A = A_; sa.U = U_; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S_; sa.zT = nullptr;
     sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
-    st = hip_status(launch_scan(sa, nt, false, stream_));
+    st = hip_status(launch_scan(sa, s.io, nt, false, stream_));
     if (st != GDN_OK) return st;
     A = A_;
     S = S_;
   }
-  float* X = reinterpret_cast<float*>(ws + 3 * s.mat);
-  float* G = reinterpret_cast<float*>(ws + 4 * s.mat);
-  float* W = reinterpret_cast<float*>(ws + 5 * s.mat);
+  void* X = ws + 3 * s.mat;
+  void* G = ws + 4 * s.mat;
+  void* W = ws + 5 * s.mat;
 
   // X_t = dO_t Q^_t^T, the frame's own contribution to dLoss/dS_t.
   GramArgs gx{};
   gx.x0 = d_o; gx.x1 = nullptr; gx.y = q; gx.w = nullptr; gx.out0 = X; gx.out1 = nullptr;
+  gx.layout0 = LAYOUT_TILES; gx.layout1 = LAYOUT_TILES;
   gx.scale0 = 1.f; gx.scale1 = 0.f;
   gx.B = (int)s.B; gx.H = (int)s.H; gx.T = (int)s.T; gx.N = (int)s.N;
   st = hip_status(launch_gram(gx, s.io, nt, 1, stream_));
@@ -285,13 +310,13 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   ScanArgs ra{};
   ra.A = A; ra.U = X; ra.gamma = gamma; ra.z0 = d_state_out; ra.emit = G; ra.zT = d_state_in;
   ra.B = (int)s.B; ra.H = (int)s.H; ra.T = (int)s.T;
-  st = hip_status(launch_scan(ra, nt, true, stream_));
+  st = hip_status(launch_scan(ra, s.io, nt, true, stream_));
   if (st != GDN_OK) return st;
 
   DmArgs da{};
   da.S = S; da.s0 = state_in; da.G = G; da.W = W; da.dgamma = dgamma;
   da.B = (int)s.B; da.H = (int)s.H; da.T = (int)s.T;
-  st = hip_status(launch_dm(da, nt, stream_));
+  st = hip_status(launch_dm(da, s.io, nt, stream_));
   if (st != GDN_OK) return st;
 
   BwdTokArgs ba{};

@@ -11,8 +11,12 @@
 //   dbeta_n  = v_n . y_n - 1/2 k^_n . w_n   (= v^T G k^ - k^^T dM k^)
 // with k^ = s k.
 //
-// dm_kernel: one workgroup per frame forms dM_t with fp32 MFMA from S_{t-1}
-// and G_t staged in LDS, writes W_t and dgamma_t (a fixed-order block sum).
+// Per-frame matrices are in the intermediate type (bf16 for bf16 io, fp32
+// for fp32 io).
+// dm_kernel: one workgroup per frame forms dM_t on MFMA from S_{t-1} and G_t
+// staged in LDS (bf16: both operands read with the transposing LDS read;
+// fp32: 16x16x4 fp32 MFMA), writes W_t and dgamma_t (a fixed-order block
+// sum).
 // bwd_tok_kernel: one workgroup per frame, one wave per 16-feature tile.
 // Each wave keeps its rows of S_t^T, G_t, G_t^T and W_t as MFMA operands
 // in registers; K, V, dO and beta stream through LDS in token chunks.  The
@@ -25,13 +29,18 @@
 
 namespace gdn {
 
-template <int NT>
+template <int IO, int NT>
 __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
+  typedef typename Io<IO>::elem E;
+  constexpr bool BF = (IO == IO_BF16);
   constexpr int D = 16 * NT;
   constexpr int NCT = (NT + 3) / 4;
-  constexpr int LD = D + 1;
-  __shared__ __attribute__((aligned(16))) float Sl[D * LD];
-  __shared__ __attribute__((aligned(16))) float Gl[D * LD];
+  constexpr int KP = BF ? ((D + 31) / 32) * 32 : D;   // contraction rows, zero padded
+  constexpr int LD = D + 1;                           // padded fp32 row for dM
+  constexpr int IN_BYTES = 2 * KP * (BF ? D : LD) * (BF ? 2 : 4);
+  constexpr int DM_BYTES = D * LD * 4;
+  constexpr int SMEM = IN_BYTES > DM_BYTES ? IN_BYTES : DM_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ float red[256];
 
   const int total = a.B * a.T * a.H;
@@ -41,19 +50,39 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
   const int b = item / (a.H * a.T);
   const long DD = (long)D * D;
   const long bh = (long)b * a.H + h;
-  const float* Sp = t > 0 ? a.S + (bh * a.T + t - 1) * DD : (a.s0 ? a.s0 + bh * DD : nullptr);
-  const float* Gt = a.G + (bh * a.T + t) * DD;
+  const E* Sp = t > 0 ? static_cast<const E*>(a.S) + (bh * a.T + t - 1) * DD : nullptr;
+  const float* S0 = (t == 0 && a.s0) ? a.s0 + bh * DD : nullptr;
+  const E* Gt = static_cast<const E*>(a.G) + (bh * a.T + t) * DD;
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int g = lane >> 4, li = lane & 15;
 
+  // Stage S_{t-1} and G_t (intermediate type; S_0 rounded like the saved
+  // states) and accumulate dgamma_t = <S_{t-1}, G_t>.
+  E* Sl = reinterpret_cast<E*>(smem);
+  E* Gl = Sl + KP * (BF ? D : LD);
+  const int SLD = BF ? D : LD;
   float dot = 0.f;
-  for (int idx = tid; idx < D * D / 4; idx += 256) {
-    const f32x4 gv = reinterpret_cast<const f32x4*>(Gt)[idx];
-    const f32x4 sv = Sp ? reinterpret_cast<const f32x4*>(Sp)[idx] : zero4();
-    reinterpret_cast<f32x4*>(Gl)[idx] = gv;
-    reinterpret_cast<f32x4*>(Sl)[idx] = sv;
-    dot += sv[0] * gv[0] + sv[1] * gv[1] + sv[2] * gv[2] + sv[3] * gv[3];
+  for (int idx = tid; idx < KP * D; idx += 256) {
+    const int i = idx / D, j = idx % D;
+    float sv = 0.f, gv = 0.f;
+    if (i < D) {
+      gv = BF ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(Gt)[idx])
+              : reinterpret_cast<const float*>(Gt)[idx];
+      if (Sp)
+        sv = BF ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(Sp)[idx])
+                : reinterpret_cast<const float*>(Sp)[idx];
+      else if (S0)
+        sv = BF ? bf16_bits_to_f32(f32_to_bf16_bits(S0[idx])) : S0[idx];
+    }
+    if constexpr (BF) {
+      reinterpret_cast<uint16_t*>(Sl)[i * SLD + j] = f32_to_bf16_bits(sv);
+      reinterpret_cast<uint16_t*>(Gl)[i * SLD + j] = f32_to_bf16_bits(gv);
+    } else {
+      reinterpret_cast<float*>(Sl)[i * SLD + j] = sv;
+      reinterpret_cast<float*>(Gl)[i * SLD + j] = gv;
+    }
+    dot += sv * gv;
   }
   red[tid] = dot;
   block_sync();
@@ -69,24 +98,47 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
   for (int j = 0; j < NCT; ++j)
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt) acc[j][lt] = zero4();
+  if constexpr (BF) {
+    const uint16_t* S16 = reinterpret_cast<const uint16_t*>(Sl);
+    const uint16_t* G16 = reinterpret_cast<const uint16_t*>(Gl);
+#pragma unroll
+    for (int kb = 0; kb < KP / 32; ++kb) {
+      bf16x8 gb[NT];
+#pragma unroll
+      for (int lt = 0; lt < NT; ++lt) gb[lt] = lds_col_frag_bf16(G16, D, kb * 32, lt * 16);
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        const int jt = wave + 4 * j;
+        if (jt < NT) {
+          const bf16x8 af = lds_col_frag_bf16(S16, D, kb * 32, jt * 16);
+#pragma unroll
+          for (int lt = 0; lt < NT; ++lt) acc[j][lt] = mfma_bf16(af, gb[lt], acc[j][lt]);
+        }
+      }
+    }
+  } else {
+    const float* Sf = reinterpret_cast<const float*>(Sl);
+    const float* Gf = reinterpret_cast<const float*>(Gl);
 #pragma unroll 2
-  for (int kb = 0; kb < D / 4; ++kb) {
-    const int i = kb * 4 + g;
-    float gb[NT];
+    for (int kb = 0; kb < D / 4; ++kb) {
+      const int i = kb * 4 + g;
+      float gb[NT];
 #pragma unroll
-    for (int lt = 0; lt < NT; ++lt) gb[lt] = Gl[i * D + lt * 16 + li];
+      for (int lt = 0; lt < NT; ++lt) gb[lt] = Gf[i * LD + lt * 16 + li];
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int jt = wave + 4 * j;
-      if (jt < NT) {
-        const float av = Sl[i * D + jt * 16 + li];
+      for (int j = 0; j < NCT; ++j) {
+        const int jt = wave + 4 * j;
+        if (jt < NT) {
+          const float av = Sf[i * LD + jt * 16 + li];
 #pragma unroll
-        for (int lt = 0; lt < NT; ++lt) acc[j][lt] = mfma_f32(av, gb[lt], acc[j][lt]);
+          for (int lt = 0; lt < NT; ++lt) acc[j][lt] = mfma_f32(av, gb[lt], acc[j][lt]);
+        }
       }
     }
   }
   block_sync();
-  // Stage dM (padded rows) and emit W = dM + dM^T.
+  // Stage dM (padded fp32 rows) and emit W = dM + dM^T.
+  float* dm = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int j = 0; j < NCT; ++j) {
     const int jt = wave + 4 * j;
@@ -94,14 +146,18 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
 #pragma unroll
       for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sl[(jt * 16 + 4 * g + r) * LD + lt * 16 + li] = acc[j][lt][r];
+        for (int r = 0; r < 4; ++r) dm[(jt * 16 + 4 * g + r) * LD + lt * 16 + li] = acc[j][lt][r];
     }
   }
   block_sync();
-  float* Wt = a.W + (bh * a.T + t) * DD;
+  E* Wt = static_cast<E*>(a.W) + (bh * a.T + t) * DD;
   for (int idx = tid; idx < D * D; idx += 256) {
     const int j = idx / D, l = idx % D;
-    Wt[idx] = Sl[j * LD + l] + Sl[l * LD + j];
+    const float w = dm[j * LD + l] + dm[l * LD + j];
+    if constexpr (BF)
+      reinterpret_cast<uint16_t*>(Wt)[idx] = f32_to_bf16_bits(w);
+    else
+      reinterpret_cast<float*>(Wt)[idx] = w;
   }
 }
 
@@ -135,10 +191,11 @@ __global__ __launch_bounds__(64 * NT) void bwd_tok_kernel(BwdTokArgs a) {
   const int g = lane >> 4, li = lane & 15;
   const float s = a.s;
 
-  // Operand rows of this wave's feature tile: S_t^T, G, G^T, W.
-  const float* St = a.S + moff;
-  const float* Gt = a.G + moff;
-  const float* Wt = a.W + moff;
+  // Operand rows of this wave's feature tile: S_t^T, G, G^T, W
+  // (intermediate type, row-major in memory).
+  const E* St = static_cast<const E*>(a.S) + moff;
+  const E* Gt = static_cast<const E*>(a.G) + moff;
+  const E* Wt = static_cast<const E*>(a.W) + moff;
   const int fr = ft * 16 + li;
   typedef typename std::conditional<IO == IO_BF16, bf16x8, float>::type Frag;
   Frag mS[KB], mG[KB], mGT[KB], mW[KB];
@@ -147,18 +204,16 @@ __global__ __launch_bounds__(64 * NT) void bwd_tok_kernel(BwdTokArgs a) {
     if constexpr (IO == IO_BF16) {
       const int k = kb * 32 + 8 * g;
       if (k < D) {
-        float vs[8], vg[8], vgt[8], vw[8];
+        i16x8 vs, vgt;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          vs[e] = St[(k + e) * D + fr];
-          vg[e] = Gt[fr * D + k + e];
-          vgt[e] = Gt[(k + e) * D + fr];
-          vw[e] = Wt[fr * D + k + e];
+          vs[e] = (short)St[(k + e) * D + fr];
+          vgt[e] = (short)Gt[(k + e) * D + fr];
         }
-        mS[kb] = f32x8_to_bf16x8(vs);
-        mG[kb] = f32x8_to_bf16x8(vg);
-        mGT[kb] = f32x8_to_bf16x8(vgt);
-        mW[kb] = f32x8_to_bf16x8(vw);
+        mS[kb] = __builtin_bit_cast(bf16x8, vs);
+        mGT[kb] = __builtin_bit_cast(bf16x8, vgt);
+        mG[kb] = load_bf16x8(Gt + fr * D + k);
+        mW[kb] = load_bf16x8(Wt + fr * D + k);
       } else {
         mS[kb] = mG[kb] = mGT[kb] = mW[kb] = zero_bf16x8();
       }
@@ -314,24 +369,29 @@ __global__ __launch_bounds__(64 * NT) void bwd_tok_kernel(BwdTokArgs a) {
   }
 }
 
-template <int NT>
+template <int IO, int NT>
 static hipError_t launch_dm_nt(const DmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((dm_kernel<NT>), dim3(a.B * a.T * a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((dm_kernel<IO, NT>), dim3(a.B * a.T * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_dm(const DmArgs& a, int nt, hipStream_t s) {
+template <int IO>
+static hipError_t launch_dm_io(const DmArgs& a, int nt, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_dm_nt<1>(a, s);
-    case 2: return launch_dm_nt<2>(a, s);
-    case 3: return launch_dm_nt<3>(a, s);
-    case 4: return launch_dm_nt<4>(a, s);
-    case 5: return launch_dm_nt<5>(a, s);
-    case 6: return launch_dm_nt<6>(a, s);
-    case 7: return launch_dm_nt<7>(a, s);
-    case 8: return launch_dm_nt<8>(a, s);
+    case 1: return launch_dm_nt<IO, 1>(a, s);
+    case 2: return launch_dm_nt<IO, 2>(a, s);
+    case 3: return launch_dm_nt<IO, 3>(a, s);
+    case 4: return launch_dm_nt<IO, 4>(a, s);
+    case 5: return launch_dm_nt<IO, 5>(a, s);
+    case 6: return launch_dm_nt<IO, 6>(a, s);
+    case 7: return launch_dm_nt<IO, 7>(a, s);
+    case 8: return launch_dm_nt<IO, 8>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s) {
+  return io == IO_BF16 ? launch_dm_io<IO_BF16>(a, nt, s) : launch_dm_io<IO_F32>(a, nt, s);
 }
 
 template <int IO, int NT>

@@ -13,6 +13,10 @@
 // All tokens of a frame read the same S_{t-1}, so there is no intra-frame
 // triangular structure: the contraction is a dense D x N x D product.
 //
+// Outputs are stored in the intermediate type (bf16 for bf16 io, fp32 for
+// fp32 io): A_t row-major, U_t and dO_t Q^_t^T in the MFMA tile layout that
+// the scan consumes.
+//
 // Layout of the work: one workgroup (4 waves) per (b, t, h), XCD-aware
 // ordering so heads of one frame run on one XCD.  Tokens stream through LDS
 // in chunks of CT rows (natural [token][feature] layout, double-buffered,
@@ -46,7 +50,8 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   typedef GramCfg<IO, NT, NR, Y_IS_X0> C;
   typedef typename Io<IO>::elem E;
   constexpr int D = C::D;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  constexpr int SMEM = (2 * C::STAGE_BYTES > D * D * C::ES) ? 2 * C::STAGE_BYTES : D * D * C::ES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int total = a.B * a.T * a.H;
   const int item = xcd_item(blockIdx.x, total);
@@ -187,20 +192,63 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   }
 
   // Epilogue: C[m][n] lives in lane (g, n) register r with m = 4g + r.
+  // Outputs are in the intermediate type (the io type).  The tiles layout
+  // is written straight from the accumulators (4 contiguous values per
+  // lane); a row-major output is staged through LDS (the chunk buffers are
+  // free after the last barrier) and stored in 16-byte pieces.
   const long obase = (((long)b * a.H + h) * a.T + t) * (long)(D * D);
 #pragma unroll
   for (int j = 0; j < C::RT; ++j) {
     const int rtg = wave + 4 * j;
     if (rtg < NR * NT) {
       const int m = rtg / NT, ft = rtg % NT;
-      float* out = (m == 0 ? a.out0 : a.out1) + obase;
-      const float sc = (m == 0 ? a.scale0 : a.scale1);
+      if ((m == 0 ? a.layout0 : a.layout1) == LAYOUT_TILES) {
+        E* out = static_cast<E*>(m == 0 ? a.out0 : a.out1) + obase;
+        const float sc = (m == 0 ? a.scale0 : a.scale1);
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          out[(ft * 16 + 4 * g + r) * D + ct * 16 + li] = sc * acc[j][ct][r];
+        for (int ct = 0; ct < NT; ++ct) {
+          E* dst = out + ((ft * NT + ct) * 64 + lane) * 4;
+          const f32x4 v = sc * acc[j][ct];
+          if constexpr (IO == IO_BF16) {
+            u32x2 pk;
+            pk[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+            pk[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<u32x2*>(dst) = pk;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          }
+        }
+      }
     }
+  }
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    if ((m == 0 ? a.layout0 : a.layout1) != LAYOUT_ROWMAJOR) continue;
+    E* stage = reinterpret_cast<E*>(smem);
+    const float sc = (m == 0 ? a.scale0 : a.scale1);
+#pragma unroll
+    for (int j = 0; j < C::RT; ++j) {
+      const int rtg = wave + 4 * j;
+      if (rtg < NR * NT && rtg / NT == m) {
+        const int ft = rtg % NT;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = sc * acc[j][ct][r];
+            E* dst = stage + (ft * 16 + 4 * g + r) * D + ct * 16 + li;
+            if constexpr (IO == IO_BF16)
+              *dst = f32_to_bf16_bits(v);
+            else
+              *dst = v;
+          }
+      }
+    }
+    block_sync();
+    u32x4* out = reinterpret_cast<u32x4*>(static_cast<E*>(m == 0 ? a.out0 : a.out1) + obase);
+    for (int idx = tid; idx < D * D * C::ES / 16; idx += 256)
+      out[idx] = reinterpret_cast<const u32x4*>(stage)[idx];
+    block_sync();
   }
 }
 

@@ -7,14 +7,24 @@
 
 namespace gdn {
 
+// Per-frame D x D intermediates are stored in the "intermediate type": bf16
+// when the io dtype is bf16, fp32 when it is fp32.  Two layouts:
+//   row-major  [D][D];
+//   tiles      [D/16][D/16][64][4]: 16x16 tile (I, J), lane (g, i) holds
+//              the elements [16 I + 4 g + r][16 J + i], r = 0..3 (the MFMA
+//              accumulator layout, so a consumer in the same layout reads
+//              4 contiguous values per lane).
+enum MatLayout { LAYOUT_ROWMAJOR = 0, LAYOUT_TILES = 1 };
+
 // Token contraction C_r = scale_r X_r^T diag(w) Y per (b, t, h) frame.
 struct GramArgs {
   const void* x0;      // [B, L, H, D] io dtype
   const void* x1;      // second row operand (NR == 2) or unused
   const void* y;       // column operand (NR == 1); NR == 2 uses x0
   const float* w;      // [B, L, H] per-token weights, or nullptr for 1
-  float* out0;         // [B, H, T, D, D]
-  float* out1;         // [B, H, T, D, D] (NR == 2)
+  void* out0;          // [B, H, T] x D x D, intermediate type, layout0
+  void* out1;          // [B, H, T] x D x D, intermediate type, layout1 (NR == 2)
+  int layout0, layout1;
   float scale0, scale1;
   int B, H, T, N;
 };
@@ -24,37 +34,23 @@ hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s)
 //   forward  (reverse = 0), t = 0..T-1:  Z <- gamma_t Z - Z A_t + U_t; emit Z
 //   backward (reverse = 1), t = T-1..0:  Z <- Z + U_t; emit Z;
 //                                        Z <- gamma_t Z - Z A_t
-// z0 / zT: [B, H, D, D] initial / final Z (nullptr: zero / not written).
+// z0 / zT: [B, H, D, D] fp32 initial / final Z (nullptr: zero / not written).
 struct ScanArgs {
-  const float* A;       // [B, H, T, D, D]
-  const float* U;       // [B, H, T, D, D]
+  const void* A;        // [B, H, T] x D x D row-major, intermediate type
+  const void* U;        // [B, H, T] x D x D tiles, intermediate type
   const float* gamma;   // [B, T, H]
   const float* z0;
-  float* emit;          // [B, H, T, D, D] fp32
+  void* emit;           // [B, H, T] x D x D row-major, intermediate type
   float* zT;
   int B, H, T;
 };
-hipError_t launch_scan(const ScanArgs& a, int nt, bool reverse, hipStream_t s);
-
-// Composite (chunked) forward scan: chunks of `chunk` frames.
-struct ChunkScanArgs {
-  const float* A;       // [B, H, T, D, D]
-  const float* U;       // [B, H, T, D, D]
-  const float* gamma;   // [B, T, H]
-  const float* z0;      // [B, H, D, D] or nullptr
-  float* emit;          // [B, H, T, D, D] states S_t
-  float* zT;            // [B, H, D, D] or nullptr
-  float* comp;          // [B, H, P, D, D] transition composites (workspace)
-  float* hin;           // [B, H, P, D, D] input composites, then incoming states
-  int B, H, T, chunk;
-};
-hipError_t launch_chunk_scan(const ChunkScanArgs& a, int nt, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, int io, int nt, bool reverse, hipStream_t s);
 
 // Token-stream products with per-frame D x D matrices, one wave per output
 // feature tile.  Forward output: O_t = S_t Q^_t.
 struct OutArgs {
   const void* tok;      // Q [B, L, H, D]
-  const float* mat;     // S_t [B, H, T, D, D]
+  const void* mat;      // S_t [B, H, T] x D x D row-major, intermediate type
   void* out;            // O [B, L, H, D]
   int B, H, T, N;
 };
@@ -63,14 +59,14 @@ hipError_t launch_output(const OutArgs& a, int io, int nt, hipStream_t s);
 // Backward, per frame: W_t = dM_t + dM_t^T with dM_t = S_{t-1}^T G_t, and
 // dgamma_t = tr(dM_t).
 struct DmArgs {
-  const float* S;       // [B, H, T, D, D] states after each frame
-  const float* s0;      // [B, H, D, D] initial state or nullptr (zero)
-  const float* G;       // [B, H, T, D, D]
-  float* W;             // [B, H, T, D, D]
+  const void* S;        // states after each frame, row-major, intermediate type
+  const float* s0;      // [B, H, D, D] fp32 initial state or nullptr (zero)
+  const void* G;        // row-major, intermediate type
+  void* W;              // row-major, intermediate type
   float* dgamma;        // [B, T, H]
   int B, H, T;
 };
-hipError_t launch_dm(const DmArgs& a, int nt, hipStream_t s);
+hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s);
 
 // Backward, per frame, token pass: dQ, dK, dV, dbeta.
 struct BwdTokArgs {
@@ -78,9 +74,9 @@ struct BwdTokArgs {
   const void* v;
   const void* d_o;
   const float* beta;    // [B, L, H]
-  const float* S;       // [B, H, T, D, D] states after each frame
-  const float* G;       // [B, H, T, D, D]
-  const float* W;       // [B, H, T, D, D]
+  const void* S;        // states after each frame, row-major, intermediate type
+  const void* G;        // row-major, intermediate type
+  const void* W;        // row-major, intermediate type
   void* dq;
   void* dk;
   void* dv;

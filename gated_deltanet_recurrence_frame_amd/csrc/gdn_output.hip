@@ -40,22 +40,17 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   const int lane = lane_id(), ft = wave_id();
   const int g = lane >> 4, li = lane & 15;
 
-  // This wave's rows of S_t as left MFMA operands.
-  const float* Sm = a.mat + (((long)b * a.H + h) * a.T + t) * (long)(D * D) + (ft * 16 + li) * D;
+  // This wave's rows of S_t (intermediate type, row-major) as left MFMA
+  // operands.
+  const E* Sm = static_cast<const E*>(a.mat) + (((long)b * a.H + h) * a.T + t) * (long)(D * D) +
+                (ft * 16 + li) * D;
   typedef typename std::conditional<IO == IO_BF16, bf16x8, float>::type Frag;
   Frag sf[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     if constexpr (IO == IO_BF16) {
       const int k = kb * 32 + 8 * g;
-      if (k < D) {
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(Sm + k);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(Sm + k + 4);
-        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        sf[kb] = f32x8_to_bf16x8(v);
-      } else {
-        sf[kb] = zero_bf16x8();
-      }
+      sf[kb] = (k < D) ? load_bf16x8(Sm + k) : zero_bf16x8();
     } else {
       sf[kb] = Sm[kb * 4 + g];
     }

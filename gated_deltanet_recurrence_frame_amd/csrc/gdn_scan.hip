@@ -4,184 +4,222 @@
 // (summary page: 前置知识 "Gated DeltaNet" and 方法步骤详情 module 2) is
 // evaluated as S_t = gamma_t S_{t-1} - S_{t-1} A_t + U_t.  M_t itself is
 // never formed: at the default key scale A_t is ~1e-4 while gamma_t ~ 1,
-// so gamma_t I - A_t in fp32 would discard most of A_t's bits.
+// so gamma_t I - A_t would discard most of A_t's bits.
 //
 // Rows of S evolve independently (row i of S_t depends only on row i of
 // S_{t-1}), so a workgroup owns 16 rows of one head's state and walks all T
-// frames; B*H*(D/16) workgroups run side by side.  Each of the 4 waves owns
-// up to two 16x16 column tiles of the rows, kept in registers in fp32.  Per
-// frame the rows are staged in LDS (the left operand of Z A_t, fp32 MFMA
-// 16x16x4), A_t is staged in LDS (double-buffered; the next frame's A and
-// U are prefetched into registers during the current frame's product), and
-// one barrier separates consecutive frames.
+// frames; the B*H*(D/16) workgroups of a launch are ordered so that the
+// row blocks of one head share an XCD (and its L2 copy of A_t).  One wave
+// per 16-column tile keeps its 16x16 tile of the state in fp32 registers.
+// Per frame:
+//   1. the tile is rounded to the intermediate type and staged in LDS, one
+//      barrier, and every wave reads the 16 staged rows as the left MFMA
+//      operand (the staged rows are also what is stored as S_{t-1});
+//   2. P = Z A_t on MFMA (bf16 16x16x32, or fp32 16x16x4 for fp32 io).  A_t
+//      is symmetric, so the right operand "column" k of tile j is row
+//      16 j + i of A_t: each lane loads contiguous row pieces of A_t straight
+//      from memory into registers;
+//   3. Z <- gamma_t Z - P + U_t in fp32.
+// The A_t pieces, the U_t tile and gamma_t of the next PD frames are in
+// flight in a register ring while the current frame is processed, so the
+// per-frame chain does not wait on memory latency.
 //
-// The same kernel runs the reverse scan of the backward pass (adjoint of the
-// recurrence, G_t = dO_t Q^_t^T + G_{t+1} M_{t+1}^T): there the input is
-// added first, the sum is emitted, and then multiplied by M_t.
+// The reverse scan of the backward pass (adjoint of the recurrence,
+// G_t = dO_t Q^_t^T + G_{t+1} M_{t+1}^T) runs the same code backwards in t:
+// the input is added first, the sum is staged and stored, then multiplied
+// by M_t.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-template <int NT, bool REVERSE>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+template <int IO, int NT, bool REVERSE>
+__global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
+  typedef typename Io<IO>::elem E;
+  constexpr bool BF = (IO == IO_BF16);
   constexpr int D = 16 * NT;
-  constexpr int NCT = (NT + 3) / 4;         // column tiles per wave
-  constexpr int ZLD = D + 1;                // padded LDS row of the staged rows
-  constexpr int AV4 = D * D / 4;            // float4 pieces of A_t
-  constexpr int APT = (AV4 + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float Abuf[2][D * D];
-  __shared__ float Zbuf[2][16 * ZLD];
+  constexpr int ES = Io<IO>::bytes;
+  constexpr int KB = BF ? (D + 31) / 32 : D / 4;   // MFMA steps of one product
+  constexpr int NAF = BF ? KB : D / 16;            // A pieces per lane per frame
+  constexpr int PD = BF ? 8 : 3;                   // frames in flight
+  constexpr int ZLD = BF ? D + 8 : D + 4;          // LDS row, a 16-byte multiple
+  constexpr int GW = 512;                          // gamma window held in LDS
+  constexpr int NTH = 64 * NT;
+  typedef typename std::conditional<BF, bf16x8, f32x4>::type AF;
+  typedef typename std::conditional<BF, u32x2, f32x4>::type UF;
+  struct Buf {
+    AF af[NAF];
+    UF u;
+  };
+  __shared__ __attribute__((aligned(16))) E Zbuf[2][16 * ZLD];
+  __shared__ float gam_lds[GW];
 
-  const int bh = blockIdx.x / NT, rb = blockIdx.x % NT;
+  const int total = a.B * a.H * NT;
+  const int item = xcd_item(blockIdx.x, total);
+  const int bh = item / NT, rb = item % NT;
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const int lane = lane_id(), wave = wave_id();
+  const int lane = lane_id(), ct = wave_id();
   const int g = lane >> 4, li = lane & 15;
   const long DD = (long)D * D;
-  const long mbase = (long)bh * a.T * DD;
   const int T = a.T;
+  const E* Ab = static_cast<const E*>(a.A) + (long)bh * T * DD;
+  const E* Ub = static_cast<const E*>(a.U) + (long)bh * T * DD;
+  E* Eb = static_cast<E*>(a.emit) + (long)bh * T * DD;
 
-  f32x4 z[NCT];
+  f32x4 z = zero4();
+  if (a.z0) {
 #pragma unroll
-  for (int j = 0; j < NCT; ++j) {
-    z[j] = zero4();
-    const int ct = wave + 4 * j;
-    if (ct < NT && a.z0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        z[j][r] = a.z0[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li];
-    }
+    for (int r = 0; r < 4; ++r) z[r] = a.z0[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li];
   }
 
-  f32x4 apre[APT];
-  f32x4 upre[NCT];
-  float gpre = 0.f;
-  auto prefetch = [&](int t) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.A + mbase + t * DD);
+  auto frame_of = [&](int s) { return REVERSE ? T - 1 - s : s; };
+  auto load = [&](Buf& B, int s) {
+    const int t = frame_of(s < T ? s : T - 1);
+    const E* At = Ab + t * DD + (ct * 16 + li) * D;
+    if constexpr (BF) {
 #pragma unroll
-    for (int j = 0; j < APT; ++j) {
-      const int idx = tid + 256 * j;
-      if (idx < AV4) apre[j] = src[idx];
-    }
-    const float* Ut = a.U + mbase + t * DD;
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int ct = wave + 4 * j;
-      if (ct < NT) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) upre[j][r] = Ut[(rb * 16 + 4 * g + r) * D + ct * 16 + li];
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k = kb * 32 + 8 * g;
+        B.af[kb] = (k < D) ? load_bf16x8(At + k) : zero_bf16x8();
       }
-    }
-    gpre = a.gamma[((long)b * T + t) * a.H + h];
-  };
-  auto emit = [&](int t) {
-    float* dst = a.emit + mbase + t * DD;
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int ct = wave + 4 * j;
-      if (ct < NT) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(rb * 16 + 4 * g + r) * D + ct * 16 + li] = z[j][r];
-      }
-    }
-  };
-
-  prefetch(REVERSE ? T - 1 : 0);
-  for (int s = 0; s < T; ++s) {
-    const int t = REVERSE ? T - 1 - s : s;
-    const int cur = s & 1;
-    f32x4 u[NCT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) u[j] = upre[j];
-    const float gam = gpre;
-
-    if constexpr (REVERSE) {
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) z[j] += u[j];
-      emit(t);
-    }
-    // Stage the left operand (this block's rows of Z) and A_t.
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int ct = wave + 4 * j;
-      if (ct < NT) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Zbuf[cur][(4 * g + r) * ZLD + ct * 16 + li] = z[j][r];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < APT; ++j) {
-      const int idx = tid + 256 * j;
-      if (idx < AV4) reinterpret_cast<f32x4*>(Abuf[cur])[idx] = apre[j];
-    }
-    block_sync();
-    if (s + 1 < T) prefetch(REVERSE ? t - 1 : t + 1);
-
-    // P = Z[rows] A_t
-    f32x4 p[NCT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) p[j] = zero4();
-    const float* zrow = &Zbuf[cur][li * ZLD + g];
-    const float* acol = &Abuf[cur][g * D + li];
-#pragma unroll 4
-    for (int kb = 0; kb < D / 4; ++kb) {
-      const float av = zrow[kb * 4];
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const int ct = wave + 4 * j;
-        if (ct < NT) p[j] = mfma_f32(av, acol[kb * 4 * D + ct * 16], p[j]);
-      }
-    }
-    if constexpr (!REVERSE) {
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) z[j] = gam * z[j] - p[j] + u[j];
-      emit(t);
+      B.u = *reinterpret_cast<const u32x2*>(Ub + t * DD + ((rb * NT + ct) * 64 + lane) * 4);
     } else {
 #pragma unroll
-      for (int j = 0; j < NCT; ++j) z[j] = gam * z[j] - p[j];
+      for (int q = 0; q < NAF; ++q)
+        B.af[q] = *reinterpret_cast<const f32x4*>(At + g * (D / 4) + 4 * q);
+      B.u = *reinterpret_cast<const f32x4*>(Ub + t * DD + ((rb * NT + ct) * 64 + lane) * 4);
+    }
+  };
+  auto unpack_u = [&](const Buf& B) -> f32x4 {
+    if constexpr (BF) {
+      f32x4 r;
+      r[0] = bf16_bits_to_f32((uint16_t)(B.u[0] & 0xffff));
+      r[1] = bf16_bits_to_f32((uint16_t)(B.u[0] >> 16));
+      r[2] = bf16_bits_to_f32((uint16_t)(B.u[1] & 0xffff));
+      r[3] = bf16_bits_to_f32((uint16_t)(B.u[1] >> 16));
+      return r;
+    } else {
+      return B.u;
+    }
+  };
+  auto stage = [&](int cur) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      E* dst = &Zbuf[cur][(4 * g + r) * ZLD + ct * 16 + li];
+      if constexpr (BF)
+        *dst = f32_to_bf16_bits(z[r]);
+      else
+        *dst = z[r];
+    }
+  };
+  auto emit_rows = [&](int cur, int t) {   // the 16 staged rows -> S_t / G_t
+    constexpr int PRW = D * ES / 16, NP = 16 * PRW;
+    for (int p = tid; p < NP; p += NTH) {
+      const int row = p / PRW, pc = p % PRW;
+      *reinterpret_cast<u32x4*>(Eb + t * DD + (rb * 16 + row) * D + pc * (16 / ES)) =
+          *reinterpret_cast<const u32x4*>(&Zbuf[cur][row * ZLD + pc * (16 / ES)]);
+    }
+  };
+  auto load_gammas = [&](int s0) {
+    for (int i = tid; i < GW; i += NTH) {
+      const int s = s0 + i;
+      gam_lds[i] = s < T ? a.gamma[((long)b * T + frame_of(s)) * a.H + h] : 0.f;
+    }
+  };
+
+  Buf ring[PD];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) load(ring[j], j);
+
+  for (int s0 = 0; s0 < T; s0 += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      const int s = s0 + j;
+      if (s < T) {
+        const int cur = s & 1;
+        const int t = frame_of(s);
+        if (s % GW == 0) {
+          block_sync();
+          load_gammas(s);
+        }
+        const f32x4 u = unpack_u(ring[j]);
+        if constexpr (REVERSE) z += u;
+        stage(cur);
+        block_sync();
+        const float gam = gam_lds[s % GW];
+        if constexpr (REVERSE)
+          emit_rows(cur, t);
+        else if (s > 0)
+          emit_rows(cur, t - 1);
+        // P = Z[rows] A_t
+        f32x4 p = zero4();
+        const E* zrow = &Zbuf[cur][li * ZLD];
+        if constexpr (BF) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int k = kb * 32 + 8 * g;
+            const bf16x8 zf = (k < D) ? load_bf16x8(zrow + k) : zero_bf16x8();
+            p = mfma_bf16(zf, ring[j].af[kb], p);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < NAF; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              p = mfma_f32(zrow[g * (D / 4) + 4 * q + e], ring[j].af[q][e], p);
+        }
+        if constexpr (REVERSE)
+          z = gam * z - p;
+        else
+          z = gam * z - p + u;
+        load(ring[j], s + PD);
+      }
     }
   }
 
+  if constexpr (!REVERSE) {   // the last state S_{T-1} still has to be stored
+    const int cur = T & 1;
+    stage(cur);
+    block_sync();
+    emit_rows(cur, T - 1);
+  }
   if (a.zT) {
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int ct = wave + 4 * j;
-      if (ct < NT) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          a.zT[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li] = z[j][r];
-      }
-    }
+    for (int r = 0; r < 4; ++r) a.zT[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li] = z[r];
   }
 }
 
-template <int NT>
+template <int IO, int NT>
 static hipError_t launch_scan_nt(const ScanArgs& a, bool reverse, hipStream_t s) {
-  const dim3 grid(a.B * a.H * NT), block(256);
+  const dim3 grid(a.B * a.H * NT), block(64 * NT);
   if (reverse)
-    hipLaunchKernelGGL((scan_kernel<NT, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<IO, NT, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((scan_kernel<NT, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<IO, NT, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_scan(const ChunkScanArgs&, int, hipStream_t) {
-  return hipErrorNotSupported;
-}
-
-hipError_t launch_scan(const ScanArgs& a, int nt, bool reverse, hipStream_t s) {
+template <int IO>
+static hipError_t launch_scan_io(const ScanArgs& a, int nt, bool reverse, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_scan_nt<1>(a, reverse, s);
-    case 2: return launch_scan_nt<2>(a, reverse, s);
-    case 3: return launch_scan_nt<3>(a, reverse, s);
-    case 4: return launch_scan_nt<4>(a, reverse, s);
-    case 5: return launch_scan_nt<5>(a, reverse, s);
-    case 6: return launch_scan_nt<6>(a, reverse, s);
-    case 7: return launch_scan_nt<7>(a, reverse, s);
-    case 8: return launch_scan_nt<8>(a, reverse, s);
+    case 1: return launch_scan_nt<IO, 1>(a, reverse, s);
+    case 2: return launch_scan_nt<IO, 2>(a, reverse, s);
+    case 3: return launch_scan_nt<IO, 3>(a, reverse, s);
+    case 4: return launch_scan_nt<IO, 4>(a, reverse, s);
+    case 5: return launch_scan_nt<IO, 5>(a, reverse, s);
+    case 6: return launch_scan_nt<IO, 6>(a, reverse, s);
+    case 7: return launch_scan_nt<IO, 7>(a, reverse, s);
+    case 8: return launch_scan_nt<IO, 8>(a, reverse, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_scan(const ScanArgs& a, int io, int nt, bool reverse, hipStream_t s) {
+  return io == IO_BF16 ? launch_scan_io<IO_BF16>(a, nt, reverse, s)
+                       : launch_scan_io<IO_F32>(a, nt, reverse, s);
 }
 
 }  // namespace gdn

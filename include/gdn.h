@@ -95,8 +95,10 @@ const char* gdn_status_string(int status);
 gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes);
 
 /* Bytes of the optional forward->backward buffer `saved` (written to
- * *bytes).  Layout, fp32: A_t = K^_t beta_t K^_t^T as [B, H, T, Dk, Dk],
- * followed by the states S_t after every frame as [B, H, T, Dv, Dk]. */
+ * *bytes).  Layout: A_t = K^_t beta_t K^_t^T as [B, H, T, Dk, Dk], followed
+ * by the states S_t after every frame as [B, H, T, Dv, Dk], row-major, in
+ * the intermediate type: bf16 (round to nearest even) when io_dtype is
+ * GDN_BF16, fp32 when it is GDN_FP32. */
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
 
 /* Whole-sequence forward (module 2 recurrence over t = 1..T):
@@ -114,6 +116,19 @@ gdn_status gdn_forward(const gdn_problem* p,
                        const float* state_in,
                        void* o, float* state_out, void* saved,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* gdn_forward, additionally recording four caller-created hipEvent_t
+ * (events[0..3], all non-NULL) on `stream`: before the per-frame Gram/write
+ * kernel, between it and the inter-frame scan, between the scan and the
+ * output kernel, and after the output kernel.  For measuring the three
+ * phases; results are identical to gdn_forward. */
+gdn_status gdn_forward_events(const gdn_problem* p,
+                              const void* q, const void* k, const void* v,
+                              const float* gamma, const float* beta,
+                              const float* state_in,
+                              void* o, float* state_out, void* saved,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* events);
 
 /* Streaming step: advance the carried state by one latent frame
  * (p->T must be 1), as the chunk-by-chunk autoregressive variant does

@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = gb.header_functions()
     assert set(names) == {"gdn_abi_version", "gdn_status_string", "gdn_workspace_size",
-                          "gdn_saved_size", "gdn_forward", "gdn_step", "gdn_backward"}
+                          "gdn_saved_size", "gdn_forward", "gdn_forward_events", "gdn_step",
+                          "gdn_backward"}
     for n in names:
         assert hasattr(lib, n), n
     # and the shared object's dynamic symbol table really carries them
@@ -49,13 +50,15 @@ def _ws(prob, op):
 def test_workspace_sizes(lib):
     B, H, T, N, D = 1, 20, 121, 880, 112
     p = gb.make_problem(B, H, T, N, D, "bf16")
-    mat = B * H * T * D * D * 4
+    mat = B * H * T * D * D * 2            # bf16 intermediates for bf16 io
     assert _ws(p, gb.GDN_OP_FORWARD) == (0, 3 * mat)
     assert _ws(p, gb.GDN_OP_BACKWARD) == (0, 6 * mat)
     assert gb.STATUS[_ws(p, gb.GDN_OP_STEP)[0]] == "GDN_ERR_BAD_SHAPE"     # T != 1
     p1 = gb.make_problem(B, H, 1, N, D, "bf16")
-    assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 4)
+    assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 2)
     assert gb.saved_size(p) == 2 * mat
+    pf = gb.make_problem(B, H, T, N, D, "fp32")
+    assert gb.saved_size(pf) == 2 * B * H * T * D * D * 4
 
 
 @pytest.mark.parametrize("field,value,status", [
