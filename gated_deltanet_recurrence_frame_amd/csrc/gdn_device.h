@@ -39,7 +39,12 @@ template <> struct Io<IO_F32> {
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave index is the same for all lanes of a wave; readfirstlane makes
+// that visible to the compiler so per-wave choices compile to scalar
+// branches instead of exec-masked ones.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -94,6 +99,36 @@ __device__ __forceinline__ bf16x8 lds_col_frag_bf16(const uint16_t* M, int ld, i
 
 // Block-wide barrier.
 __device__ __forceinline__ void block_sync() { __syncthreads(); }
+
+// ---- Direct global -> LDS copies (gfx950 global_load_lds) --------------
+// One instruction copies `size` bytes per lane; lane l's bytes land at
+// lds_base + size * l (lds_base must be the same for the whole wave).  The
+// copies count in the wave's vector-memory counter and complete in issue
+// order with its other vector-memory operations; the compiler does not
+// track them, so consumers wait explicitly with wait_vm_barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(src), (lds_void_t*)(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(src), (lds_void_t*)(lds_base), 4, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory operations are still
+// outstanding, then barrier the workgroup.  With N no larger than the
+// number of copies the wave issued after a given stage, that stage has
+// landed for every wave once the barrier is passed.  The empty asm keeps
+// the compiler from moving LDS accesses across.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // XCD-aware work ordering.  Hardware hands consecutive workgroup ids to the
 // 8 XCDs in turn; this maps them so that each XCD receives a contiguous

@@ -18,13 +18,13 @@
 // the scan consumes.
 //
 // Layout of the work: one workgroup (4 waves) per (b, t, h), XCD-aware
-// ordering so heads of one frame run on one XCD.  Tokens stream through LDS
-// in chunks of CT rows (natural [token][feature] layout, double-buffered,
-// next chunk prefetched into registers while the current one is consumed).
+// ordering so heads of one frame run on one XCD, two workgroups per CU.
+// Tokens stream through LDS in chunks of CT rows (natural [token][feature]
+// layout, double-buffered), the next chunk in flight in registers.
 // Both MFMA operands need a feature's values over consecutive tokens; they
 // are read with the gfx950 transposing LDS read.  The weight w multiplies
 // the X operand in fp32 before rounding to bf16.  Tail tokens of the last
-// chunk re-read the frame's last row and get w = 0, so they add exactly 0.
+// chunk re-read the frame's last row and get weight 0, so they add exactly 0.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -34,19 +34,18 @@ template <int IO, int NT, int NR, bool Y_IS_X0>
 struct GramCfg {
   static constexpr int D = 16 * NT;
   static constexpr int ES = Io<IO>::bytes;
-  static constexpr int KBK = Io<IO>::kblock;
   static constexpr int CT = (IO == IO_BF16) ? 64 : 32;     // tokens per chunk
   static constexpr int NMAT = NR + (Y_IS_X0 ? 0 : 1);       // matrices staged
+  static constexpr int MAT_ELEMS = CT * D;
   static constexpr int PR = D * ES / 16;                    // 16-byte pieces per row
   static constexpr int PIECES = NMAT * CT * PR;
   static constexpr int PPT = (PIECES + 255) / 256;          // pieces per thread
-  static constexpr int MAT_ELEMS = CT * D;
   static constexpr int STAGE_BYTES = NMAT * MAT_ELEMS * ES + CT * 4;
   static constexpr int RT = (NR * NT + 3) / 4;              // row tiles per wave
 };
 
 template <int IO, int NT, int NR, bool Y_IS_X0>
-__global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
+__global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   typedef GramCfg<IO, NT, NR, Y_IS_X0> C;
   typedef typename Io<IO>::elem E;
   constexpr int D = C::D;
@@ -62,23 +61,21 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   const long L = (long)a.T * N;
   const long row0 = (long)b * L + (long)t * N;   // first token row of the frame
 
-  const E* mats[3] = {static_cast<const E*>(a.x0), static_cast<const E*>(a.x1),
+  const E* srcs[3] = {static_cast<const E*>(a.x0), static_cast<const E*>(NR == 2 ? a.x1 : a.y),
                       static_cast<const E*>(a.y)};
-  // staged matrix m -> source: 0 -> x0, 1 -> x1 (NR == 2) or y, 2 -> y
-  auto src_of = [&](int m) -> const E* {
-    if (m < NR) return mats[m];
-    return mats[2];
-  };
-
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int g = lane >> 4, li = lane & 15;
   const int nchunks = (N + C::CT - 1) / C::CT;
 
-  u32x4 pre[C::PPT];
-  float wpre = 0.f;
-
-  auto issue = [&](int c) {
+  // Register staging of the next chunk.  A chunk's weights are masked
+  // here: 0 past the frame's last token (whose row is re-read), 1 when
+  // there are no weights.
+  struct Pre {
+    u32x4 v[C::PPT];
+    float w;
+  };
+  auto issue = [&](Pre& P, int c) {
     const int c0 = c * C::CT;
 #pragma unroll
     for (int j = 0; j < C::PPT; ++j) {
@@ -86,36 +83,26 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
       if (p < C::PIECES) {
         const int m = p / (C::CT * C::PR);
         const int r = p % (C::CT * C::PR);
-        int row = r / C::PR;
-        const int pc = r % C::PR;
+        const int row = r / C::PR, pc = r % C::PR;
         int tok = c0 + row;
         if (tok >= N) tok = N - 1;
-        const E* src = src_of(m) + ((row0 + tok) * a.H + h) * (long)D + pc * (16 / C::ES);
-        pre[j] = *reinterpret_cast<const u32x4*>(src);
+        P.v[j] = *reinterpret_cast<const u32x4*>(srcs[m] + ((row0 + tok) * a.H + h) * (long)D +
+                                                 pc * (16 / C::ES));
       }
     }
     if (tid < C::CT) {
       const int tok = c0 + tid;
-      if (tok < N)
-        wpre = a.w ? a.w[(row0 + tok) * a.H + h] : 1.0f;
-      else
-        wpre = 0.f;
+      P.w = tok < N ? (a.w ? a.w[(row0 + tok) * a.H + h] : 1.0f) : 0.0f;
     }
   };
-  auto commit = [&](int stage) {
+  auto commit = [&](const Pre& P, int stage) {
     char* base = smem + stage * C::STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < C::PPT; ++j) {
       const int p = tid + 256 * j;
-      if (p < C::PIECES) {
-        const int m = p / (C::CT * C::PR);
-        const int r = p % (C::CT * C::PR);
-        E* dst = reinterpret_cast<E*>(base) + m * C::MAT_ELEMS + r * (16 / C::ES);
-        *reinterpret_cast<u32x4*>(dst) = pre[j];
-      }
+      if (p < C::PIECES) *reinterpret_cast<u32x4*>(reinterpret_cast<E*>(base) + p * (16 / C::ES)) = P.v[j];
     }
-    if (tid < C::CT)
-      reinterpret_cast<float*>(base + C::NMAT * C::MAT_ELEMS * C::ES)[tid] = wpre;
+    if (tid < C::CT) reinterpret_cast<float*>(base + C::NMAT * C::MAT_ELEMS * C::ES)[tid] = P.w;
   };
 
   f32x4 acc[C::RT][NT];
@@ -124,42 +111,41 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
 
-  issue(0);
-  commit(0);
-  block_sync();
-
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) issue(c + 1);
-    const char* base = smem + (c & 1) * C::STAGE_BYTES;
+  auto compute = [&](int stage) {
+    const char* base = smem + stage * C::STAGE_BYTES;
     const E* xs = reinterpret_cast<const E*>(base);
     const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * C::MAT_ELEMS;
     const float* ws = reinterpret_cast<const float*>(base + C::NMAT * C::MAT_ELEMS * C::ES);
-
     if constexpr (IO == IO_BF16) {
 #pragma unroll
       for (int kb = 0; kb < C::CT / 32; ++kb) {
         const int k0 = kb * 32;
-        float wv[8];
-        {
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { wv[e] = w0[e]; wv[4 + e] = w1[e]; }
-        }
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g + 4);
         bf16x8 bfr[NT];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
           bfr[ct] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(ys), D, k0, ct * 16);
+        bf16x8 afr[C::RT];
 #pragma unroll
         for (int j = 0; j < C::RT; ++j) {
           const int rtg = wave + 4 * j;
           if (rtg < NR * NT) {
             const int m = rtg / NT, ft = rtg % NT;
-            bf16x8 af = lds_col_frag_bf16(
-                reinterpret_cast<const uint16_t*>(xs + m * C::MAT_ELEMS), D, k0, ft * 16);
+            afr[j] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(xs + m * C::MAT_ELEMS), D,
+                                       k0, ft * 16);
+          }
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              af[e] = static_cast<__bf16>(static_cast<float>(af[e]) * wv[e]);
+        for (int j = 0; j < C::RT; ++j) {
+          const int rtg = wave + 4 * j;
+          if (rtg < NR * NT) {
+            bf16x8 af = afr[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              af[e] = static_cast<__bf16>(static_cast<float>(af[e]) * w0[e]);
+              af[4 + e] = static_cast<__bf16>(static_cast<float>(af[4 + e]) * w1[e]);
+            }
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_bf16(af, bfr[ct], acc[j][ct]);
           }
@@ -186,8 +172,19 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
         }
       }
     }
+  };
 
-    if (c + 1 < nchunks) commit((c + 1) & 1);
+  // Pipeline: chunk c is computed from LDS stage c % 2 while chunk c + 1 is
+  // in flight in registers; two workgroups per CU overlap each other's
+  // waits.
+  Pre P;
+  issue(P, 0);
+  commit(P, 0);
+  block_sync();
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + 1 < nchunks) issue(P, c + 1);
+    compute(c & 1);
+    if (c + 1 < nchunks) commit(P, (c + 1) & 1);
     block_sync();
   }
 

@@ -5,10 +5,11 @@
 // One workgroup per (b, t, h) frame (XCD-aware order), one wave per 16-row
 // feature tile of the output.  A wave keeps its 16 rows of S_t as MFMA
 // operand fragments in registers for the whole frame (bf16: 4 x 8 values
-// per lane at D = 112).  Query rows stream through LDS in chunks (natural
-// [token][feature] layout, double-buffered, register prefetch of the next
-// chunk); every wave reads the chunk's query rows as the other operand and
-// writes its 16 features of each token (8-byte stores of 4 bf16).
+// per lane at D = 112).  Query rows stream through a 3-stage LDS ring in
+// chunks (natural [token][feature] layout, copied straight from memory to
+// LDS two chunks ahead); every wave reads the chunk's query rows as the
+// other operand and stages its 16 features of each token in LDS; the next
+// iteration stores the chunk's output rows as contiguous 16-byte pieces.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -22,12 +23,15 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   constexpr int D = 16 * NT;
   constexpr int ES = Io<IO>::bytes;
   constexpr int CT = (IO == IO_BF16) ? 64 : 32;
-  constexpr int PR = D * ES / 16;
-  constexpr int PIECES = CT * PR;
-  constexpr int NTH = 64 * NT;
-  constexpr int PPT = (PIECES + NTH - 1) / NTH;
+  constexpr int MAT_BYTES = CT * D * ES;          // one chunk of query rows
+  constexpr int WL = MAT_BYTES / 1024;            // 1 KB copies per chunk (= 2 NT)
+  constexpr int OPS = WL / NT;                    // copies per wave per chunk
+  constexpr int STAGES = 3;
   constexpr int KB = (IO == IO_BF16) ? (D + 31) / 32 : D / 4;
-  __shared__ __attribute__((aligned(16))) E tok[2][CT * D];
+  constexpr int NTH = 64 * NT;
+  static_assert(WL % NT == 0, "copies must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES][MAT_BYTES];
+  __shared__ __attribute__((aligned(16))) E obuf[2][CT * D];   // output chunk staging
 
   const int total = a.B * a.T * a.H;
   const int item = xcd_item(blockIdx.x, total);
@@ -36,7 +40,6 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   const int b = item / (a.H * a.T);
   const int N = a.N;
   const long row0 = (long)b * a.T * N + (long)t * N;
-  const int tid = threadIdx.x;
   const int lane = lane_id(), ft = wave_id();
   const int g = lane >> 4, li = lane & 15;
 
@@ -56,37 +59,54 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
     }
   }
 
-  u32x4 pre[PPT];
+  // Copy op i = ft + NT j of a chunk covers LDS bytes [1 KB i, +1 KB) of the
+  // stage, lane l the 16 bytes at + 16 l (token row o / (D*ES)).
+  const char* qsrc = static_cast<const char*>(a.tok);
   auto issue = [&](int c) {
     const int c0 = c * CT;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int p = tid + NTH * j;
-      if (p < PIECES) {
-        const int row = p / PR, pc = p % PR;
-        int tk = c0 + row;
-        if (tk >= N) tk = N - 1;
-        const E* src = static_cast<const E*>(a.tok) + ((row0 + tk) * a.H + h) * (long)D +
-                       pc * (16 / ES);
-        pre[j] = *reinterpret_cast<const u32x4*>(src);
-      }
+    for (int j = 0; j < OPS; ++j) {
+      const int i = ft + NT * j;
+      const int o = i * 1024 + lane * 16;
+      const int row = o / (D * ES), col = o % (D * ES);
+      int tk = c0 + row;
+      if (tk >= N) tk = N - 1;
+      dma16(qsrc + (((row0 + tk) * a.H + h) * (long)D) * ES + col, &ring[c % STAGES][i * 1024]);
     }
   };
-  auto commit = [&](int stage) {
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int p = tid + NTH * j;
-      if (p < PIECES) *reinterpret_cast<u32x4*>(&tok[stage][p * (16 / ES)]) = pre[j];
+
+  // Output rows of a chunk are staged in LDS and stored one iteration later
+  // as whole 16-byte pieces of token rows (each row of a head is D*ES
+  // contiguous bytes), instead of 4 values per lane scattered over 16 rows.
+  const int tid = threadIdx.x;
+  auto store_chunk = [&](int c) {
+    const E* src = obuf[c & 1];
+    constexpr int PRW = D * ES / 16;
+    for (int p = tid; p < CT * PRW; p += NTH) {
+      const int row = p / PRW, pc = p % PRW;
+      const int tk = c * CT + row;
+      if (tk < N)
+        *reinterpret_cast<u32x4*>(static_cast<E*>(a.out) + ((row0 + tk) * a.H + h) * (long)D +
+                                  pc * (16 / ES)) =
+            *reinterpret_cast<const u32x4*>(src + row * D + pc * (16 / ES));
     }
   };
 
   const int nchunks = (N + CT - 1) / CT;
-  issue(0);
-  commit(0);
-  block_sync();
+#pragma unroll
+  for (int c = 0; c < STAGES - 1; ++c)
+    if (c < nchunks) issue(c);
   for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) issue(c + 1);
-    const E* ts = tok[c & 1];
+    // Copies of chunk c+1 (if any) are younger than chunk c's; the output
+    // stores in between only make the wait more conservative.
+    if (c + 1 < nchunks)
+      wait_vm_barrier<OPS>();
+    else
+      wait_vm_barrier<0>();
+    if (c + STAGES - 1 < nchunks) issue(c + STAGES - 1);
+    if (c > 0) store_chunk(c - 1);      // staged by every wave before the barrier
+    const E* ts = reinterpret_cast<const E*>(ring[c % STAGES]);
+    E* ob = obuf[c & 1];
 #pragma unroll
     for (int tt = 0; tt < CT / 16; ++tt) {
       f32x4 acc = zero4();
@@ -102,22 +122,19 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
           acc = mfma_f32(sf[kb], reinterpret_cast<const float*>(trow)[kb * 4 + g], acc);
         }
       }
-      const int tk = c * CT + tt * 16 + li;
-      if (tk < N) {
-        E* dst = static_cast<E*>(a.out) + ((row0 + tk) * a.H + h) * (long)D + ft * 16 + 4 * g;
-        if constexpr (IO == IO_BF16) {
-          u32x2 pk;
-          pk[0] = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-          pk[1] = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
-          *reinterpret_cast<u32x2*>(dst) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = acc;
-        }
+      E* dst = ob + (tt * 16 + li) * D + ft * 16 + 4 * g;
+      if constexpr (IO == IO_BF16) {
+        u32x2 pk;
+        pk[0] = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+        pk[1] = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+        *reinterpret_cast<u32x2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = acc;
       }
     }
-    if (c + 1 < nchunks) commit((c + 1) & 1);
-    block_sync();
   }
+  block_sync();
+  store_chunk(nchunks - 1);
 }
 
 template <int IO, int NT>
