@@ -13,7 +13,6 @@ gdn_step calls.
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -27,20 +26,6 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 SHAPE = dict(B=1, H=20, D=112, T=121, N=880)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_frame_amd", "csrc")
-KERNEL_SOURCES = {  # kernel -> source files its code depends on
-    "gram": ["gdn_gram.hip", "gdn_device.h", "gdn_internal.h"],
-    "scan": ["gdn_scan.hip", "gdn_device.h", "gdn_internal.h"],
-    "output": ["gdn_output.hip", "gdn_device.h", "gdn_internal.h"],
-}
-
-
-def source_sha(kernel):
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def algorithmic(kernel, B, H, D, T, N):
@@ -86,6 +71,7 @@ class HipEvents:
 def load_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the kernel's current source."""
+    from gated_deltanet_recurrence_frame_amd.rocprof_summary import source_sha
     try:
         with open(PROFILE_TRAFFIC) as f:
             tr = json.load(f)
