@@ -101,6 +101,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   ga.layout0 = LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
   ga.scale0 = s.s * s.s; ga.scale1 = s.s;
   ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
+  ga.t0 = 0; ga.Tc = (int)s.T;
   gdn_status st = record(events, 0, stream);
   if (st != GDN_OK) return st;
   st = hip_status(launch_gram(ga, s.io, nt, 2, stream));
@@ -112,6 +113,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
     ScanArgs sa{};
     sa.A = A; sa.U = U; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S; sa.zT = state_out;
     sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
+    sa.t0 = 0; sa.Tc = (int)s.T;
     st = hip_status(launch_scan(sa, s.io, nt, false, stream));
   }
   if (st != GDN_OK) return st;
@@ -121,6 +123,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   OutArgs oa{};
   oa.tok = q; oa.mat = S; oa.out = o;
   oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
+  oa.t0 = 0; oa.Tc = (int)s.T;
   st = hip_status(launch_output(oa, s.io, nt, stream));
   if (st != GDN_OK) return st;
   return record(events, 3, stream);
@@ -283,11 +286,13 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     ga.layout0 = LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
     ga.scale0 = s.s * s.s; ga.scale1 = s.s;
     ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
+    ga.t0 = 0; ga.Tc = (int)s.T;
     st = hip_status(launch_gram(ga, s.io, nt, 2, stream_));
     if (st != GDN_OK) return st;
     ScanArgs sa{};
     sa.A = A_; sa.U = U_; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S_; sa.zT = nullptr;
     sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
+    sa.t0 = 0; sa.Tc = (int)s.T;
     st = hip_status(launch_scan(sa, s.io, nt, false, stream_));
     if (st != GDN_OK) return st;
     A = A_;
@@ -303,6 +308,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   gx.layout0 = LAYOUT_TILES; gx.layout1 = LAYOUT_TILES;
   gx.scale0 = 1.f; gx.scale1 = 0.f;
   gx.B = (int)s.B; gx.H = (int)s.H; gx.T = (int)s.T; gx.N = (int)s.N;
+  gx.t0 = 0; gx.Tc = (int)s.T;
   st = hip_status(launch_gram(gx, s.io, nt, 1, stream_));
   if (st != GDN_OK) return st;
 
@@ -310,6 +316,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   ScanArgs ra{};
   ra.A = A; ra.U = X; ra.gamma = gamma; ra.z0 = d_state_out; ra.emit = G; ra.zT = d_state_in;
   ra.B = (int)s.B; ra.H = (int)s.H; ra.T = (int)s.T;
+  ra.t0 = 0; ra.Tc = (int)s.T;
   st = hip_status(launch_scan(ra, s.io, nt, true, stream_));
   if (st != GDN_OK) return st;
 

@@ -52,11 +52,11 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   constexpr int SMEM = (2 * C::STAGE_BYTES > D * D * C::ES) ? 2 * C::STAGE_BYTES : D * D * C::ES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-  const int total = a.B * a.T * a.H;
+  const int total = a.B * a.Tc * a.H;
   const int item = xcd_item(blockIdx.x, total);
   const int h = item % a.H;
-  const int t = (item / a.H) % a.T;
-  const int b = item / (a.H * a.T);
+  const int t = a.t0 + (item / a.H) % a.Tc;
+  const int b = item / (a.H * a.Tc);
   const int N = a.N;
   const long L = (long)a.T * N;
   const long row0 = (long)b * L + (long)t * N;   // first token row of the frame
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
 
 template <int IO, int NT>
 static hipError_t launch_gram_nt(const GramArgs& a, int nr, hipStream_t s) {
-  const dim3 grid(a.B * a.T * a.H), block(256);
+  const dim3 grid(a.B * a.Tc * a.H), block(256);
   if (nr == 2)
     hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true>), grid, block, 0, s, a);
   else

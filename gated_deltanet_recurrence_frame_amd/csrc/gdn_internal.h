@@ -27,6 +27,7 @@ struct GramArgs {
   int layout0, layout1;
   float scale0, scale1;
   int B, H, T, N;
+  int t0, Tc;          // frames t0 .. t0 + Tc - 1 of the T-frame tensors
 };
 hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
 
@@ -43,6 +44,8 @@ struct ScanArgs {
   void* emit;           // [B, H, T] x D x D row-major, intermediate type
   float* zT;
   int B, H, T;
+  int t0, Tc;           // forward: frames t0 .. t0 + Tc - 1 (z0 = state before t0);
+                        // reverse: whole sequence (t0 = 0, Tc = T)
 };
 hipError_t launch_scan(const ScanArgs& a, int io, int nt, bool reverse, hipStream_t s);
 
@@ -53,6 +56,7 @@ struct OutArgs {
   const void* mat;      // S_t [B, H, T] x D x D row-major, intermediate type
   void* out;            // O [B, L, H, D]
   int B, H, T, N;
+  int t0, Tc;           // frames t0 .. t0 + Tc - 1
 };
 hipError_t launch_output(const OutArgs& a, int io, int nt, hipStream_t s);
 

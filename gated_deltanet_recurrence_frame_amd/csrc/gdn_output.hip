@@ -33,11 +33,11 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring[STAGES][MAT_BYTES];
   __shared__ __attribute__((aligned(16))) E obuf[2][CT * D];   // output chunk staging
 
-  const int total = a.B * a.T * a.H;
+  const int total = a.B * a.Tc * a.H;
   const int item = xcd_item(blockIdx.x, total);
   const int h = item % a.H;
-  const int t = (item / a.H) % a.T;
-  const int b = item / (a.H * a.T);
+  const int t = a.t0 + (item / a.H) % a.Tc;
+  const int b = item / (a.H * a.Tc);
   const int N = a.N;
   const long row0 = (long)b * a.T * N + (long)t * N;
   const int lane = lane_id(), ft = wave_id();
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
 
 template <int IO, int NT>
 static hipError_t launch_output_nt(const OutArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((output_kernel<IO, NT>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0, s, a);
+  hipLaunchKernelGGL((output_kernel<IO, NT>), dim3(a.B * a.Tc * a.H), dim3(64 * NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
   const int lane = lane_id(), ct = wave_id();
   const int g = lane >> 4, li = lane & 15;
   const long DD = (long)D * D;
-  const int T = a.T;
+  const int T = a.T;             // frames in the tensors
+  const int NS = a.Tc;           // frames walked by this launch, from a.t0
   const E* Ab = static_cast<const E*>(a.A) + (long)bh * T * DD;
   const E* Ub = static_cast<const E*>(a.U) + (long)bh * T * DD;
   E* Eb = static_cast<E*>(a.emit) + (long)bh * T * DD;
@@ -75,9 +76,9 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     for (int r = 0; r < 4; ++r) z[r] = a.z0[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li];
   }
 
-  auto frame_of = [&](int s) { return REVERSE ? T - 1 - s : s; };
+  auto frame_of = [&](int s) { return REVERSE ? a.t0 + NS - 1 - s : a.t0 + s; };
   auto load = [&](Buf& B, int s) {
-    const int t = frame_of(s < T ? s : T - 1);
+    const int t = frame_of(s < NS ? s : NS - 1);
     const E* At = Ab + t * DD + (ct * 16 + li) * D;
     if constexpr (BF) {
 #pragma unroll
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
   auto load_gammas = [&](int s0) {
     for (int i = tid; i < GW; i += NTH) {
       const int s = s0 + i;
-      gam_lds[i] = s < T ? a.gamma[((long)b * T + frame_of(s)) * a.H + h] : 0.f;
+      gam_lds[i] = s < NS ? a.gamma[((long)b * T + frame_of(s)) * a.H + h] : 0.f;
     }
   };
 
@@ -134,11 +135,11 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int j = 0; j < PD; ++j) load(ring[j], j);
 
-  for (int s0 = 0; s0 < T; s0 += PD) {
+  for (int s0 = 0; s0 < NS; s0 += PD) {
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
       const int s = s0 + j;
-      if (s < T) {
+      if (s < NS) {
         const int cur = s & 1;
         const int t = frame_of(s);
         if (s % GW == 0) {
@@ -180,11 +181,11 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     }
   }
 
-  if constexpr (!REVERSE) {   // the last state S_{T-1} still has to be stored
-    const int cur = T & 1;
+  if constexpr (!REVERSE) {   // the walk's last state still has to be stored
+    const int cur = NS & 1;
     stage(cur);
     block_sync();
-    emit_rows(cur, T - 1);
+    emit_rows(cur, a.t0 + NS - 1);
   }
   if (a.zT) {
 #pragma unroll

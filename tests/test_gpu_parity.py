@@ -286,3 +286,84 @@ def test_errors_write_nothing():
     assert gb.STATUS[code] == "GDN_ERR_ALIASING"
     torch.cuda.synchronize()
     assert torch.all(o == 7.0)
+
+
+# ------------------------------------------------------ longer sequences
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_forward_long_sequence_in_place(io):
+    # more frames than the scan's prefetch ring and gamma window split, in
+    # place and against the allocating call
+    B, H, T, N, D = 1, 3, 64, 100, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=20,
+                          with_state=True)
+    check_forward(inp, N, io, with_state=True)
+    # in place, and with the saved buffer
+    d = {k: to_dev(v) for k, v in inp.items()}
+    st = d["state"].clone()
+    prob = gb.make_problem(B, H, T, N, D, io)
+    o = torch.empty_like(d["v"])
+    ws = torch.empty(gb.workspace_size(prob, gb.GDN_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    import ctypes
+    code = gb.lib().gdn_forward(ctypes.byref(prob), gb._p(d["q"]), gb._p(d["k"]), gb._p(d["v"]),
+                                gb._p(d["gamma"]), gb._p(d["beta"]), gb._p(st), gb._p(o),
+                                gb._p(st), None, gb._p(ws), ws.numel(),
+                                gb._stream(torch.device(DEV)))
+    assert code == 0
+    o_ref, s_ref = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                              state_in=d["state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(st, s_ref)
+
+
+_MINUTE = {}
+
+
+def _minute_inputs():
+    if not _MINUTE:
+        _MINUTE.update(gin.make_config("minute", seed=0, with_do=True))
+    return _MINUTE
+
+
+def _head_slice(t, heads):
+    return t[:, :, heads].contiguous()
+
+
+def test_forward_minute_config_sampled_heads():
+    # the benchmark's own configuration and launch path (pipelined chunks);
+    # heads are independent, so the oracle checks a sample of them in full
+    inp = _minute_inputs()
+    d = {k: to_dev(v) for k, v in inp.items() if k != "d_o"}
+    N = 880
+    plan = gb.ForwardPlan(1, 20, 121, N, 112, "bf16", torch.device(DEV))
+    o, st = plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    torch.cuda.synchronize()
+    o, st = o.cpu(), st.cpu()
+    assert torch.isfinite(o.float()).all()
+    heads = [0, 7, 19]
+    sub = {k: _head_slice(inp[k], heads) for k in ("q", "k", "v", "gamma", "beta")}
+    ro, rs = oracle.forward(*(f64(sub[k]) for k in ("q", "k", "v", "gamma", "beta")), N)
+    eo = rel_l2(f64(o[:, :, heads]), ro)
+    es = rel_l2(f64(st[:, heads]), rs)
+    print("minute forward, heads %s: o %.3e state %.3e" % (heads, eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_train_minute_config_sampled_heads():
+    inp = _minute_inputs()
+    d = {k: to_dev(v) for k, v in inp.items()}
+    N = 880
+    plan = gb.ForwardPlan(1, 20, 121, N, 112, "bf16", torch.device(DEV), saved=True)
+    plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                     saved=plan.saved)
+    torch.cuda.synchronize()
+    heads = [3, 12]
+    sub = {k: _head_slice(inp[k], heads) for k in ("q", "k", "v", "gamma", "beta", "d_o")}
+    ref = oracle.backward(*(f64(sub[k]) for k in ("q", "k", "v", "gamma", "beta")), N,
+                          f64(sub["d_o"]))
+    for name in ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]:
+        g = gr[name].cpu()
+        g = g[:, heads] if name == "dstate_in" else g[:, :, heads]
+        e = rel_l2(f64(g), ref[name])
+        print("minute backward %s: %.3e" % (name, e))
+        assert e <= TOL["bf16"], (name, e)
