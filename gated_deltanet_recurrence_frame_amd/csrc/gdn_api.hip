@@ -124,7 +124,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   oa.tok = q; oa.mat = S; oa.out = o;
   oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
   oa.t0 = 0; oa.Tc = (int)s.T;
-  st = hip_status(launch_output(oa, s.io, nt, stream));
+  st = hip_status(launch_output(oa, s.io, nt, false, stream));
   if (st != GDN_OK) return st;
   return record(events, 3, stream);
 }
@@ -326,9 +326,17 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   st = hip_status(launch_dm(da, s.io, nt, stream_));
   if (st != GDN_OK) return st;
 
+  // dQ^_t = S_t^T dO_t: the output kernel on the transposed states.
+  OutArgs qa{};
+  qa.tok = d_o; qa.mat = S; qa.out = dq;
+  qa.B = (int)s.B; qa.H = (int)s.H; qa.T = (int)s.T; qa.N = (int)s.N;
+  qa.t0 = 0; qa.Tc = (int)s.T;
+  st = hip_status(launch_output(qa, s.io, nt, true, stream_));
+  if (st != GDN_OK) return st;
+
   BwdTokArgs ba{};
-  ba.k = k; ba.v = v; ba.d_o = d_o; ba.beta = beta; ba.S = S; ba.G = G; ba.W = W;
-  ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
+  ba.k = k; ba.v = v; ba.beta = beta; ba.G = G; ba.W = W;
+  ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
   ba.B = (int)s.B; ba.H = (int)s.H; ba.T = (int)s.T; ba.N = (int)s.N;
   return hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
 }

@@ -49,16 +49,17 @@ struct ScanArgs {
 };
 hipError_t launch_scan(const ScanArgs& a, int io, int nt, bool reverse, hipStream_t s);
 
-// Token-stream products with per-frame D x D matrices, one wave per output
-// feature tile.  Forward output: O_t = S_t Q^_t.
+// Token-stream product with a per-frame D x D matrix M, one wave per output
+// feature tile: out[n] = M tok[n] (trans = false) or M^T tok[n] (trans =
+// true).  Forward output: O_t = S_t Q^_t; backward: dQ^_t = S_t^T dO_t.
 struct OutArgs {
-  const void* tok;      // Q [B, L, H, D]
-  const void* mat;      // S_t [B, H, T] x D x D row-major, intermediate type
-  void* out;            // O [B, L, H, D]
+  const void* tok;      // [B, L, H, D] io dtype (Q, or dO)
+  const void* mat;      // [B, H, T] x D x D row-major, intermediate type
+  void* out;            // [B, L, H, D] io dtype
   int B, H, T, N;
   int t0, Tc;           // frames t0 .. t0 + Tc - 1
 };
-hipError_t launch_output(const OutArgs& a, int io, int nt, hipStream_t s);
+hipError_t launch_output(const OutArgs& a, int io, int nt, bool trans, hipStream_t s);
 
 // Backward, per frame: W_t = dM_t + dM_t^T with dM_t = S_{t-1}^T G_t, and
 // dgamma_t = tr(dM_t).
@@ -72,16 +73,13 @@ struct DmArgs {
 };
 hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s);
 
-// Backward, per frame, token pass: dQ, dK, dV, dbeta.
+// Backward, per frame, token pass: dK, dV, dbeta.
 struct BwdTokArgs {
   const void* k;
   const void* v;
-  const void* d_o;
   const float* beta;    // [B, L, H]
-  const void* S;        // states after each frame, row-major, intermediate type
   const void* G;        // row-major, intermediate type
   const void* W;        // row-major, intermediate type
-  void* dq;
   void* dk;
   void* dv;
   float* dbeta;         // [B, L, H]

@@ -17,7 +17,7 @@
 
 namespace gdn {
 
-template <int IO, int NT>
+template <int IO, int NT, bool TRANS>
 __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   typedef typename Io<IO>::elem E;
   constexpr int D = 16 * NT;
@@ -43,20 +43,40 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   const int lane = lane_id(), ft = wave_id();
   const int g = lane >> 4, li = lane & 15;
 
-  // This wave's rows of S_t (intermediate type, row-major) as left MFMA
-  // operands.
-  const E* Sm = static_cast<const E*>(a.mat) + (((long)b * a.H + h) * a.T + t) * (long)(D * D) +
-                (ft * 16 + li) * D;
+  // This wave's rows of the frame matrix (intermediate type, row-major in
+  // memory) as left MFMA operands: rows of S_t, or with TRANS rows of
+  // S_t^T (columns of S_t; the backward's dQ = S_t^T dO), which are staged
+  // in LDS and read with the transposing LDS read.
+  const E* Sm = static_cast<const E*>(a.mat) + (((long)b * a.H + h) * a.T + t) * (long)(D * D);
   typedef typename std::conditional<IO == IO_BF16, bf16x8, float>::type Frag;
   Frag sf[KB];
+  if constexpr (!TRANS) {
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    if constexpr (IO == IO_BF16) {
-      const int k = kb * 32 + 8 * g;
-      sf[kb] = (k < D) ? load_bf16x8(Sm + k) : zero_bf16x8();
-    } else {
-      sf[kb] = Sm[kb * 4 + g];
+    for (int kb = 0; kb < KB; ++kb) {
+      if constexpr (IO == IO_BF16) {
+        const int k = kb * 32 + 8 * g;
+        sf[kb] = (k < D) ? load_bf16x8(Sm + (ft * 16 + li) * D + k) : zero_bf16x8();
+      } else {
+        sf[kb] = Sm[(ft * 16 + li) * D + kb * 4 + g];
+      }
     }
+  } else if constexpr (IO == IO_BF16) {
+    // [KB*32][D] rows in the output staging area (free until the first
+    // chunk), rows past D zero.
+    uint16_t* ms = reinterpret_cast<uint16_t*>(&obuf[0][0]);
+    constexpr int PRW = D / 8;
+    for (int p = threadIdx.x; p < KB * 32 * PRW; p += NTH) {
+      const int row = p / PRW, pc = p % PRW;
+      *reinterpret_cast<u32x4*>(ms + row * D + pc * 8) =
+          row < D ? *reinterpret_cast<const u32x4*>(Sm + row * D + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    block_sync();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sf[kb] = lds_col_frag_bf16(ms, D, kb * 32, ft * 16);
+    block_sync();
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sf[kb] = Sm[(kb * 4 + g) * D + ft * 16 + li];
   }
 
   // Copy op i = ft + NT j of a chunk covers LDS bytes [1 KB i, +1 KB) of the
@@ -137,29 +157,32 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   store_chunk(nchunks - 1);
 }
 
-template <int IO, int NT>
+template <int IO, int NT, bool TRANS>
 static hipError_t launch_output_nt(const OutArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((output_kernel<IO, NT>), dim3(a.B * a.Tc * a.H), dim3(64 * NT), 0, s, a);
+  hipLaunchKernelGGL((output_kernel<IO, NT, TRANS>), dim3(a.B * a.Tc * a.H), dim3(64 * NT), 0, s,
+                     a);
   return hipGetLastError();
 }
 
-template <int IO>
+template <int IO, bool TRANS>
 static hipError_t launch_output_io(const OutArgs& a, int nt, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_output_nt<IO, 1>(a, s);
-    case 2: return launch_output_nt<IO, 2>(a, s);
-    case 3: return launch_output_nt<IO, 3>(a, s);
-    case 4: return launch_output_nt<IO, 4>(a, s);
-    case 5: return launch_output_nt<IO, 5>(a, s);
-    case 6: return launch_output_nt<IO, 6>(a, s);
-    case 7: return launch_output_nt<IO, 7>(a, s);
-    case 8: return launch_output_nt<IO, 8>(a, s);
+    case 1: return launch_output_nt<IO, 1, TRANS>(a, s);
+    case 2: return launch_output_nt<IO, 2, TRANS>(a, s);
+    case 3: return launch_output_nt<IO, 3, TRANS>(a, s);
+    case 4: return launch_output_nt<IO, 4, TRANS>(a, s);
+    case 5: return launch_output_nt<IO, 5, TRANS>(a, s);
+    case 6: return launch_output_nt<IO, 6, TRANS>(a, s);
+    case 7: return launch_output_nt<IO, 7, TRANS>(a, s);
+    case 8: return launch_output_nt<IO, 8, TRANS>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_output(const OutArgs& a, int io, int nt, hipStream_t s) {
-  return io == IO_BF16 ? launch_output_io<IO_BF16>(a, nt, s) : launch_output_io<IO_F32>(a, nt, s);
+hipError_t launch_output(const OutArgs& a, int io, int nt, bool trans, hipStream_t s) {
+  if (io == IO_BF16)
+    return trans ? launch_output_io<IO_BF16, true>(a, nt, s) : launch_output_io<IO_BF16, false>(a, nt, s);
+  return trans ? launch_output_io<IO_F32, true>(a, nt, s) : launch_output_io<IO_F32, false>(a, nt, s);
 }
 
 }  // namespace gdn
