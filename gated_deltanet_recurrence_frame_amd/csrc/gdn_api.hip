@@ -52,8 +52,36 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   return GDN_OK;
 }
 
-int64_t forward_ws(const Shape& s) { return 3 * s.mat; }
-int64_t backward_ws(const Shape& s) { return 6 * s.mat; }
+// Token splits for launches with few frames (streaming steps, short
+// clips): the Gram/write kernel splits a frame's token chunks over
+// gram_splits workgroups (fp32 partials, then a fixed-order sum), the
+// output kernel over out_splits workgroups.
+int gram_splits(const Shape& s) {
+  const int64_t frames = s.B * s.T * s.H;
+  if (frames >= 256) return 1;
+  const int64_t ct = s.io == IO_BF16 ? 64 : 32;
+  int64_t p = (256 + frames - 1) / frames;
+  const int64_t nch = (s.N + ct - 1) / ct;
+  if (p > nch) p = nch;
+  if (p > 8) p = 8;
+  return (int)(p < 1 ? 1 : p);
+}
+int out_splits(const Shape& s) {
+  const int64_t frames = s.B * s.T * s.H;
+  if (frames >= 512) return 1;
+  const int64_t ct = s.io == IO_BF16 ? 64 : 32;
+  int64_t p = (512 + frames - 1) / frames;
+  const int64_t nch = (s.N + ct - 1) / ct;
+  if (p > nch) p = nch;
+  return (int)(p < 1 ? 1 : p);
+}
+int64_t partial_bytes(const Shape& s, int nr) {
+  const int p = gram_splits(s);
+  return p > 1 ? (int64_t)p * s.B * s.H * s.T * nr * s.D * s.D * 4 : 0;
+}
+
+int64_t forward_ws(const Shape& s) { return 3 * s.mat + partial_bytes(s, 2); }
+int64_t backward_ws(const Shape& s) { return 6 * s.mat + partial_bytes(s, 2); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
@@ -102,10 +130,14 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   ga.scale0 = s.s * s.s; ga.scale1 = s.s;
   ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
   ga.t0 = 0; ga.Tc = (int)s.T;
+  ga.P = gram_splits(s);
+  ga.part = reinterpret_cast<float*>(ws + 3 * s.mat);
   gdn_status st = record(events, 0, stream);
   if (st != GDN_OK) return st;
   st = hip_status(launch_gram(ga, s.io, nt, 2, stream));
   if (st != GDN_OK) return st;
+  if (ga.P > 1 && (st = hip_status(launch_gram_reduce(ga, s.io, nt, 2, stream))) != GDN_OK)
+    return st;
   st = record(events, 1, stream);
   if (st != GDN_OK) return st;
 
@@ -124,6 +156,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   oa.tok = q; oa.mat = S; oa.out = o;
   oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
   oa.t0 = 0; oa.Tc = (int)s.T;
+  oa.P = out_splits(s);
   st = hip_status(launch_output(oa, s.io, nt, false, stream));
   if (st != GDN_OK) return st;
   return record(events, 3, stream);
@@ -287,8 +320,12 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     ga.scale0 = s.s * s.s; ga.scale1 = s.s;
     ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
     ga.t0 = 0; ga.Tc = (int)s.T;
+    ga.P = gram_splits(s);
+    ga.part = reinterpret_cast<float*>(ws + 6 * s.mat);
     st = hip_status(launch_gram(ga, s.io, nt, 2, stream_));
     if (st != GDN_OK) return st;
+    if (ga.P > 1 && (st = hip_status(launch_gram_reduce(ga, s.io, nt, 2, stream_))) != GDN_OK)
+      return st;
     ScanArgs sa{};
     sa.A = A_; sa.U = U_; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S_; sa.zT = nullptr;
     sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
@@ -309,8 +346,12 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   gx.scale0 = 1.f; gx.scale1 = 0.f;
   gx.B = (int)s.B; gx.H = (int)s.H; gx.T = (int)s.T; gx.N = (int)s.N;
   gx.t0 = 0; gx.Tc = (int)s.T;
+  gx.P = gram_splits(s);
+  gx.part = reinterpret_cast<float*>(ws + 6 * s.mat);
   st = hip_status(launch_gram(gx, s.io, nt, 1, stream_));
   if (st != GDN_OK) return st;
+  if (gx.P > 1 && (st = hip_status(launch_gram_reduce(gx, s.io, nt, 1, stream_))) != GDN_OK)
+    return st;
 
   // Reverse scan: G_t = X_t + G_{t+1} M_{t+1}^T, dS_0 = G_1 M_1^T.
   ScanArgs ra{};
@@ -331,6 +372,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   qa.tok = d_o; qa.mat = S; qa.out = dq;
   qa.B = (int)s.B; qa.H = (int)s.H; qa.T = (int)s.T; qa.N = (int)s.N;
   qa.t0 = 0; qa.Tc = (int)s.T;
+  qa.P = out_splits(s);
   st = hip_status(launch_output(qa, s.io, nt, true, stream_));
   if (st != GDN_OK) return st;
 

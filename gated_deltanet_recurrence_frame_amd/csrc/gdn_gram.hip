@@ -52,11 +52,13 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   constexpr int SMEM = (2 * C::STAGE_BYTES > D * D * C::ES) ? 2 * C::STAGE_BYTES : D * D * C::ES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-  const int total = a.B * a.Tc * a.H;
+  const int total = a.B * a.Tc * a.H * a.P;
   const int item = xcd_item(blockIdx.x, total);
-  const int h = item % a.H;
-  const int t = a.t0 + (item / a.H) % a.Tc;
-  const int b = item / (a.H * a.Tc);
+  const int sp = item % a.P;                       // token split
+  const int h = (item / a.P) % a.H;
+  const int tl = (item / (a.P * a.H)) % a.Tc;
+  const int t = a.t0 + tl;
+  const int b = item / (a.P * a.H * a.Tc);
   const int N = a.N;
   const long L = (long)a.T * N;
   const long row0 = (long)b * L + (long)t * N;   // first token row of the frame
@@ -66,7 +68,10 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int g = lane >> 4, li = lane & 15;
-  const int nchunks = (N + C::CT - 1) / C::CT;
+  const int nchunks_all = (N + C::CT - 1) / C::CT;
+  const int cps = (nchunks_all + a.P - 1) / a.P;  // chunks per split
+  const int cbeg = sp * cps;
+  const int nchunks = min(nchunks_all, cbeg + cps) - cbeg;   // may be <= 0
 
   // Register staging of the next chunk.  A chunk's weights are masked
   // here: 0 past the frame's last token (whose row is re-read), 1 when
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
     float w;
   };
   auto issue = [&](Pre& P, int c) {
-    const int c0 = c * C::CT;
+    const int c0 = (cbeg + c) * C::CT;
 #pragma unroll
     for (int j = 0; j < C::PPT; ++j) {
       const int p = tid + 256 * j;
@@ -178,8 +183,10 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   // in flight in registers; two workgroups per CU overlap each other's
   // waits.
   Pre P;
-  issue(P, 0);
-  commit(P, 0);
+  if (nchunks > 0) {
+    issue(P, 0);
+    commit(P, 0);
+  }
   block_sync();
   for (int c = 0; c < nchunks; ++c) {
     if (c + 1 < nchunks) issue(P, c + 1);
@@ -193,6 +200,22 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   // is written straight from the accumulators (4 contiguous values per
   // lane); a row-major output is staged through LDS (the chunk buffers are
   // free after the last barrier) and stored in 16-byte pieces.
+  if (a.P > 1) {   // fp32 partial sums, tile layout
+    const long pbase = ((((long)sp * a.B + b) * a.H + h) * a.Tc + tl) * NR * (long)(D * D);
+#pragma unroll
+    for (int j = 0; j < C::RT; ++j) {
+      const int rtg = wave + 4 * j;
+      if (rtg < NR * NT) {
+        const int m = rtg / NT, ft = rtg % NT;
+        const float sc = (m == 0 ? a.scale0 : a.scale1);
+        float* out = a.part + pbase + m * (long)(D * D);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          *reinterpret_cast<f32x4*>(out + ((ft * NT + ct) * 64 + lane) * 4) = sc * acc[j][ct];
+      }
+    }
+    return;
+  }
   const long obase = (((long)b * a.H + h) * a.T + t) * (long)(D * D);
 #pragma unroll
   for (int j = 0; j < C::RT; ++j) {
@@ -249,9 +272,85 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
   }
 }
 
+// Sum of the P fp32 partials of one (b, t, h) frame and matrix r, in split
+// order, written in the intermediate type and the output's layout.  One
+// thread per 4 contiguous values of the tile layout.
+template <int IO, int NT, int NR>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs a) {
+  typedef typename Io<IO>::elem E;
+  constexpr int D = 16 * NT;
+  constexpr int Q = D * D / 4;                 // 4-value groups per matrix
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long nframes = (long)a.B * a.H * a.Tc;
+  if (gid >= nframes * NR * Q) return;
+  const int q = (int)(gid % Q);
+  const int m = (int)((gid / Q) % NR);
+  const long f = gid / ((long)Q * NR);          // (b, h, tl)
+  const int tl = (int)(f % a.Tc);
+  const long bh = f / a.Tc;
+  f32x4 sum = zero4();
+  for (int p = 0; p < a.P; ++p)
+    sum += *reinterpret_cast<const f32x4*>(a.part + (((long)p * nframes + f) * NR + m) * (long)(D * D) +
+                                           (long)q * 4);
+  const int lane = q % 64, tile = q / 64;
+  const int ft = tile / NT, ct = tile % NT, g = lane >> 4, li = lane & 15;
+  E* out = static_cast<E*>(m == 0 ? a.out0 : a.out1) + (bh * a.T + a.t0 + tl) * (long)(D * D);
+  if ((m == 0 ? a.layout0 : a.layout1) == LAYOUT_TILES) {
+    E* dst = out + (long)q * 4;
+    if constexpr (IO == IO_BF16) {
+      u32x2 pk;
+      pk[0] = (uint32_t)f32_to_bf16_bits(sum[0]) | ((uint32_t)f32_to_bf16_bits(sum[1]) << 16);
+      pk[1] = (uint32_t)f32_to_bf16_bits(sum[2]) | ((uint32_t)f32_to_bf16_bits(sum[3]) << 16);
+      *reinterpret_cast<u32x2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = sum;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      E* dst = out + (ft * 16 + 4 * g + r) * D + ct * 16 + li;
+      if constexpr (IO == IO_BF16)
+        *dst = f32_to_bf16_bits(sum[r]);
+      else
+        *dst = sum[r];
+    }
+  }
+}
+
+template <int IO, int NT>
+static hipError_t launch_gram_reduce_nt(const GramArgs& a, int nr, hipStream_t s) {
+  const long n = (long)a.B * a.H * a.Tc * nr * (16 * NT) * (16 * NT) / 4;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (nr == 2)
+    hipLaunchKernelGGL((gram_reduce_kernel<IO, NT, 2>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gram_reduce_kernel<IO, NT, 1>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int IO>
+static hipError_t launch_gram_reduce_io(const GramArgs& a, int nt, int nr, hipStream_t s) {
+  switch (nt) {
+    case 1: return launch_gram_reduce_nt<IO, 1>(a, nr, s);
+    case 2: return launch_gram_reduce_nt<IO, 2>(a, nr, s);
+    case 3: return launch_gram_reduce_nt<IO, 3>(a, nr, s);
+    case 4: return launch_gram_reduce_nt<IO, 4>(a, nr, s);
+    case 5: return launch_gram_reduce_nt<IO, 5>(a, nr, s);
+    case 6: return launch_gram_reduce_nt<IO, 6>(a, nr, s);
+    case 7: return launch_gram_reduce_nt<IO, 7>(a, nr, s);
+    case 8: return launch_gram_reduce_nt<IO, 8>(a, nr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gram_reduce(const GramArgs& a, int io, int nt, int nr, hipStream_t s) {
+  return io == IO_BF16 ? launch_gram_reduce_io<IO_BF16>(a, nt, nr, s)
+                       : launch_gram_reduce_io<IO_F32>(a, nt, nr, s);
+}
+
 template <int IO, int NT>
 static hipError_t launch_gram_nt(const GramArgs& a, int nr, hipStream_t s) {
-  const dim3 grid(a.B * a.Tc * a.H), block(256);
+  const dim3 grid(a.B * a.Tc * a.H * a.P), block(256);
   if (nr == 2)
     hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true>), grid, block, 0, s, a);
   else

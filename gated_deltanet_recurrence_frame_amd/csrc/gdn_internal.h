@@ -28,8 +28,15 @@ struct GramArgs {
   float scale0, scale1;
   int B, H, T, N;
   int t0, Tc;          // frames t0 .. t0 + Tc - 1 of the T-frame tensors
+  // Token splits: P > 1 splits each frame's token chunks over P workgroups,
+  // which write fp32 partial sums (scaled, tile layout) to
+  //   part[(((p * B + b) * H + h) * Tc + (t - t0)) * NR + r] x D x D;
+  // launch_gram_reduce then sums them in a fixed order into out0 / out1.
+  int P;
+  float* part;
 };
 hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
+hipError_t launch_gram_reduce(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
 
 // Inter-frame scan over the carried D x D matrix Z, 16 rows per workgroup.
 //   forward  (reverse = 0), t = 0..T-1:  Z <- gamma_t Z - Z A_t + U_t; emit Z
@@ -58,6 +65,7 @@ struct OutArgs {
   void* out;            // [B, L, H, D] io dtype
   int B, H, T, N;
   int t0, Tc;           // frames t0 .. t0 + Tc - 1
+  int P;                // token splits: each frame's chunks over P workgroups
 };
 hipError_t launch_output(const OutArgs& a, int io, int nt, bool trans, hipStream_t s);
 

@@ -33,11 +33,12 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring[STAGES][MAT_BYTES];
   __shared__ __attribute__((aligned(16))) E obuf[2][CT * D];   // output chunk staging
 
-  const int total = a.B * a.Tc * a.H;
+  const int total = a.B * a.Tc * a.H * a.P;
   const int item = xcd_item(blockIdx.x, total);
-  const int h = item % a.H;
-  const int t = a.t0 + (item / a.H) % a.Tc;
-  const int b = item / (a.H * a.Tc);
+  const int sp = item % a.P;                       // token split
+  const int h = (item / a.P) % a.H;
+  const int t = a.t0 + (item / (a.P * a.H)) % a.Tc;
+  const int b = item / (a.P * a.H * a.Tc);
   const int N = a.N;
   const long row0 = (long)b * a.T * N + (long)t * N;
   const int lane = lane_id(), ft = wave_id();
@@ -82,8 +83,15 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   // Copy op i = ft + NT j of a chunk covers LDS bytes [1 KB i, +1 KB) of the
   // stage, lane l the 16 bytes at + 16 l (token row o / (D*ES)).
   const char* qsrc = static_cast<const char*>(a.tok);
+  const int nchunks_all = (N + CT - 1) / CT;
+  const int cps = (nchunks_all + a.P - 1) / a.P;  // chunks per split
+  const int cbeg = sp * cps;
+  const int nchunks = min(nchunks_all, cbeg + cps) - cbeg;
+  if (nchunks <= 0) return;                        // before any barrier
+
+  // local chunk c is frame chunk cbeg + c
   auto issue = [&](int c) {
-    const int c0 = c * CT;
+    const int c0 = (cbeg + c) * CT;
 #pragma unroll
     for (int j = 0; j < OPS; ++j) {
       const int i = ft + NT * j;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
     constexpr int PRW = D * ES / 16;
     for (int p = tid; p < CT * PRW; p += NTH) {
       const int row = p / PRW, pc = p % PRW;
-      const int tk = c * CT + row;
+      const int tk = (cbeg + c) * CT + row;
       if (tk < N)
         *reinterpret_cast<u32x4*>(static_cast<E*>(a.out) + ((row0 + tk) * a.H + h) * (long)D +
                                   pc * (16 / ES)) =
@@ -112,7 +120,6 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
     }
   };
 
-  const int nchunks = (N + CT - 1) / CT;
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nchunks) issue(c);
@@ -159,8 +166,8 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
 
 template <int IO, int NT, bool TRANS>
 static hipError_t launch_output_nt(const OutArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((output_kernel<IO, NT, TRANS>), dim3(a.B * a.Tc * a.H), dim3(64 * NT), 0, s,
-                     a);
+  hipLaunchKernelGGL((output_kernel<IO, NT, TRANS>), dim3(a.B * a.Tc * a.H * a.P), dim3(64 * NT),
+                     0, s, a);
   return hipGetLastError();
 }
 

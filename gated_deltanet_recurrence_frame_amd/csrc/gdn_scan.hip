@@ -176,7 +176,7 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
           z = gam * z - p;
         else
           z = gam * z - p + u;
-        load(ring[j], s + PD);
+        load(ring[j], s + PD);   // unconditional (clamped) keeps the compiler's wait counts exact
       }
     }
   }

@@ -55,7 +55,9 @@ def test_workspace_sizes(lib):
     assert _ws(p, gb.GDN_OP_BACKWARD) == (0, 6 * mat)
     assert gb.STATUS[_ws(p, gb.GDN_OP_STEP)[0]] == "GDN_ERR_BAD_SHAPE"     # T != 1
     p1 = gb.make_problem(B, H, 1, N, D, "bf16")
-    assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 2)
+    # a streaming step splits each frame's tokens over 8 workgroups and
+    # keeps their fp32 partial A_t, U_t in the workspace
+    assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 2 + 8 * B * H * 2 * D * D * 4)
     assert gb.saved_size(p) == 2 * mat
     pf = gb.make_problem(B, H, T, N, D, "fp32")
     assert gb.saved_size(pf) == 2 * B * H * T * D * D * 4

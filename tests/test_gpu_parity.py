@@ -203,9 +203,11 @@ def test_step_chain_equals_forward(io):
                             d["beta"][:, sl].contiguous(), state).clone())
     torch.cuda.synchronize()
     o_step = torch.cat(outs, dim=1)
-    # the step path runs the same kernels frame by frame: identical results
-    assert torch.equal(o_step, o_full)
-    assert torch.equal(state, s_full)
+    # the step path runs the same kernels frame by frame, the Gram/write sums
+    # split over token ranges (fixed order): equal up to summation order
+    tol_same = 1e-6 if io == "fp32" else 2e-3
+    assert rel_l2(f64(o_step.cpu()), f64(o_full.cpu())) <= tol_same
+    assert rel_l2(f64(state.cpu()), f64(s_full.cpu())) <= tol_same
     ro, rs = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
                             f64(inp["beta"]), N, state_in=f64(inp["state"]))
     assert rel_l2(f64(o_step.cpu()), ro) <= TOL[io]
