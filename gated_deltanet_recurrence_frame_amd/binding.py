@@ -217,7 +217,7 @@ def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None):
 
 
 def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None, saved=None,
-             key_scale=0.0, workspace=None):
+             key_scale=0.0, workspace=None, scan_chunk=0):
     """Gradients dict (dq, dk, dv, dgamma, dbeta, dstate_in) of gdn_backward."""
     B, L, H, D, T, dev = _shapes(q, k, v, gamma, beta, n)
     _need(d_o, "d_o", q.dtype, (B, L, H, D), dev)
@@ -225,7 +225,7 @@ def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None, save
         _need(state_in, "state_in", torch.float32, (B, H, D, D), dev)
     if d_state_out is not None:
         _need(d_state_out, "d_state_out", torch.float32, (B, H, D, D), dev)
-    prob = make_problem(B, H, T, n, D, _io_of(q), key_scale, 0)
+    prob = make_problem(B, H, T, n, D, _io_of(q), key_scale, scan_chunk)
     if saved is not None and saved.numel() != saved_size(prob):
         raise ValueError("saved buffer has the wrong size")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

@@ -34,7 +34,6 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (p->scan_chunk < 0) return GDN_ERR_BAD_SHAPE;
   if (!isfinite(p->key_scale)) return GDN_ERR_BAD_SHAPE;
   if (p->Dk != p->Dv || p->Dk % 16 != 0 || p->Dk > 128) return GDN_ERR_UNSUPPORTED;
-  if (p->scan_chunk > 1) return GDN_ERR_UNSUPPORTED;
   Shape s;
   s.B = p->B; s.H = p->H; s.T = p->T; s.N = p->N; s.D = p->Dk;
   s.L = s.T * s.N;
@@ -47,7 +46,7 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   s.chunk = p->scan_chunk == 0 ? kDefaultChunk : p->scan_chunk;
   if (s.chunk > s.T) s.chunk = (int)s.T;
   s.mat = s.B * s.H * s.T * s.D * s.D * s.es;
-  s.parts = (s.T + s.chunk - 1) / s.chunk;
+  s.parts = s.chunk <= 1 ? 1 : (s.T + s.chunk - 1) / s.chunk;   // 1: sequential
   *sh = s;
   return GDN_OK;
 }
@@ -80,8 +79,20 @@ int64_t partial_bytes(const Shape& s, int nr) {
   return p > 1 ? (int64_t)p * s.B * s.H * s.T * nr * s.D * s.D * 4 : 0;
 }
 
-int64_t forward_ws(const Shape& s) { return 3 * s.mat + partial_bytes(s, 2); }
-int64_t backward_ws(const Shape& s) { return 6 * s.mat + partial_bytes(s, 2); }
+// Chunked scan: -C_w^T, H_w and the entering state of every chunk, fp32.
+int64_t composite_bytes(const Shape& s) {
+  return s.parts > 1 ? 3 * s.B * s.H * s.parts * s.D * s.D * 4 : 0;
+}
+// The token-split partials (used by the Gram launches) and the composites
+// (used by the scans) are never live at the same time on the stream, so
+// they share one region after the D x D buffers.
+int64_t scratch_bytes(const Shape& s) {
+  const int64_t a = partial_bytes(s, 2), b = composite_bytes(s);
+  return a > b ? a : b;
+}
+
+int64_t forward_ws(const Shape& s) { return 3 * s.mat + scratch_bytes(s); }
+int64_t backward_ws(const Shape& s) { return 6 * s.mat + scratch_bytes(s); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
@@ -106,6 +117,44 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
 }
 
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// Inter-frame scan over the whole sequence, sequential or chunked
+// (composites, a fold over chunks, then a parallel replay of every chunk).
+gdn_status run_scan(const Shape& s, const void* A, const void* U, const float* gamma,
+                    const float* z0, void* emit, float* zT, bool reverse, char* scratch,
+                    hipStream_t stream) {
+  const int nt = (int)(s.D / 16);
+  ScanArgs sa{};
+  sa.A = A; sa.U = U; sa.gamma = gamma; sa.z0 = z0; sa.emit = emit; sa.zT = zT;
+  sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
+  sa.t0 = 0; sa.Tc = (int)s.T;
+  const int mode = reverse ? SCAN_REV : SCAN_FWD;
+  if (s.parts <= 1) return hip_status(launch_scan(sa, s.io, nt, mode, stream));
+
+  const int64_t cm = s.B * s.H * s.parts * s.D * s.D;   // floats per composite buffer
+  float* compC = reinterpret_cast<float*>(scratch);
+  float* compH = compC + cm;
+  float* zmid = compH + cm;
+  ScanArgs ca = sa;
+  ca.z0 = nullptr; ca.emit = nullptr; ca.zT = nullptr;
+  ca.chunk = s.chunk; ca.compC = compC; ca.compH = compH;
+  gdn_status st = hip_status(
+      launch_scan(ca, s.io, nt, reverse ? SCAN_COMP_REV : SCAN_COMP_FWD, stream));
+  if (st != GDN_OK) return st;
+
+  // Fold: Z_{w+1} = Z_w C_w + H_w, in fp32, emitting every chunk's entering state.
+  ScanArgs fa{};
+  fa.A = compC; fa.U = compH; fa.gamma = nullptr; fa.z0 = z0;
+  fa.emit = zmid + s.D * s.D;   // slot t + 1 receives the state after chunk t
+  fa.emit_entry = 1;            // slot 0 receives z0 itself
+  fa.B = (int)s.B; fa.H = (int)s.H; fa.T = (int)s.parts;
+  fa.t0 = 0; fa.Tc = (int)s.parts - 1;
+  st = hip_status(launch_scan(fa, IO_F32, nt, SCAN_FWD, stream));
+  if (st != GDN_OK) return st;
+
+  sa.chunk = s.chunk; sa.zmid = zmid;
+  return hip_status(launch_scan(sa, s.io, nt, mode, stream));
+}
 
 // Forward pipeline shared by gdn_forward and gdn_step.
 gdn_status record(void* const* events, int i, hipStream_t stream) {
@@ -141,13 +190,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   st = record(events, 1, stream);
   if (st != GDN_OK) return st;
 
-  {
-    ScanArgs sa{};
-    sa.A = A; sa.U = U; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S; sa.zT = state_out;
-    sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
-    sa.t0 = 0; sa.Tc = (int)s.T;
-    st = hip_status(launch_scan(sa, s.io, nt, false, stream));
-  }
+  st = run_scan(s, A, U, gamma, state_in, S, state_out, false, ws + 3 * s.mat, stream);
   if (st != GDN_OK) return st;
   st = record(events, 2, stream);
   if (st != GDN_OK) return st;
@@ -326,11 +369,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     if (st != GDN_OK) return st;
     if (ga.P > 1 && (st = hip_status(launch_gram_reduce(ga, s.io, nt, 2, stream_))) != GDN_OK)
       return st;
-    ScanArgs sa{};
-    sa.A = A_; sa.U = U_; sa.gamma = gamma; sa.z0 = state_in; sa.emit = S_; sa.zT = nullptr;
-    sa.B = (int)s.B; sa.H = (int)s.H; sa.T = (int)s.T;
-    sa.t0 = 0; sa.Tc = (int)s.T;
-    st = hip_status(launch_scan(sa, s.io, nt, false, stream_));
+    st = run_scan(s, A_, U_, gamma, state_in, S_, nullptr, false, ws + 6 * s.mat, stream_);
     if (st != GDN_OK) return st;
     A = A_;
     S = S_;
@@ -354,11 +393,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     return st;
 
   // Reverse scan: G_t = X_t + G_{t+1} M_{t+1}^T, dS_0 = G_1 M_1^T.
-  ScanArgs ra{};
-  ra.A = A; ra.U = X; ra.gamma = gamma; ra.z0 = d_state_out; ra.emit = G; ra.zT = d_state_in;
-  ra.B = (int)s.B; ra.H = (int)s.H; ra.T = (int)s.T;
-  ra.t0 = 0; ra.Tc = (int)s.T;
-  st = hip_status(launch_scan(ra, s.io, nt, true, stream_));
+  st = run_scan(s, A, X, gamma, d_state_out, G, d_state_in, true, ws + 6 * s.mat, stream_);
   if (st != GDN_OK) return st;
 
   DmArgs da{};

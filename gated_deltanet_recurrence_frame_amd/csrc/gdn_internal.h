@@ -39,22 +39,42 @@ hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s)
 hipError_t launch_gram_reduce(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
 
 // Inter-frame scan over the carried D x D matrix Z, 16 rows per workgroup.
-//   forward  (reverse = 0), t = 0..T-1:  Z <- gamma_t Z - Z A_t + U_t; emit Z
-//   backward (reverse = 1), t = T-1..0:  Z <- Z + U_t; emit Z;
-//                                        Z <- gamma_t Z - Z A_t
+//   forward  (SCAN_FWD), t = t0..t0+Tc-1:   Z <- gamma_t Z - Z A_t + U_t; emit Z
+//   backward (SCAN_REV), t = t0+Tc-1..t0:   Z <- Z + U_t; emit Z;
+//                                           Z <- gamma_t Z - Z A_t
 // z0 / zT: [B, H, D, D] fp32 initial / final Z (nullptr: zero / not written).
+// gamma == nullptr means gamma_t = 0 (used by the chunk fold below).
+//
+// Composite (chunked) scan.  With chunk = c > 0 the walk (in walk order:
+// forward or backward in t) is cut into nck = ceil(Tc / c) chunks that run
+// in parallel:
+//   SCAN_COMP_FWD / SCAN_COMP_REV walk each chunk w twice at once, from
+//     Z = 0 with the inputs (H_w) and from Z = I without them (C_w, the
+//     product of the chunk's transition matrices in walk order), and store
+//     compH[w] = H_w (tiles) and compC[w] = -C_w^T (row-major), fp32;
+//   a fold, the forward scan in fp32 with A = compC, U = compH,
+//     gamma = nullptr and emit_entry = 1 over the nck - 1 first slots,
+//     gives the state entering every chunk, Z_w = Z_{w-1} C_{w-1} + H_{w-1};
+//   SCAN_FWD / SCAN_REV with the same chunk then replay every chunk from
+//     zmid[w] = Z_w (slot w of [B, H, nck] x D x D fp32), emitting as the
+//     sequential walk does; only the last chunk writes zT.
+enum ScanMode { SCAN_FWD = 0, SCAN_REV = 1, SCAN_COMP_FWD = 2, SCAN_COMP_REV = 3 };
 struct ScanArgs {
   const void* A;        // [B, H, T] x D x D row-major, intermediate type
   const void* U;        // [B, H, T] x D x D tiles, intermediate type
-  const float* gamma;   // [B, T, H]
+  const float* gamma;   // [B, T, H], or nullptr for 0
   const float* z0;
   void* emit;           // [B, H, T] x D x D row-major, intermediate type
   float* zT;
   int B, H, T;
-  int t0, Tc;           // forward: frames t0 .. t0 + Tc - 1 (z0 = state before t0);
-                        // reverse: whole sequence (t0 = 0, Tc = T)
+  int t0, Tc;           // frames t0 .. t0 + Tc - 1 of the T-frame tensors
+  int chunk;            // 0: one walk; c > 0: chunks of c frames (see above)
+  int emit_entry;       // forward: also emit the entering Z (at slot t0 - 1)
+  const float* zmid;    // replay with chunk > 0: entering state of every chunk
+  float* compC;         // composite output -C_w^T
+  float* compH;         // composite output H_w
 };
-hipError_t launch_scan(const ScanArgs& a, int io, int nt, bool reverse, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, int io, int nt, int mode, hipStream_t s);
 
 // Token-stream product with a per-frame D x D matrix M, one wave per output
 // feature tile: out[n] = M tok[n] (trans = false) or M^T tok[n] (trans =

@@ -28,6 +28,14 @@
 // G_t = dO_t Q^_t^T + G_{t+1} M_{t+1}^T) runs the same code backwards in t:
 // the input is added first, the sum is staged and stored, then multiplied
 // by M_t.
+//
+// Chunked mode (the transition / input composites of the context-parallel
+// scheme, summary page 技术新颖性 point 1, with chunks of frames in place
+// of devices): the composite walk keeps 32 staged rows, 16 of the input
+// composite H (from zero, with the inputs) and 16 of the transition
+// composite C (from the identity, without them), which share every A_t
+// fragment.  C is kept in fp32 registers and stored in fp32; it is never
+// rounded to the intermediate type except as an MFMA operand, like S.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -35,10 +43,13 @@
 
 namespace gdn {
 
-template <int IO, int NT, bool REVERSE>
+template <int IO, int NT, int MODE>
 __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
   typedef typename Io<IO>::elem E;
   constexpr bool BF = (IO == IO_BF16);
+  constexpr bool REVERSE = (MODE & 1) != 0;
+  constexpr bool COMP = (MODE & 2) != 0;   // composite: H and C walked together
+  constexpr int ZR = COMP ? 32 : 16;       // staged rows (H rows, then C rows)
   constexpr int D = 16 * NT;
   constexpr int ES = Io<IO>::bytes;
   constexpr int KB = BF ? (D + 31) / 32 : D / 4;   // MFMA steps of one product
@@ -53,30 +64,44 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     AF af[NAF];
     UF u;
   };
-  __shared__ __attribute__((aligned(16))) E Zbuf[2][16 * ZLD];
+  __shared__ __attribute__((aligned(16))) E Zbuf[2][ZR * ZLD];
   __shared__ float gam_lds[GW];
 
-  const int total = a.B * a.H * NT;
+  const int NW = a.Tc;                                // frames of the whole walk
+  const int CH = a.chunk > 0 ? a.chunk : NW;
+  const int nck = (NW + CH - 1) / CH;
+  const int total = a.B * a.H * nck * NT;
   const int item = xcd_item(blockIdx.x, total);
-  const int bh = item / NT, rb = item % NT;
+  const int rb = item % NT;
+  const int w = (item / NT) % nck;                    // chunk, in walk order
+  const int bh = item / NT / nck;
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
   const int lane = lane_id(), ct = wave_id();
   const int g = lane >> 4, li = lane & 15;
   const long DD = (long)D * D;
-  const int T = a.T;             // frames in the tensors
-  const int NS = a.Tc;           // frames walked by this launch, from a.t0
+  const int T = a.T;                                  // frames in the tensors
+  const int sb = w * CH;                              // first walk step of the chunk
+  const int NS = NW - sb < CH ? NW - sb : CH;         // steps walked here
   const E* Ab = static_cast<const E*>(a.A) + (long)bh * T * DD;
   const E* Ub = static_cast<const E*>(a.U) + (long)bh * T * DD;
   E* Eb = static_cast<E*>(a.emit) + (long)bh * T * DD;
 
   f32x4 z = zero4();
-  if (a.z0) {
+  f32x4 zc = zero4();   // COMP: the transition composite, from the identity
+  if constexpr (COMP) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = a.z0[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li];
+    for (int r = 0; r < 4; ++r) zc[r] = (rb * 16 + 4 * g + r == ct * 16 + li) ? 1.f : 0.f;
+  } else {
+    const float* zs = a.chunk > 0 ? a.zmid + ((long)bh * nck + w) * DD
+                                  : (a.z0 ? a.z0 + (long)bh * DD : nullptr);
+    if (zs) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[r] = zs[(rb * 16 + 4 * g + r) * D + ct * 16 + li];
+    }
   }
 
-  auto frame_of = [&](int s) { return REVERSE ? a.t0 + NS - 1 - s : a.t0 + s; };
+  auto frame_of = [&](int s) { return REVERSE ? a.t0 + NW - 1 - (sb + s) : a.t0 + sb + s; };
   auto load = [&](Buf& B, int s) {
     const int t = frame_of(s < NS ? s : NS - 1);
     const E* At = Ab + t * DD + (ct * 16 + li) * D;
@@ -106,14 +131,14 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
       return B.u;
     }
   };
-  auto stage = [&](int cur) {
+  auto stage_tile = [&](int cur, int row0, const f32x4& v) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      E* dst = &Zbuf[cur][(4 * g + r) * ZLD + ct * 16 + li];
+      E* dst = &Zbuf[cur][(row0 + 4 * g + r) * ZLD + ct * 16 + li];
       if constexpr (BF)
-        *dst = f32_to_bf16_bits(z[r]);
+        *dst = f32_to_bf16_bits(v[r]);
       else
-        *dst = z[r];
+        *dst = v[r];
     }
   };
   auto emit_rows = [&](int cur, int t) {   // the 16 staged rows -> S_t / G_t
@@ -127,8 +152,26 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
   auto load_gammas = [&](int s0) {
     for (int i = tid; i < GW; i += NTH) {
       const int s = s0 + i;
-      gam_lds[i] = s < NS ? a.gamma[((long)b * T + frame_of(s)) * a.H + h] : 0.f;
+      gam_lds[i] = (s < NS && a.gamma) ? a.gamma[((long)b * T + frame_of(s)) * a.H + h] : 0.f;
     }
+  };
+  auto product = [&](const E* zrow, const Buf& B) {   // staged rows x A_t
+    f32x4 p = zero4();
+    if constexpr (BF) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k = kb * 32 + 8 * g;
+        const bf16x8 zf = (k < D) ? load_bf16x8(zrow + k) : zero_bf16x8();
+        p = mfma_bf16(zf, B.af[kb], p);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NAF; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p = mfma_f32(zrow[g * (D / 4) + 4 * q + e], B.af[q][e], p);
+    }
+    return p;
   };
 
   Buf ring[PD];
@@ -148,29 +191,21 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
         }
         const f32x4 u = unpack_u(ring[j]);
         if constexpr (REVERSE) z += u;
-        stage(cur);
+        stage_tile(cur, 0, z);
+        if constexpr (COMP) stage_tile(cur, 16, zc);
         block_sync();
         const float gam = gam_lds[s % GW];
-        if constexpr (REVERSE)
-          emit_rows(cur, t);
-        else if (s > 0)
-          emit_rows(cur, t - 1);
+        if constexpr (!COMP) {
+          if constexpr (REVERSE)
+            emit_rows(cur, t);
+          else if (s > 0 || a.emit_entry)
+            emit_rows(cur, t - 1);
+        }
         // P = Z[rows] A_t
-        f32x4 p = zero4();
-        const E* zrow = &Zbuf[cur][li * ZLD];
-        if constexpr (BF) {
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const int k = kb * 32 + 8 * g;
-            const bf16x8 zf = (k < D) ? load_bf16x8(zrow + k) : zero_bf16x8();
-            p = mfma_bf16(zf, ring[j].af[kb], p);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < NAF; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              p = mfma_f32(zrow[g * (D / 4) + 4 * q + e], ring[j].af[q][e], p);
+        const f32x4 p = product(&Zbuf[cur][li * ZLD], ring[j]);
+        if constexpr (COMP) {
+          const f32x4 pc = product(&Zbuf[cur][(16 + li) * ZLD], ring[j]);
+          zc = gam * zc - pc;
         }
         if constexpr (REVERSE)
           z = gam * z - p;
@@ -181,46 +216,63 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     }
   }
 
-  if constexpr (!REVERSE) {   // the walk's last state still has to be stored
-    const int cur = NS & 1;
-    stage(cur);
-    block_sync();
-    emit_rows(cur, a.t0 + NS - 1);
-  }
-  if (a.zT) {
+  if constexpr (COMP) {
+    float* Hd = a.compH + ((long)bh * nck + w) * DD + ((rb * NT + ct) * 64 + lane) * 4;
+    *reinterpret_cast<f32x4*>(Hd) = z;
+    float* Cd = a.compC + ((long)bh * nck + w) * DD + (ct * 16 + li) * D + rb * 16 + 4 * g;
+    *reinterpret_cast<f32x4*>(Cd) = -zc;
+  } else {
+    if constexpr (!REVERSE) {   // the walk's last state still has to be stored
+      const int cur = NS & 1;
+      stage_tile(cur, 0, z);
+      block_sync();
+      emit_rows(cur, frame_of(NS - 1));
+    }
+    if (a.zT && w == nck - 1) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a.zT[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li] = z[r];
+      for (int r = 0; r < 4; ++r) a.zT[(long)bh * DD + (rb * 16 + 4 * g + r) * D + ct * 16 + li] = z[r];
+    }
   }
 }
 
 template <int IO, int NT>
-static hipError_t launch_scan_nt(const ScanArgs& a, bool reverse, hipStream_t s) {
-  const dim3 grid(a.B * a.H * NT), block(64 * NT);
-  if (reverse)
-    hipLaunchKernelGGL((scan_kernel<IO, NT, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((scan_kernel<IO, NT, false>), grid, block, 0, s, a);
+static hipError_t launch_scan_nt(const ScanArgs& a, int mode, hipStream_t s) {
+  const int ch = a.chunk > 0 ? a.chunk : a.Tc;
+  const int nck = (a.Tc + ch - 1) / ch;
+  const dim3 grid(a.B * a.H * nck * NT), block(64 * NT);
+  switch (mode) {
+    case SCAN_FWD: hipLaunchKernelGGL((scan_kernel<IO, NT, SCAN_FWD>), grid, block, 0, s, a); break;
+    case SCAN_REV: hipLaunchKernelGGL((scan_kernel<IO, NT, SCAN_REV>), grid, block, 0, s, a); break;
+    case SCAN_COMP_FWD:
+      hipLaunchKernelGGL((scan_kernel<IO, NT, SCAN_COMP_FWD>), grid, block, 0, s, a);
+      break;
+    case SCAN_COMP_REV:
+      hipLaunchKernelGGL((scan_kernel<IO, NT, SCAN_COMP_REV>), grid, block, 0, s, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <int IO>
-static hipError_t launch_scan_io(const ScanArgs& a, int nt, bool reverse, hipStream_t s) {
+static hipError_t launch_scan_io(const ScanArgs& a, int nt, int mode, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_scan_nt<IO, 1>(a, reverse, s);
-    case 2: return launch_scan_nt<IO, 2>(a, reverse, s);
-    case 3: return launch_scan_nt<IO, 3>(a, reverse, s);
-    case 4: return launch_scan_nt<IO, 4>(a, reverse, s);
-    case 5: return launch_scan_nt<IO, 5>(a, reverse, s);
-    case 6: return launch_scan_nt<IO, 6>(a, reverse, s);
-    case 7: return launch_scan_nt<IO, 7>(a, reverse, s);
-    case 8: return launch_scan_nt<IO, 8>(a, reverse, s);
+    case 1: return launch_scan_nt<IO, 1>(a, mode, s);
+    case 2: return launch_scan_nt<IO, 2>(a, mode, s);
+    case 3: return launch_scan_nt<IO, 3>(a, mode, s);
+    case 4: return launch_scan_nt<IO, 4>(a, mode, s);
+    case 5: return launch_scan_nt<IO, 5>(a, mode, s);
+    case 6: return launch_scan_nt<IO, 6>(a, mode, s);
+    case 7: return launch_scan_nt<IO, 7>(a, mode, s);
+    case 8: return launch_scan_nt<IO, 8>(a, mode, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan(const ScanArgs& a, int io, int nt, bool reverse, hipStream_t s) {
-  return io == IO_BF16 ? launch_scan_io<IO_BF16>(a, nt, reverse, s)
-                       : launch_scan_io<IO_F32>(a, nt, reverse, s);
+hipError_t launch_scan(const ScanArgs& a, int io, int nt, int mode, hipStream_t s) {
+  if (a.Tc < 1) return hipErrorInvalidValue;
+  return io == IO_BF16 ? launch_scan_io<IO_BF16>(a, nt, mode, s)
+                       : launch_scan_io<IO_F32>(a, nt, mode, s);
 }
 
 }  // namespace gdn

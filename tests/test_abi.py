@@ -59,6 +59,15 @@ def test_workspace_sizes(lib):
     # keeps their fp32 partial A_t, U_t in the workspace
     assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 2 + 8 * B * H * 2 * D * D * 4)
     assert gb.saved_size(p) == 2 * mat
+    # a chunked scan (8-frame chunks: 16 chunks) keeps -C_w^T, H_w and the
+    # entering state of every chunk in fp32
+    pc = gb.make_problem(B, H, T, N, D, "bf16", scan_chunk=8)
+    comp = 3 * B * H * 16 * D * D * 4
+    assert _ws(pc, gb.GDN_OP_FORWARD) == (0, 3 * mat + comp)
+    assert _ws(pc, gb.GDN_OP_BACKWARD) == (0, 6 * mat + comp)
+    # a chunk as long as the sequence is the sequential scan
+    assert _ws(gb.make_problem(B, H, T, N, D, "bf16", scan_chunk=T), gb.GDN_OP_FORWARD) == (0, 3 * mat)
+    assert _ws(gb.make_problem(B, H, T, N, D, "bf16", scan_chunk=500), gb.GDN_OP_FORWARD) == (0, 3 * mat)
     pf = gb.make_problem(B, H, T, N, D, "fp32")
     assert gb.saved_size(pf) == 2 * B * H * T * D * D * 4
 

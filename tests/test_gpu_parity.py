@@ -216,7 +216,7 @@ def test_step_chain_equals_forward(io):
 
 # -------------------------------------------------------------- backward
 def check_backward(inp, N, io, with_state=True, with_dstate=True, use_saved=False,
-                   key_scale=0.0):
+                   key_scale=0.0, scan_chunk=0):
     d = {k: to_dev(v) for k, v in inp.items()}
     st = d["state"] if with_state else None
     dst = d["d_state"] if with_dstate else None
@@ -225,7 +225,8 @@ def check_backward(inp, N, io, with_state=True, with_dstate=True, use_saved=Fals
         _, _, saved = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
                                  state_in=st, key_scale=key_scale, return_saved=True)
     gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
-                     state_in=st, d_state_out=dst, saved=saved, key_scale=key_scale)
+                     state_in=st, d_state_out=dst, saved=saved, key_scale=key_scale,
+                     scan_chunk=scan_chunk)
     torch.cuda.synchronize()
     ref = oracle.backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
                           f64(inp["beta"]), N, f64(inp["d_o"]),
@@ -238,7 +239,7 @@ def check_backward(inp, N, io, with_state=True, with_dstate=True, use_saved=Fals
     print("backward rel_l2:", {k: "%.2e" % v for k, v in errs.items()})
     for name, e in errs.items():
         assert e <= TOL[io], (name, e)
-    return errs
+    return errs, gr
 
 
 def test_backward_tiny_fp32():
@@ -266,6 +267,82 @@ def test_backward_delta_stress(io):
 def test_backward_short_clip_bf16():
     inp = gin.make_config("short", seed=0, with_do=True)
     check_backward(inp, 880, "bf16", with_state=False, with_dstate=False, use_saved=True)
+
+
+# ------------------------------------------ chunked (composite) scan
+# The transition / input composites of the context-parallel scheme (summary
+# page, 技术新颖性 point 1), with chunks of frames standing in for devices:
+# the chunked forward and backward must give the sequential result.
+# Sequential and chunked GPU runs differ only in rounding order (fp32 fold of
+# the composites), so they are compared with a bar well under the oracle's.
+SAME = {"fp32": 2e-6, "bf16": 5e-3}
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("chunk", [2, 3, 4, 11])
+def test_chunked_forward_matches_oracle(io, chunk):
+    B, H, T, N, D = 2, 3, 11, 100, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=30 + chunk,
+                          with_state=True)
+    (o, so), (ro, rs) = run_forward_pair(inp, N, io, scan_chunk=chunk, with_state=True)
+    eo, es = rel_l2(f64(o), ro), rel_l2(f64(so), rs)
+    print("chunk %d forward rel_l2: o %.3e state %.3e" % (chunk, eo, es))
+    assert eo <= TOL[io] and es <= TOL[io]
+    # the oracle's own composite path agrees with its sequential one
+    co, cs = oracle.composite_forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]),
+                                      f64(inp["gamma"]), f64(inp["beta"]), N, chunk,
+                                      state_in=f64(inp["state"]))
+    assert rel_l2(f64(o), co) <= TOL[io] and rel_l2(f64(so), cs) <= TOL[io]
+    (o1, so1), _ = run_forward_pair(inp, N, io, scan_chunk=1, with_state=True)
+    assert rel_l2(f64(o), f64(o1)) <= SAME[io]
+    assert rel_l2(f64(so), f64(so1)) <= SAME[io]
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [16, 48, 128])
+def test_chunked_forward_long_ragged(io, D):
+    # 64 frames in chunks of 5 (last chunk of 4): longer than the prefetch
+    # ring inside a chunk, 13 chunks in the fold
+    B, H, T, N = 1, 2, 64, 40
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=40 + D,
+                          with_state=True)
+    check_forward(inp, N, io, scan_chunk=5, with_state=True)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_chunked_forward_in_place(io):
+    # state_out == state_in: the first chunk reads the entering state only
+    # through the fold's copy, so the last chunk may overwrite it
+    B, H, T, N, D = 1, 3, 20, 64, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=50,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    st = d["state"].clone()
+    prob = gb.make_problem(B, H, T, N, D, io, scan_chunk=3)
+    o = torch.empty_like(d["v"])
+    ws = torch.empty(gb.workspace_size(prob, gb.GDN_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    import ctypes
+    code = gb.lib().gdn_forward(ctypes.byref(prob), gb._p(d["q"]), gb._p(d["k"]), gb._p(d["v"]),
+                                gb._p(d["gamma"]), gb._p(d["beta"]), gb._p(st), gb._p(o),
+                                gb._p(st), None, gb._p(ws), ws.numel(),
+                                gb._stream(torch.device(DEV)))
+    assert code == 0
+    o_ref, s_ref = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                              state_in=d["state"], scan_chunk=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(st, s_ref)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("chunk", [2, 3, 5])
+def test_chunked_backward(io, chunk):
+    inp = gin.make_inputs(B=2, H=3, T=11, N=100, D=112, io=io, gamma="uniform", seed=60 + chunk,
+                          with_do=True, with_dstate=True, with_state=True)
+    _, g_chunk = check_backward(inp, 100, io, scan_chunk=chunk)
+    _, g_seq = check_backward(inp, 100, io, scan_chunk=1, use_saved=True)
+    for name in ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]:
+        e = rel_l2(f64(g_chunk[name].cpu()), f64(g_seq[name].cpu()))
+        assert e <= SAME[io], (name, e)
 
 
 # ---------------------------------------------------- host-side failures
