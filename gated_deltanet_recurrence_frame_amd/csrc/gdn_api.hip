@@ -66,9 +66,11 @@ int gram_splits(const Shape& s) {
   return (int)(p < 1 ? 1 : p);
 }
 int out_splits(const Shape& s) {
-  const int64_t frames = s.B * s.T * s.H;
+  // the output kernel takes adjacent head pairs when H is even
+  const int64_t hpw = s.H % 2 == 0 ? 2 : 1;
+  const int64_t frames = s.B * s.T * (s.H / hpw);
   if (frames >= 512) return 1;
-  const int64_t ct = s.io == IO_BF16 ? 64 : 32;
+  const int64_t ct = (s.io == IO_BF16 ? 64 : 32) / hpw;
   int64_t p = (512 + frames - 1) / frames;
   const int64_t nch = (s.N + ct - 1) / ct;
   if (p > nch) p = nch;

@@ -130,6 +130,17 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, then barriers.  Unlike __syncthreads it carries no memory
+// fence, so it does not wait for global loads still in flight (a
+// prefetch ring stays in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // XCD-aware work ordering.  Hardware hands consecutive workgroup ids to the
 // 8 XCDs in turn; this maps them so that each XCD receives a contiguous
 // range of work items (neighbouring heads of the same frame share L2 there).

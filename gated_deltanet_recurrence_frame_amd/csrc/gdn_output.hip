@@ -1,15 +1,24 @@
 // Output pass of the frame-wise GDN: O_t = S_t Q^_t (summary page,
 // 方法步骤详情 module 2), i.e. o_{t,n} = S_t q_{t,n} for every token of the
-// frame, with S_t the state after frame t's own update.
+// frame, with S_t the state after frame t's own update.  The backward's
+// dQ^_t = S_t^T dO_t is the same pass on the transposed matrix.
 //
-// One workgroup per (b, t, h) frame (XCD-aware order), one wave per 16-row
-// feature tile of the output.  A wave keeps its 16 rows of S_t as MFMA
-// operand fragments in registers for the whole frame (bf16: 4 x 8 values
-// per lane at D = 112).  Query rows stream through a 3-stage LDS ring in
-// chunks (natural [token][feature] layout, copied straight from memory to
-// LDS two chunks ahead); every wave reads the chunk's query rows as the
-// other operand and stages its 16 features of each token in LDS; the next
-// iteration stores the chunk's output rows as contiguous 16-byte pieces.
+// One workgroup per (b, t, h) frame (or per token range of it, for
+// launches with few frames), XCD-aware order, one wave per 16-row feature
+// tile of the output.  A wave keeps its 16 rows of S_t as MFMA operand
+// fragments in registers for the whole frame.  Query rows stream in chunks
+// of CT tokens: each thread loads two 16-byte pieces of a chunk (whole
+// token rows per instruction) into a register ring PF chunks deep, commits
+// them to LDS in the natural [token][feature] layout one chunk at a time,
+// and every wave reads the chunk's query rows as the other MFMA operand.
+// The outputs of a chunk are staged in LDS and stored one iteration later
+// as contiguous 16-byte pieces of token rows.
+//
+// The ring is plain register loads that the compiler's wait counts track
+// exactly (no direct-to-LDS copies, whose waits the compiler cannot relax
+// while stores are pending), and the barriers are LDS-only, so the PF - 1
+// chunks ahead stay in flight across them.  The loop over whole chunks is
+// straight-line; the frame's last, partial chunk is finished after it.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -17,157 +26,221 @@
 
 namespace gdn {
 
-template <int IO, int NT, bool TRANS>
+template <int IO, int NT, bool TRANS, int HPW>
 __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   typedef typename Io<IO>::elem E;
+  constexpr bool BF = (IO == IO_BF16);
   constexpr int D = 16 * NT;
   constexpr int ES = Io<IO>::bytes;
-  constexpr int CT = (IO == IO_BF16) ? 64 : 32;
-  constexpr int MAT_BYTES = CT * D * ES;          // one chunk of query rows
-  constexpr int WL = MAT_BYTES / 1024;            // 1 KB copies per chunk (= 2 NT)
-  constexpr int OPS = WL / NT;                    // copies per wave per chunk
-  constexpr int STAGES = 3;
-  constexpr int KB = (IO == IO_BF16) ? (D + 31) / 32 : D / 4;
+  constexpr int RW = HPW * D;                    // elements of a token's row segment
+  constexpr int CT = (BF ? 64 : 32) / HPW;       // tokens per chunk
+  constexpr int PR = RW * ES / 16;               // 16-byte pieces per row segment
   constexpr int NTH = 64 * NT;
-  static_assert(WL % NT == 0, "copies must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES][MAT_BYTES];
-  __shared__ __attribute__((aligned(16))) E obuf[2][CT * D];   // output chunk staging
+  constexpr int PPT = CT * PR / NTH;             // pieces per thread per chunk (2)
+  constexpr int PF = 4;                          // chunks in flight
+  static_assert(PPT * NTH == CT * PR, "pieces must split evenly over the threads");
+  // contraction blocks: bf16 32-deep (the last one zero past D), fp32 4-deep
+  constexpr int KF = BF ? (D + 31) / 32 : D / 4;
+  constexpr bool KTAIL = BF && (D % 32) != 0;
+  // (16 elements of padding: the zeroed tail of the last row's read stays in the array)
+  __shared__ __attribute__((aligned(16))) E stage[2][CT * RW + 16];
+  __shared__ __attribute__((aligned(16))) E obuf[2][CT * RW];
 
-  const int total = a.B * a.Tc * a.H * a.P;
+  const int HG = a.H / HPW;                        // head groups
+  const int total = a.B * a.Tc * HG * a.P;
   const int item = xcd_item(blockIdx.x, total);
   const int sp = item % a.P;                       // token split
-  const int h = (item / a.P) % a.H;
-  const int t = a.t0 + (item / (a.P * a.H)) % a.Tc;
-  const int b = item / (a.P * a.H * a.Tc);
+  const int h0 = ((item / a.P) % HG) * HPW;        // first head of the group
+  const int t = a.t0 + (item / (a.P * HG)) % a.Tc;
+  const int b = item / (a.P * HG * a.Tc);
   const int N = a.N;
   const long row0 = (long)b * a.T * N + (long)t * N;
+  const int tid = threadIdx.x;
   const int lane = lane_id(), ft = wave_id();
   const int g = lane >> 4, li = lane & 15;
 
-  // This wave's rows of the frame matrix (intermediate type, row-major in
-  // memory) as left MFMA operands: rows of S_t, or with TRANS rows of
-  // S_t^T (columns of S_t; the backward's dQ = S_t^T dO), which are staged
-  // in LDS and read with the transposing LDS read.
-  const E* Sm = static_cast<const E*>(a.mat) + (((long)b * a.H + h) * a.T + t) * (long)(D * D);
-  typedef typename std::conditional<IO == IO_BF16, bf16x8, float>::type Frag;
-  Frag sf[KB];
-  if constexpr (!TRANS) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if constexpr (IO == IO_BF16) {
-        const int k = kb * 32 + 8 * g;
-        sf[kb] = (k < D) ? load_bf16x8(Sm + (ft * 16 + li) * D + k) : zero_bf16x8();
-      } else {
-        sf[kb] = Sm[(ft * 16 + li) * D + kb * 4 + g];
-      }
-    }
-  } else if constexpr (IO == IO_BF16) {
-    // [KB*32][D] rows in the output staging area (free until the first
-    // chunk), rows past D zero.
-    uint16_t* ms = reinterpret_cast<uint16_t*>(&obuf[0][0]);
-    constexpr int PRW = D / 8;
-    for (int p = threadIdx.x; p < KB * 32 * PRW; p += NTH) {
-      const int row = p / PRW, pc = p % PRW;
-      *reinterpret_cast<u32x4*>(ms + row * D + pc * 8) =
-          row < D ? *reinterpret_cast<const u32x4*>(Sm + row * D + pc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    block_sync();
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sf[kb] = lds_col_frag_bf16(ms, D, kb * 32, ft * 16);
-    block_sync();
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sf[kb] = Sm[(kb * 4 + g) * D + ft * 16 + li];
-  }
-
-  // Copy op i = ft + NT j of a chunk covers LDS bytes [1 KB i, +1 KB) of the
-  // stage, lane l the 16 bytes at + 16 l (token row o / (D*ES)).
-  const char* qsrc = static_cast<const char*>(a.tok);
   const int nchunks_all = (N + CT - 1) / CT;
-  const int cps = (nchunks_all + a.P - 1) / a.P;  // chunks per split
+  const int cps = (nchunks_all + a.P - 1) / a.P;   // chunks per split
   const int cbeg = sp * cps;
   const int nchunks = min(nchunks_all, cbeg + cps) - cbeg;
-  if (nchunks <= 0) return;                        // before any barrier
+  if (nchunks <= 0) return;                        // whole workgroup, before any barrier
 
-  // local chunk c is frame chunk cbeg + c
-  auto issue = [&](int c) {
-    const int c0 = (cbeg + c) * CT;
+  // This wave's rows of each head's frame matrix as left MFMA operands:
+  // rows of S_t, or with TRANS rows of S_t^T (columns of S_t), read from
+  // S_t staged in LDS with the transposing LDS read.
+  typedef typename std::conditional<BF, bf16x8, float>::type Frag;
+  Frag sf[HPW][KF];
 #pragma unroll
-    for (int j = 0; j < OPS; ++j) {
-      const int i = ft + NT * j;
-      const int o = i * 1024 + lane * 16;
-      const int row = o / (D * ES), col = o % (D * ES);
-      int tk = c0 + row;
-      if (tk >= N) tk = N - 1;
-      dma16(qsrc + (((row0 + tk) * a.H + h) * (long)D) * ES + col, &ring[c % STAGES][i * 1024]);
-    }
-  };
-
-  // Output rows of a chunk are staged in LDS and stored one iteration later
-  // as whole 16-byte pieces of token rows (each row of a head is D*ES
-  // contiguous bytes), instead of 4 values per lane scattered over 16 rows.
-  const int tid = threadIdx.x;
-  auto store_chunk = [&](int c) {
-    const E* src = obuf[c & 1];
-    constexpr int PRW = D * ES / 16;
-    for (int p = tid; p < CT * PRW; p += NTH) {
-      const int row = p / PRW, pc = p % PRW;
-      const int tk = (cbeg + c) * CT + row;
-      if (tk < N)
-        *reinterpret_cast<u32x4*>(static_cast<E*>(a.out) + ((row0 + tk) * a.H + h) * (long)D +
-                                  pc * (16 / ES)) =
-            *reinterpret_cast<const u32x4*>(src + row * D + pc * (16 / ES));
-    }
-  };
-
+  for (int hp = 0; hp < HPW; ++hp) {
+    const E* Sm = static_cast<const E*>(a.mat) + (((long)b * a.H + h0 + hp) * a.T + t) * (long)(D * D);
+    if constexpr (!TRANS) {
+      if constexpr (BF) {
+        const E* row = Sm + (ft * 16 + li) * D;
 #pragma unroll
-  for (int c = 0; c < STAGES - 1; ++c)
-    if (c < nchunks) issue(c);
-  for (int c = 0; c < nchunks; ++c) {
-    // Copies of chunk c+1 (if any) are younger than chunk c's; the output
-    // stores in between only make the wait more conservative.
-    if (c + 1 < nchunks)
-      wait_vm_barrier<OPS>();
-    else
-      wait_vm_barrier<0>();
-    if (c + STAGES - 1 < nchunks) issue(c + STAGES - 1);
-    if (c > 0) store_chunk(c - 1);      // staged by every wave before the barrier
-    const E* ts = reinterpret_cast<const E*>(ring[c % STAGES]);
-    E* ob = obuf[c & 1];
-#pragma unroll
-    for (int tt = 0; tt < CT / 16; ++tt) {
-      f32x4 acc = zero4();
-      const E* trow = ts + (tt * 16 + li) * D;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if constexpr (IO == IO_BF16) {
+        for (int kb = 0; kb < KF; ++kb) {
           const int k = kb * 32 + 8 * g;
-          const bf16x8 q = (k < D) ? load_bf16x8(reinterpret_cast<const uint16_t*>(trow) + k)
-                                   : zero_bf16x8();
-          acc = mfma_bf16(sf[kb], q, acc);
-        } else {
-          acc = mfma_f32(sf[kb], reinterpret_cast<const float*>(trow)[kb * 4 + g], acc);
+          sf[hp][kb] = (k < D) ? load_bf16x8(row + k) : zero_bf16x8();
         }
-      }
-      E* dst = ob + (tt * 16 + li) * D + ft * 16 + 4 * g;
-      if constexpr (IO == IO_BF16) {
-        u32x2 pk;
-        pk[0] = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-        pk[1] = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
-        *reinterpret_cast<u32x2*>(dst) = pk;
       } else {
-        *reinterpret_cast<f32x4*>(dst) = acc;
+#pragma unroll
+        for (int kb = 0; kb < KF; ++kb) sf[hp][kb] = Sm[(ft * 16 + li) * D + kb * 4 + g];
       }
+    } else if constexpr (BF) {
+      // S_t as [KR][D] rows in the output staging (free until the first
+      // chunk), rows past D zero
+      constexpr int KR = KF * 32;
+      static_assert(KR * D <= 2 * CT * RW, "staged matrix must fit the output buffers");
+      uint16_t* ms = reinterpret_cast<uint16_t*>(&obuf[0][0]);
+      constexpr int PRW = D / 8;
+      for (int p = tid; p < KR * PRW; p += NTH) {
+        const int row = p / PRW, pc = p % PRW;
+        *reinterpret_cast<u32x4*>(ms + row * D + pc * 8) =
+            row < D ? *reinterpret_cast<const u32x4*>(Sm + row * D + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+      block_sync();
+#pragma unroll
+      for (int kb = 0; kb < KF; ++kb) sf[hp][kb] = lds_col_frag_bf16(ms, D, kb * 32, ft * 16);
+      block_sync();
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KF; ++kb) sf[hp][kb] = Sm[(kb * 4 + g) * D + ft * 16 + li];
     }
   }
-  block_sync();
-  store_chunk(nchunks - 1);
+
+  const E* tok = static_cast<const E*>(a.tok);
+  E* out = static_cast<E*>(a.out);
+  struct Ring {
+    u32x4 v[PPT];
+  };
+  // Local chunk c is frame chunk cbeg + c; rows past the frame re-read its
+  // last row.  A row segment is the HPW adjacent heads' D features of one
+  // token (contiguous in memory).
+  auto issue = [&](Ring& R, int c) {
+    const int c0 = (cbeg + (c < nchunks ? c : nchunks - 1)) * CT;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      const int row = p / PR, pc = p % PR;
+      int tk = c0 + row;
+      if (tk >= N) tk = N - 1;
+      R.v[j] = *reinterpret_cast<const u32x4*>(tok + ((row0 + tk) * a.H + h0) * (long)D + pc * (16 / ES));
+    }
+  };
+  auto commit = [&](const Ring& R, int c) {
+    E* st = stage[c & 1];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+      *reinterpret_cast<u32x4*>(st + (tid + NTH * j) * (16 / ES)) = R.v[j];
+  };
+  auto compute = [&](int c) {
+    const E* ts = stage[c & 1];
+    E* ob = obuf[c & 1];
+#pragma unroll
+    for (int hp = 0; hp < HPW; ++hp)
+#pragma unroll
+      for (int tt = 0; tt < CT / 16; ++tt) {
+        f32x4 acc = zero4();
+        const E* trow = ts + (tt * 16 + li) * RW + hp * D;
+        if constexpr (BF) {
+#pragma unroll
+          for (int kb = 0; kb < KF; ++kb) {
+            // past D the read runs into the next head or row (or the next
+            // LDS buffer): zero it, the matching operand is zero too
+            bf16x8 q = load_bf16x8(reinterpret_cast<const uint16_t*>(trow) + kb * 32 + 8 * g);
+            if (KTAIL && kb == KF - 1 && kb * 32 + 8 * g >= D) q = zero_bf16x8();
+            acc = mfma_bf16(sf[hp][kb], q, acc);
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < KF; ++kb) acc = mfma_f32(sf[hp][kb], trow[kb * 4 + g], acc);
+        }
+        E* dst = ob + (tt * 16 + li) * RW + hp * D + ft * 16 + 4 * g;
+        if constexpr (BF) {
+          u32x2 pk;
+          pk[0] = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+          pk[1] = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+          *reinterpret_cast<u32x2*>(dst) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = acc;
+        }
+      }
+  };
+  auto store_full = [&](int c) {   // every token of chunk c exists
+    const E* src = obuf[c & 1];
+    const long r0 = row0 + (long)(cbeg + c) * CT;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      const int row = p / PR, pc = p % PR;
+      *reinterpret_cast<u32x4*>(out + ((r0 + row) * a.H + h0) * (long)D + pc * (16 / ES)) =
+          *reinterpret_cast<const u32x4*>(src + p * (16 / ES));
+    }
+  };
+  auto store_tail = [&](int c) {
+    const E* src = obuf[c & 1];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      const int row = p / PR, pc = p % PR;
+      const int tk = (cbeg + c) * CT + row;
+      if (tk < N)
+        *reinterpret_cast<u32x4*>(out + ((row0 + tk) * a.H + h0) * (long)D + pc * (16 / ES)) =
+            *reinterpret_cast<const u32x4*>(src + p * (16 / ES));
+    }
+  };
+
+  // the frame's chunks before its last are whole; the last may be partial
+  const int nfull = ((cbeg + nchunks) * CT <= N) ? nchunks : nchunks - 1;
+
+  Ring ring[PF];
+#pragma unroll
+  for (int r = 0; r < PF; ++r) issue(ring[r], r);
+  // chunk 0: nothing to store yet
+  commit(ring[0], 0);
+  lds_barrier();
+  issue(ring[0], PF);
+  compute(0);
+  // chunks 1 .. : straight-line trips of PF chunks while all are whole
+  int c0 = 1;
+  for (; c0 + PF <= nfull; c0 += PF) {
+#pragma unroll
+    for (int r = 0; r < PF; ++r) {
+      const int c = c0 + r;
+      Ring& R = ring[(1 + r) % PF];
+      commit(R, c);
+      lds_barrier();
+      issue(R, c + PF);        // clamped past the end
+      store_full(c - 1);
+      compute(c);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < PF; ++r) {
+    const int c = c0 + r;
+    if (c < nchunks) {
+      commit(ring[(1 + r) % PF], c);
+      lds_barrier();
+      store_full(c - 1);       // not the last chunk
+      compute(c);
+    }
+  }
+  lds_barrier();
+  if (nfull == nchunks)
+    store_full(nchunks - 1);
+  else
+    store_tail(nchunks - 1);
 }
 
 template <int IO, int NT, bool TRANS>
 static hipError_t launch_output_nt(const OutArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((output_kernel<IO, NT, TRANS>), dim3(a.B * a.Tc * a.H * a.P), dim3(64 * NT),
-                     0, s, a);
+  // adjacent head pairs when H is even: 2 D-wide row segments per token are
+  // contiguous and 64-byte aligned, where one head's rows are not
+  if (a.H % 2 == 0)
+    hipLaunchKernelGGL((output_kernel<IO, NT, TRANS, 2>), dim3(a.B * a.Tc * (a.H / 2) * a.P),
+                       dim3(64 * NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((output_kernel<IO, NT, TRANS, 1>), dim3(a.B * a.Tc * a.H * a.P),
+                       dim3(64 * NT), 0, s, a);
   return hipGetLastError();
 }
 

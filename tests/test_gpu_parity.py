@@ -74,10 +74,11 @@ def test_forward_head_dims_ragged(io, D):
     check_forward(inp, 100, io, with_state=True)
 
 
-@pytest.mark.parametrize("N", [1, 3, 16, 37, 64, 65])
-def test_forward_token_counts_fp32(N):
-    inp = gin.make_inputs(B=1, H=2, T=6, N=N, D=112, io="fp32", gamma="sigmoid", seed=2)
-    check_forward(inp, N, "fp32")
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("N", [1, 3, 16, 37, 64, 65, 200])
+def test_forward_token_counts(io, N):
+    inp = gin.make_inputs(B=1, H=2, T=6, N=N, D=112, io=io, gamma="sigmoid", seed=2)
+    check_forward(inp, N, io)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
