@@ -56,10 +56,12 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
 // gram_splits workgroups (fp32 partials, then a fixed-order sum), the
 // output kernel over out_splits workgroups.
 int gram_splits(const Shape& s) {
-  const int64_t frames = s.B * s.T * s.H;
-  if (frames >= 256) return 1;
-  const int64_t ct = s.io == IO_BF16 ? 64 : 32;
-  int64_t p = (256 + frames - 1) / frames;
+  // the Gram kernel takes adjacent head pairs when H is even
+  const int64_t hpw = s.H % 2 == 0 ? 2 : 1;
+  const int64_t wgs = s.B * s.T * (s.H / hpw);     // workgroups without splits
+  if (wgs >= 256) return 1;
+  const int64_t ct = s.io == IO_BF16 ? 32 : 16;     // the Gram kernel's token chunk
+  int64_t p = (256 + wgs - 1) / wgs;
   const int64_t nch = (s.N + ct - 1) / ct;
   if (p > nch) p = nch;
   if (p > 8) p = 8;

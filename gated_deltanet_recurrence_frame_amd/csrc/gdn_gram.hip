@@ -17,258 +17,295 @@
 // fp32 io): A_t row-major, U_t and dO_t Q^_t^T in the MFMA tile layout that
 // the scan consumes.
 //
-// Layout of the work: one workgroup (4 waves) per (b, t, h), XCD-aware
-// ordering so heads of one frame run on one XCD, two workgroups per CU.
-// Tokens stream through LDS in chunks of CT rows (natural [token][feature]
-// layout, double-buffered), the next chunk in flight in registers.
+// Layout of the work: one workgroup per (b, t) frame and pair of adjacent
+// heads (16 waves, one per CU) when H is even, else per single head (8
+// waves, two per CU); 8 waves share a head's row tiles.  XCD-aware ordering
+// so the heads of one frame run together on one XCD.  Tokens stream through
+// LDS in chunks of CT rows (natural [token][feature] layout, the head
+// group's row segments side by side, double-buffered); each thread loads
+// two 16-byte pieces of every chunk into a register ring PF chunks ahead,
+// with ordinary loads whose waits the compiler tracks, and commits them to
+// LDS one chunk at a time behind an LDS-only barrier, so the ring stays in
+// flight across it.  (Direct-to-LDS copies move the same bytes, but at
+// this number of waves per CU they ran about a tenth slower.)
 // Both MFMA operands need a feature's values over consecutive tokens; they
 // are read with the gfx950 transposing LDS read.  The weight w multiplies
 // the X operand in fp32 before rounding to bf16.  Tail tokens of the last
 // chunk re-read the frame's last row and get weight 0, so they add exactly 0.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-template <int IO, int NT, int NR, bool Y_IS_X0>
+constexpr int GRAM_WPH = 4;   // waves per head: 4 x 64 threads share a head's row tiles
+
+template <int IO, int NT, int NR, bool Y_IS_X0, int HPW>
 struct GramCfg {
+  static constexpr bool BF = (IO == IO_BF16);
   static constexpr int D = 16 * NT;
   static constexpr int ES = Io<IO>::bytes;
-  static constexpr int CT = (IO == IO_BF16) ? 64 : 32;     // tokens per chunk
+  static constexpr int WPH = GRAM_WPH;                      // waves per head
+  static constexpr int NW = WPH * HPW;                      // waves
+  static constexpr int NTH = 64 * NW;
+  static constexpr int RW = HPW * D;                        // elements of a token's row segment
+  static constexpr int CT = BF ? 32 : 16;                   // tokens per chunk
   static constexpr int NMAT = NR + (Y_IS_X0 ? 0 : 1);       // matrices staged
-  static constexpr int MAT_ELEMS = CT * D;
-  static constexpr int PR = D * ES / 16;                    // 16-byte pieces per row
-  static constexpr int PIECES = NMAT * CT * PR;
-  static constexpr int PPT = (PIECES + 255) / 256;          // pieces per thread
-  static constexpr int STAGE_BYTES = NMAT * MAT_ELEMS * ES + CT * 4;
-  static constexpr int RT = (NR * NT + 3) / 4;              // row tiles per wave
+  static constexpr int PR = RW * ES / 16;                   // 16-byte pieces per row segment
+  static constexpr int PIECES = NMAT * CT * PR;             // pieces per chunk
+  static constexpr int PPT = (PIECES + NTH - 1) / NTH;      // pieces per thread
+  static constexpr int NWT = CT * HPW;                      // weights per chunk
+  static constexpr int STAGE_ELEMS = NMAT * CT * RW;
+  static constexpr int PF = 2;                              // chunks in flight
+  static constexpr int RPM = (NT + WPH - 1) / WPH;          // row tiles per wave per matrix
+  static constexpr int RT = NR * RPM;                       // row tiles per wave
+  static_assert(NWT <= NTH, "one weight per thread at most");
 };
 
-template <int IO, int NT, int NR, bool Y_IS_X0>
-__global__ __launch_bounds__(256, 2) void gram_kernel(GramArgs a) {
-  typedef GramCfg<IO, NT, NR, Y_IS_X0> C;
+// Work item v (0 <= v < total) of a launch: frame (b, t), head group, token split.
+struct GramItem {
+  long row0;     // first token row of the frame
+  int b, tl, h0, sp;
+  int cbeg;      // first chunk of the split
+  int n;         // chunks of the split (may be 0)
+};
+
+template <int IO, int NT, int NR, bool Y_IS_X0, int HPW>
+__global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_kernel(GramArgs a) {
+  typedef GramCfg<IO, NT, NR, Y_IS_X0, HPW> C;
   typedef typename Io<IO>::elem E;
-  constexpr int D = C::D;
-  constexpr int SMEM = (2 * C::STAGE_BYTES > D * D * C::ES) ? 2 * C::STAGE_BYTES : D * D * C::ES;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  constexpr int D = C::D, CT = C::CT, ES = C::ES, RW = C::RW, PR = C::PR, NTH = C::NTH;
+  static_assert(C::PF == 2, "the ring below is written for two chunks in flight");
+  __shared__ __attribute__((aligned(16))) E stage[2][C::STAGE_ELEMS];
+  __shared__ float wstage[2][C::NWT];
 
-  const int total = a.B * a.Tc * a.H * a.P;
-  const int item = xcd_item(blockIdx.x, total);
-  const int sp = item % a.P;                       // token split
-  const int h = (item / a.P) % a.H;
-  const int tl = (item / (a.P * a.H)) % a.Tc;
-  const int t = a.t0 + tl;
-  const int b = item / (a.P * a.H * a.Tc);
+  const int HG = a.H / HPW;                        // head groups
+  const int total = a.B * a.Tc * HG * a.P;
   const int N = a.N;
-  const long L = (long)a.T * N;
-  const long row0 = (long)b * L + (long)t * N;   // first token row of the frame
+  const int nchunks_all = (N + CT - 1) / CT;
+  const int cps = (nchunks_all + a.P - 1) / a.P;  // chunks per split
+  const int nc2 = (cps + 1) & ~1;                  // ring steps per item (even)
+  auto decode = [&](int v) {
+    GramItem it;
+    const int item = xcd_item(v, total);
+    it.sp = item % a.P;
+    it.h0 = ((item / a.P) % HG) * HPW;
+    it.tl = (item / (a.P * HG)) % a.Tc;
+    it.b = item / (a.P * HG * a.Tc);
+    it.row0 = (long)it.b * a.T * N + (long)(a.t0 + it.tl) * N;
+    it.cbeg = it.sp * cps;
+    const int n = min(nchunks_all, it.cbeg + cps) - it.cbeg;
+    it.n = n > 0 ? n : 0;
+    return it;
+  };
 
-  const E* srcs[3] = {static_cast<const E*>(a.x0), static_cast<const E*>(NR == 2 ? a.x1 : a.y),
-                      static_cast<const E*>(a.y)};
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
+  const int hp = wave / C::WPH, wl = wave % C::WPH;   // this wave's head (in the group), slot
   const int g = lane >> 4, li = lane & 15;
-  const int nchunks_all = (N + C::CT - 1) / C::CT;
-  const int cps = (nchunks_all + a.P - 1) / a.P;  // chunks per split
-  const int cbeg = sp * cps;
-  const int nchunks = min(nchunks_all, cbeg + cps) - cbeg;   // may be <= 0
 
-  // Register staging of the next chunk.  A chunk's weights are masked
-  // here: 0 past the frame's last token (whose row is re-read), 1 when
-  // there are no weights.
-  struct Pre {
+  // staged matrix m: X_0, then X_1 (NR == 2) or Y (NR == 1, Y distinct)
+  const E* src0 = static_cast<const E*>(a.x0);
+  const E* src1 = static_cast<const E*>(NR == 2 ? a.x1 : a.y);
+  const bool has_w = a.w != nullptr;
+
+  // Register ring: chunk c of an item: pieces p = tid + NTH j of the stage
+  // ([m][CT][RW] row-major) and one weight ([token][head] of the group).
+  // Loads are clamped, never skipped (past the item's last chunk, past the
+  // frame's last row, past the stage's last piece), so the loop stays
+  // straight-line and the compiler's wait counts exact.
+  struct Ring {
     u32x4 v[C::PPT];
     float w;
   };
-  auto issue = [&](Pre& P, int c) {
-    const int c0 = (cbeg + c) * C::CT;
+  auto load = [&](Ring& R, const GramItem& it, int c) {
+    const int cl = it.n > 0 ? (c < it.n ? c : it.n - 1) : 0;
+    const int c0 = (it.n > 0 ? it.cbeg + cl : 0) * CT;
 #pragma unroll
     for (int j = 0; j < C::PPT; ++j) {
-      const int p = tid + 256 * j;
-      if (p < C::PIECES) {
-        const int m = p / (C::CT * C::PR);
-        const int r = p % (C::CT * C::PR);
-        const int row = r / C::PR, pc = r % C::PR;
-        int tok = c0 + row;
-        if (tok >= N) tok = N - 1;
-        P.v[j] = *reinterpret_cast<const u32x4*>(srcs[m] + ((row0 + tok) * a.H + h) * (long)D +
-                                                 pc * (16 / C::ES));
-      }
+      int p = tid + NTH * j;
+      p = p < C::PIECES ? p : C::PIECES - 1;
+      const int m = p / (CT * PR), q = p % (CT * PR);
+      int tk = c0 + q / PR;
+      tk = tk < N ? tk : N - 1;
+      const E* src = (m == 0 ? src0 : src1) + ((it.row0 + tk) * a.H + it.h0) * (long)D + (q % PR) * (16 / ES);
+      R.v[j] = *reinterpret_cast<const u32x4*>(src);
     }
-    if (tid < C::CT) {
-      const int tok = c0 + tid;
-      P.w = tok < N ? (a.w ? a.w[(row0 + tok) * a.H + h] : 1.0f) : 0.0f;
-    }
+    // the first NWT threads load the chunk's weights; the others load one
+    // shared address (a single cache line)
+    // (without weights: a dummy load of the first input, value unused)
+    const int wi = tid < C::NWT ? tid : 0;
+    int tk = c0 + wi / HPW;
+    tk = tk < N ? tk : N - 1;
+    const float* wp = has_w ? a.w + (it.row0 + tk) * a.H + it.h0 + wi % HPW
+                            : reinterpret_cast<const float*>(src0);
+    R.w = *wp;
   };
-  auto commit = [&](const Pre& P, int stage) {
-    char* base = smem + stage * C::STAGE_BYTES;
+  auto commit = [&](const Ring& R, int st, int nv) {   // nv: tokens of the chunk in the frame
 #pragma unroll
     for (int j = 0; j < C::PPT; ++j) {
-      const int p = tid + 256 * j;
-      if (p < C::PIECES) *reinterpret_cast<u32x4*>(reinterpret_cast<E*>(base) + p * (16 / C::ES)) = P.v[j];
+      const int p = tid + NTH * j;
+      if (C::PIECES % NTH == 0 || p < C::PIECES)
+        *reinterpret_cast<u32x4*>(&stage[st][p * (16 / ES)]) = R.v[j];
     }
-    if (tid < C::CT) reinterpret_cast<float*>(base + C::NMAT * C::MAT_ELEMS * C::ES)[tid] = P.w;
+    // tokens past the frame's end get weight 0 (their rows are re-read copies)
+    if (tid < C::NWT) wstage[st][tid] = tid / HPW < nv ? (has_w ? R.w : 1.0f) : 0.0f;
   };
 
   f32x4 acc[C::RT][NT];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int j = 0; j < C::RT; ++j)
+    for (int j = 0; j < C::RT; ++j)
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
+      for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
+  };
 
-  auto compute = [&](int stage) {
-    const char* base = smem + stage * C::STAGE_BYTES;
-    const E* xs = reinterpret_cast<const E*>(base);
-    const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * C::MAT_ELEMS;
-    const float* ws = reinterpret_cast<const float*>(base + C::NMAT * C::MAT_ELEMS * C::ES);
-    if constexpr (IO == IO_BF16) {
+  auto compute = [&](int st) {
+    // this wave's head: its D features at offset hp * D of each row segment
+    const E* xs = &stage[st][hp * D];
+    const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * CT * RW;
+    const float* ws = wstage[st];
+    if constexpr (C::BF) {
+      float wv[8];
 #pragma unroll
-      for (int kb = 0; kb < C::CT / 32; ++kb) {
-        const int k0 = kb * 32;
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(ws + k0 + 8 * g + 4);
-        bf16x8 bfr[NT];
+      for (int e = 0; e < 8; ++e) wv[e] = ws[(8 * g + e) * HPW + hp];
+      // the wave's weighted row fragments first, then one column fragment at
+      // a time (few fragments live next to the accumulators)
+      bf16x8 af[C::RT];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-          bfr[ct] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(ys), D, k0, ct * 16);
-        bf16x8 afr[C::RT];
+      for (int j = 0; j < C::RT; ++j) {
+        // row tile j of every wave: matrix m = j / RPM, tile ft = wl + WPH
+        // (j % RPM); every wave runs all RT (no branch in the loop), one past
+        // NT repeats tile NT - 1 and is dropped at the end
+        const int m = j / C::RPM;
+        const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
+        af[j] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(xs + m * CT * RW), RW, 0,
+                                  ft * 16);
 #pragma unroll
-        for (int j = 0; j < C::RT; ++j) {
-          const int rtg = wave + 4 * j;
-          if (rtg < NR * NT) {
-            const int m = rtg / NT, ft = rtg % NT;
-            afr[j] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(xs + m * C::MAT_ELEMS), D,
-                                       k0, ft * 16);
-          }
-        }
+        for (int e = 0; e < 8; ++e)
+          af[j][e] = static_cast<__bf16>(static_cast<float>(af[j][e]) * wv[e]);
+      }
 #pragma unroll
-        for (int j = 0; j < C::RT; ++j) {
-          const int rtg = wave + 4 * j;
-          if (rtg < NR * NT) {
-            bf16x8 af = afr[j];
+      for (int ct = 0; ct < NT; ++ct) {
+        const bf16x8 bfr = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(ys), RW, 0, ct * 16);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              af[e] = static_cast<__bf16>(static_cast<float>(af[e]) * w0[e]);
-              af[4 + e] = static_cast<__bf16>(static_cast<float>(af[4 + e]) * w1[e]);
-            }
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_bf16(af, bfr[ct], acc[j][ct]);
-          }
-        }
+        for (int j = 0; j < C::RT; ++j) acc[j][ct] = mfma_bf16(af[j], bfr, acc[j][ct]);
       }
     } else {
-#pragma unroll 2
-      for (int kb = 0; kb < C::CT / 4; ++kb) {
+      // not unrolled: hoisting every k step's operands would spill
+#pragma unroll 1
+      for (int kb = 0; kb < CT / 4; ++kb) {
         const int k = kb * 4 + g;
-        const float wv = ws[k];
+        const float wv = ws[k * HPW + hp];
         float bfr[NT];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * D + ct * 16 + li];
+        for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * RW + ct * 16 + li];
 #pragma unroll
         for (int j = 0; j < C::RT; ++j) {
-          const int rtg = wave + 4 * j;
-          if (rtg < NR * NT) {
-            const int m = rtg / NT, ft = rtg % NT;
-            const float af =
-                reinterpret_cast<const float*>(xs + m * C::MAT_ELEMS)[k * D + ft * 16 + li] * wv;
+          const int m = j / C::RPM;   // see the bf16 path
+          const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
+          const float af =
+              reinterpret_cast<const float*>(xs + m * CT * RW)[k * RW + ft * 16 + li] * wv;
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_f32(af, bfr[ct], acc[j][ct]);
-          }
+          for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_f32(af, bfr[ct], acc[j][ct]);
         }
       }
     }
   };
 
-  // Pipeline: chunk c is computed from LDS stage c % 2 while chunk c + 1 is
-  // in flight in registers; two workgroups per CU overlap each other's
-  // waits.
-  Pre P;
-  if (nchunks > 0) {
-    issue(P, 0);
-    commit(P, 0);
-  }
-  block_sync();
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) issue(P, c + 1);
-    compute(c & 1);
-    if (c + 1 < nchunks) commit(P, (c + 1) & 1);
-    block_sync();
-  }
-
-  // Epilogue: C[m][n] lives in lane (g, n) register r with m = 4g + r.
-  // Outputs are in the intermediate type (the io type).  The tiles layout
-  // is written straight from the accumulators (4 contiguous values per
-  // lane); a row-major output is staged through LDS (the chunk buffers are
-  // free after the last barrier) and stored in 16-byte pieces.
-  if (a.P > 1) {   // fp32 partial sums, tile layout
-    const long pbase = ((((long)sp * a.B + b) * a.H + h) * a.Tc + tl) * NR * (long)(D * D);
+  // Results of an item straight from the accumulators (C[m][n] in lane
+  // (g, n) register r with m = 4g + r): fp32 partial sums (token splits),
+  // the tiles layout (4 contiguous values per lane), or a row-major matrix,
+  // requested only for symmetric products (A_t): tile (I, J) read by
+  // columns is row pieces of tile (J, I), 4 contiguous values of one row
+  // per lane.
+  auto pack = [&](const f32x4& v, E* dst) {
+    if constexpr (C::BF) {
+      u32x2 pk;
+      pk[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+      pk[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+      *reinterpret_cast<u32x2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = v;
+    }
+  };
+  // Every wave stores all RT tiles unconditionally (the same number of
+  // stores on every path keeps the compiler's count of memory operations in
+  // flight exact, so the next item's loads stay in flight across them): a
+  // spare tile past NT is a bit-identical copy of tile NT - 1 (same inputs,
+  // same operations) and rewrites its bytes.
+  auto epilogue = [&](const GramItem& it) {
+    const int h = it.h0 + hp;
+    const int t = a.t0 + it.tl;
+    const bool partial = a.P > 1;
+    const long pbase =
+        ((((long)it.sp * a.B + it.b) * a.H + h) * a.Tc + it.tl) * NR * (long)(D * D);
+    const long obase = (((long)it.b * a.H + h) * a.T + t) * (long)(D * D);
 #pragma unroll
     for (int j = 0; j < C::RT; ++j) {
-      const int rtg = wave + 4 * j;
-      if (rtg < NR * NT) {
-        const int m = rtg / NT, ft = rtg % NT;
-        const float sc = (m == 0 ? a.scale0 : a.scale1);
-        float* out = a.part + pbase + m * (long)(D * D);
+      const int m = j / C::RPM;
+      const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
+      const float sc = (m == 0 ? a.scale0 : a.scale1);
+      if (partial) {
+        float* out = a.part + pbase + m * (long)(D * D) + (ft * NT * 64 + lane) * 4;
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-          *reinterpret_cast<f32x4*>(out + ((ft * NT + ct) * 64 + lane) * 4) = sc * acc[j][ct];
-      }
-    }
-    return;
-  }
-  const long obase = (((long)b * a.H + h) * a.T + t) * (long)(D * D);
-#pragma unroll
-  for (int j = 0; j < C::RT; ++j) {
-    const int rtg = wave + 4 * j;
-    if (rtg < NR * NT) {
-      const int m = rtg / NT, ft = rtg % NT;
-      if ((m == 0 ? a.layout0 : a.layout1) == LAYOUT_TILES) {
+        for (int ct = 0; ct < NT; ++ct) *reinterpret_cast<f32x4*>(out + ct * 256) = sc * acc[j][ct];
+      } else {
         E* out = static_cast<E*>(m == 0 ? a.out0 : a.out1) + obase;
-        const float sc = (m == 0 ? a.scale0 : a.scale1);
+        const bool tiles = (m == 0 ? a.layout0 : a.layout1) == LAYOUT_TILES;
+        // tiles: tile [ft][ct], this lane's slot; row-major (transposed
+        // tile): row 16 ct + i, columns 16 ft + 4g .. + 3.  Both are
+        // base + ct * stride.
+        E* base = tiles ? out + (ft * NT * 64 + lane) * 4 : out + li * D + ft * 16 + 4 * g;
+        const int stride = tiles ? 256 : 16 * D;
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          E* dst = out + ((ft * NT + ct) * 64 + lane) * 4;
-          const f32x4 v = sc * acc[j][ct];
-          if constexpr (IO == IO_BF16) {
-            u32x2 pk;
-            pk[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-            pk[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-            *reinterpret_cast<u32x2*>(dst) = pk;
-          } else {
-            *reinterpret_cast<f32x4*>(dst) = v;
-          }
+        for (int ct = 0; ct < NT; ++ct) pack(sc * acc[j][ct], base + ct * stride);
+      }
+    }
+  };
+
+  // Persistent: this workgroup walks items v = blockIdx.x + k gridDim.x
+  // (gridDim.x a multiple of 8 keeps them on this workgroup's XCD, and
+  // xcd_item gives each XCD a contiguous range: neighbouring heads of one
+  // frame run together).  Each item takes nc2 ring steps (its chunk count
+  // rounded up to even; steps past its last chunk only keep the ring in
+  // step).  Step c: commit ring slot c % 2 to stage c % 2 (free: its last
+  // readers, step c - 2, finished before the previous barrier), barrier,
+  // reload the slot with the chunk two steps ahead - the next item's first
+  // chunks at the end of an item, so they are in flight while the item's
+  // results are stored - and multiply.
+  const int G = gridDim.x;
+  int v = blockIdx.x;
+  if (v >= total) return;
+  GramItem cur = decode(v);
+  GramItem nxt = decode(v + G < total ? v + G : v);
+  Ring ring[2];
+  load(ring[0], cur, 0);
+  load(ring[1], cur, 1);
+  zero_acc();
+  for (;;) {
+    for (int c0 = 0; c0 < nc2; c0 += 2) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int c = c0 + r;
+        const bool real = c < cur.n;
+        if (real) {
+          commit(ring[r], r, N - (cur.cbeg + c) * CT);
+          lds_barrier();
         }
+        // two steps ahead: this item, or the next one's first chunks
+        const bool here = c + 2 < nc2;
+        load(ring[r], here ? cur : nxt, here ? c + 2 : c + 2 - nc2);
+        if (real) compute(r);
       }
     }
-  }
-#pragma unroll
-  for (int m = 0; m < NR; ++m) {
-    if ((m == 0 ? a.layout0 : a.layout1) != LAYOUT_ROWMAJOR) continue;
-    E* stage = reinterpret_cast<E*>(smem);
-    const float sc = (m == 0 ? a.scale0 : a.scale1);
-#pragma unroll
-    for (int j = 0; j < C::RT; ++j) {
-      const int rtg = wave + 4 * j;
-      if (rtg < NR * NT && rtg / NT == m) {
-        const int ft = rtg % NT;
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float v = sc * acc[j][ct][r];
-            E* dst = stage + (ft * 16 + 4 * g + r) * D + ct * 16 + li;
-            if constexpr (IO == IO_BF16)
-              *dst = f32_to_bf16_bits(v);
-            else
-              *dst = v;
-          }
-      }
-    }
-    block_sync();
-    u32x4* out = reinterpret_cast<u32x4*>(static_cast<E*>(m == 0 ? a.out0 : a.out1) + obase);
-    for (int idx = tid; idx < D * D * C::ES / 16; idx += 256)
-      out[idx] = reinterpret_cast<const u32x4*>(stage)[idx];
-    block_sync();
+    epilogue(cur);
+    zero_acc();
+    v += G;
+    if (v >= total) break;
+    cur = nxt;
+    nxt = decode(v + G < total ? v + G : v);
   }
 }
 
@@ -348,13 +385,40 @@ hipError_t launch_gram_reduce(const GramArgs& a, int io, int nt, int nr, hipStre
                        : launch_gram_reduce_io<IO_F32>(a, nt, nr, s);
 }
 
+// Resident workgroups of the Gram kernel: one per CU with head pairs, two
+// with single heads.
+static int gram_slots(int hpw) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return cus * (hpw == 2 ? 1 : 2);
+}
+
+template <int IO, int NT, int HPW>
+static void launch_gram_hpw(const GramArgs& a, int nr, hipStream_t s) {
+  // persistent: at most one workgroup per slot, a multiple of 8 so that a
+  // workgroup's items stay on its XCD
+  const int total = a.B * a.Tc * (a.H / HPW) * a.P;
+  int grid = gram_slots(HPW);
+  grid -= grid % 8;
+  if (total < grid) grid = total;
+  const dim3 block(64 * GRAM_WPH * HPW);
+  if (nr == 2)
+    hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW>), dim3(grid), block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW>), dim3(grid), block, 0, s, a);
+}
+
 template <int IO, int NT>
 static hipError_t launch_gram_nt(const GramArgs& a, int nr, hipStream_t s) {
-  const dim3 grid(a.B * a.Tc * a.H * a.P), block(256);
-  if (nr == 2)
-    hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true>), grid, block, 0, s, a);
+  // adjacent head pairs when H is even: each token's two row segments are
+  // one contiguous, 64-byte aligned piece of memory
+  if (a.H % 2 == 0)
+    launch_gram_hpw<IO, NT, 2>(a, nr, s);
   else
-    hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false>), grid, block, 0, s, a);
+    launch_gram_hpw<IO, NT, 1>(a, nr, s);
   return hipGetLastError();
 }
 
