@@ -56,16 +56,15 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
   constexpr int NAF = BF ? KB : D / 16;            // A pieces per lane per frame
   constexpr int PD = BF ? 8 : 3;                   // frames in flight
   constexpr int ZLD = BF ? D + 8 : D + 4;          // LDS row, a 16-byte multiple
-  constexpr int GW = 512;                          // gamma window held in LDS
   constexpr int NTH = 64 * NT;
   typedef typename std::conditional<BF, bf16x8, f32x4>::type AF;
   typedef typename std::conditional<BF, u32x2, f32x4>::type UF;
   struct Buf {
     AF af[NAF];
     UF u;
+    float gm;
   };
   __shared__ __attribute__((aligned(16))) E Zbuf[2][ZR * ZLD];
-  __shared__ float gam_lds[GW];
 
   const int NW = a.Tc;                                // frames of the whole walk
   const int CH = a.chunk > 0 ? a.chunk : NW;
@@ -101,15 +100,31 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     }
   }
 
+  // gamma_t rides in the ring with A_t and U_t.  Without gates (the fold
+  // of the composites, fp32) the load reads the first element of A instead
+  // (finite) and the state is scaled by gz = 0 before it meets it.  Nothing
+  // is applied to a loaded value until its frame is processed: an operation
+  // on it alone (a select) is free to be scheduled right after the load and
+  // would wait for it there.
+  const bool gated = a.gamma != nullptr;
+  const float* gbase = gated ? a.gamma + (long)b * T * a.H + h : static_cast<const float*>(a.A);
+  const int gstride = gated ? a.H : 0;
+  const float gz = gated ? 1.f : 0.f;
+
   auto frame_of = [&](int s) { return REVERSE ? a.t0 + NW - 1 - (sb + s) : a.t0 + sb + s; };
   auto load = [&](Buf& B, int s) {
     const int t = frame_of(s < NS ? s : NS - 1);
+    B.gm = gbase[(long)t * gstride];
     const E* At = Ab + t * DD + (ct * 16 + li) * D;
     if constexpr (BF) {
+      // unconditional loads: a branch around a load would cost the compiler
+      // its count of loads in flight and drain the ring every frame.  Lanes
+      // whose k runs past D re-read the row's last 8 elements (finite); the
+      // staged-row operand is zero there, so they add exact zeros.
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int k = kb * 32 + 8 * g;
-        B.af[kb] = (k < D) ? load_bf16x8(At + k) : zero_bf16x8();
+        B.af[kb] = load_bf16x8(At + (k < D ? k : D - 8));
       }
       B.u = *reinterpret_cast<const u32x2*>(Ub + t * DD + ((rb * NT + ct) * 64 + lane) * 4);
     } else {
@@ -141,19 +156,15 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
         *dst = v[r];
     }
   };
-  auto emit_rows = [&](int cur, int t) {   // the 16 staged rows -> S_t / G_t
-    constexpr int PRW = D * ES / 16, NP = 16 * PRW;
-    for (int p = tid; p < NP; p += NTH) {
-      const int row = p / PRW, pc = p % PRW;
-      *reinterpret_cast<u32x4*>(Eb + t * DD + (rb * 16 + row) * D + pc * (16 / ES)) =
-          *reinterpret_cast<const u32x4*>(&Zbuf[cur][row * ZLD + pc * (16 / ES)]);
-    }
-  };
-  auto load_gammas = [&](int s0) {
-    for (int i = tid; i < GW; i += NTH) {
-      const int s = s0 + i;
-      gam_lds[i] = (s < NS && a.gamma) ? a.gamma[((long)b * T + frame_of(s)) * a.H + h] : 0.f;
-    }
+  // the 16 staged rows -> S_t / G_t: 16 D elements, exactly 4 per thread,
+  // one unconditional store each (no branch around the store)
+  auto emit_rows = [&](int cur, int t) {
+    constexpr int PRW = D / 4;                     // 4-element pieces per row
+    static_assert(16 * PRW == NTH, "one piece per thread");
+    const int row = tid / PRW, pc = tid % PRW;
+    typedef typename std::conditional<BF, u32x2, u32x4>::type P4;
+    *reinterpret_cast<P4*>(Eb + t * DD + (rb * 16 + row) * D + pc * 4) =
+        *reinterpret_cast<const P4*>(&Zbuf[cur][row * ZLD + pc * 4]);
   };
   auto product = [&](const E* zrow, const Buf& B) {   // staged rows x A_t
     f32x4 p = zero4();
@@ -174,47 +185,58 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     return p;
   };
 
+  // One frame of the walk (step s, ring slot j = s % PD): add the input
+  // first in the reverse walk, stage the rows, barrier, store the staged rows
+  // (S_{t-1} / G_t), multiply by A_t, update, reload the slot PD frames
+  // ahead.
+  auto step = [&](Buf& R, int s, bool first) {
+    const int cur = s & 1;
+    const int t = frame_of(s);
+    const float gam = R.gm;   // multiplies gz * state, never alone
+    const f32x4 u = unpack_u(R);
+    if constexpr (REVERSE) z += u;
+    stage_tile(cur, 0, z);
+    if constexpr (COMP) stage_tile(cur, 16, zc);
+    block_sync();
+    if constexpr (!COMP) {
+      if constexpr (REVERSE)
+        emit_rows(cur, t);
+      else
+        // the staged rows are the state before frame t, stored at t - 1;
+        // at the walk's first frame (nothing to store unless asked) they go
+        // to frame t's own slot instead, which the same threads overwrite
+        // with S_t one step later - a select, not a branch around the store
+        emit_rows(cur, (!first || a.emit_entry) ? t - 1 : t);
+    }
+    // P = Z[rows] A_t
+    const f32x4 p = product(&Zbuf[cur][li * ZLD], R);
+    if constexpr (COMP) {
+      const f32x4 pc = product(&Zbuf[cur][(16 + li) * ZLD], R);
+      zc = gam * (gz * zc) - pc;
+    }
+    if constexpr (REVERSE)
+      z = gam * (gz * z) - p;
+    else
+      z = gam * (gz * z) - p + u;
+    load(R, s + PD);   // unconditional (clamped)
+  };
+
+  // The first frame runs on its own; then whole trips of PD frames run
+  // without any branch around a memory operation (the compiler then keeps
+  // exact counts of the loads in flight and waits only for the slot it
+  // needs); the last, partial trip follows.
   Buf ring[PD];
 #pragma unroll
   for (int j = 0; j < PD; ++j) load(ring[j], j);
-
-  for (int s0 = 0; s0 < NS; s0 += PD) {
+  step(ring[0], 0, true);
+  int s0 = 1;
+  for (; s0 + PD <= NS; s0 += PD) {
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int s = s0 + j;
-      if (s < NS) {
-        const int cur = s & 1;
-        const int t = frame_of(s);
-        if (s % GW == 0) {
-          block_sync();
-          load_gammas(s);
-        }
-        const f32x4 u = unpack_u(ring[j]);
-        if constexpr (REVERSE) z += u;
-        stage_tile(cur, 0, z);
-        if constexpr (COMP) stage_tile(cur, 16, zc);
-        block_sync();
-        const float gam = gam_lds[s % GW];
-        if constexpr (!COMP) {
-          if constexpr (REVERSE)
-            emit_rows(cur, t);
-          else if (s > 0 || a.emit_entry)
-            emit_rows(cur, t - 1);
-        }
-        // P = Z[rows] A_t
-        const f32x4 p = product(&Zbuf[cur][li * ZLD], ring[j]);
-        if constexpr (COMP) {
-          const f32x4 pc = product(&Zbuf[cur][(16 + li) * ZLD], ring[j]);
-          zc = gam * zc - pc;
-        }
-        if constexpr (REVERSE)
-          z = gam * z - p;
-        else
-          z = gam * z - p + u;
-        load(ring[j], s + PD);   // unconditional (clamped) keeps the compiler's wait counts exact
-      }
-    }
+    for (int j = 0; j < PD; ++j) step(ring[(1 + j) % PD], s0 + j, false);
   }
+#pragma unroll
+  for (int j = 0; j < PD; ++j)
+    if (s0 + j < NS) step(ring[(1 + j) % PD], s0 + j, false);
 
   if constexpr (COMP) {
     float* Hd = a.compH + ((long)bh * nck + w) * DD + ((rb * NT + ct) * 64 + lane) * 4;
