@@ -42,6 +42,12 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (s.B * s.L * s.H > (int64_t(1) << 40)) return GDN_ERR_BAD_SHAPE;
   s.io = p->io_dtype == GDN_BF16 ? IO_BF16 : IO_F32;
   s.es = p->io_dtype == GDN_BF16 ? 2 : 4;
+  // The Gram kernel addresses a frame's token rows with 32-bit byte offsets
+  // from 24-bit multiplies: one frame's rows under 2 GiB, N and a token's
+  // row (H D es bytes) under 2^24.
+  if (s.N >= (int64_t(1) << 24) || s.H * s.D * s.es >= (int64_t(1) << 24) ||
+      s.N * s.H * s.D * s.es >= (int64_t(1) << 31))
+    return GDN_ERR_BAD_SHAPE;
   s.s = p->key_scale != 0.f ? p->key_scale : (float)(1.0 / sqrt((double)s.D * (double)s.N));
   s.chunk = p->scan_chunk == 0 ? kDefaultChunk : p->scan_chunk;
   if (s.chunk > s.T) s.chunk = (int)s.T;

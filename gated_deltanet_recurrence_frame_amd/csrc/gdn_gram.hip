@@ -53,10 +53,23 @@ struct GramCfg {
   static constexpr int CT = BF ? 32 : 16;                   // tokens per chunk
   static constexpr int NMAT = NR + (Y_IS_X0 ? 0 : 1);       // matrices staged
   static constexpr int PR = RW * ES / 16;                   // 16-byte pieces per row segment
-  static constexpr int PIECES = NMAT * CT * PR;             // pieces per chunk
-  static constexpr int PPT = (PIECES + NTH - 1) / NTH;      // pieces per thread
+  static constexpr int MPC = CT * PR;                       // pieces per matrix per chunk
+  static constexpr int PPM = (MPC + NTH - 1) / NTH;         // of them per thread
+  static constexpr int PPT = NMAT * PPM;                    // pieces per thread
   static constexpr int NWT = CT * HPW;                      // weights per chunk
-  static constexpr int STAGE_ELEMS = NMAT * CT * RW;
+  // LDS row stride (elements).  A fragment read takes the same 16 bf16 (or
+  // 16 fp32) columns of 4 consecutive token rows per group of lanes; rows
+  // are padded so that those rows start on different banks of the 32
+  // (stride = 8 or 24 dwords mod 32 for bf16, 16 mod 32 for fp32).
+  static constexpr int pad_for(int rw) {
+    for (int p = 0; p < 64; p += (BF ? 8 : 4)) {
+      const int sd = (rw + p) * ES / 4;
+      if (BF ? (sd % 32 == 8 || sd % 32 == 24) : (sd % 32 == 16)) return p;
+    }
+    return 0;
+  }
+  static constexpr int LDR = RW + pad_for(RW);
+  static constexpr int STAGE_ELEMS = NMAT * CT * LDR;
   static constexpr int PF = 2;                              // chunks in flight
   static constexpr int RPM = (NT + WPH - 1) / WPH;          // row tiles per wave per matrix
   static constexpr int RT = NR * RPM;                       // row tiles per wave
@@ -71,12 +84,15 @@ struct GramItem {
   int n;         // chunks of the split (may be 0)
 };
 
-template <int IO, int NT, int NR, bool Y_IS_X0, int HPW>
+// SPLIT: the launch splits frames' tokens (a.P > 1) and stores fp32
+// partials; a compile-time choice, so that no branch joins stores of the two
+// kinds (the compiler would lose its count of the stores in flight).
+template <int IO, int NT, int NR, bool Y_IS_X0, int HPW, bool SPLIT>
 __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_kernel(GramArgs a) {
   typedef GramCfg<IO, NT, NR, Y_IS_X0, HPW> C;
   typedef typename Io<IO>::elem E;
-  constexpr int D = C::D, CT = C::CT, ES = C::ES, RW = C::RW, PR = C::PR, NTH = C::NTH;
-  static_assert(C::PF == 2, "the ring below is written for two chunks in flight");
+  constexpr int D = C::D, CT = C::CT, ES = C::ES, PR = C::PR, NTH = C::NTH;
+  constexpr int LDR = C::LDR;
   __shared__ __attribute__((aligned(16))) E stage[2][C::STAGE_ELEMS];
   __shared__ float wstage[2][C::NWT];
 
@@ -85,7 +101,8 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
   const int N = a.N;
   const int nchunks_all = (N + CT - 1) / CT;
   const int cps = (nchunks_all + a.P - 1) / a.P;  // chunks per split
-  const int nc2 = (cps + 1) & ~1;                  // ring steps per item (even)
+  constexpr int PF = C::PF;
+  const int ncp = (cps + PF - 1) / PF * PF;        // ring steps per item (whole trips)
   auto decode = [&](int v) {
     GramItem it;
     const int item = xcd_item(v, total);
@@ -110,27 +127,36 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
   const E* src1 = static_cast<const E*>(NR == 2 ? a.x1 : a.y);
   const bool has_w = a.w != nullptr;
 
-  // Register ring: chunk c of an item: pieces p = tid + NTH j of the stage
-  // ([m][CT][RW] row-major) and one weight ([token][head] of the group).
-  // Loads are clamped, never skipped (past the item's last chunk, past the
-  // frame's last row, past the stage's last piece), so the loop stays
-  // straight-line and the compiler's wait counts exact.
+  // Register ring: chunk c of an item: pieces q = tid + NTH j of each
+  // staged matrix ([CT][row segment], rows LDR apart in LDS) and one weight
+  // ([token][head] of the group).  Loads are clamped, never skipped (past
+  // the item's last chunk, past the frame's last row, past the matrix's
+  // last piece), so the loop stays straight-line and the compiler's wait
+  // counts exact.  Addresses are a uniform 64-bit frame base plus 32-bit
+  // per-lane offsets from 24-bit multiplies (the host keeps a frame's rows
+  // under 2 GiB and N, H D es under 2^24), a few full-rate instructions
+  // per piece.
   struct Ring {
     u32x4 v[C::PPT];
     float w;
   };
+  const unsigned rowb = (unsigned)(a.H * D * ES);     // bytes between tokens
   auto load = [&](Ring& R, const GramItem& it, int c) {
     const int cl = it.n > 0 ? (c < it.n ? c : it.n - 1) : 0;
     const int c0 = (it.n > 0 ? it.cbeg + cl : 0) * CT;
+    const long fb = (it.row0 * a.H + it.h0) * (long)(D * ES);
 #pragma unroll
-    for (int j = 0; j < C::PPT; ++j) {
-      int p = tid + NTH * j;
-      p = p < C::PIECES ? p : C::PIECES - 1;
-      const int m = p / (CT * PR), q = p % (CT * PR);
-      int tk = c0 + q / PR;
-      tk = tk < N ? tk : N - 1;
-      const E* src = (m == 0 ? src0 : src1) + ((it.row0 + tk) * a.H + it.h0) * (long)D + (q % PR) * (16 / ES);
-      R.v[j] = *reinterpret_cast<const u32x4*>(src);
+    for (int m = 0; m < C::NMAT; ++m) {
+      const char* base = reinterpret_cast<const char*>(m == 0 ? src0 : src1) + fb;
+#pragma unroll
+      for (int j = 0; j < C::PPM; ++j) {
+        int q = tid + NTH * j;
+        if (C::MPC % NTH != 0) q = q < C::MPC ? q : C::MPC - 1;
+        int tk = c0 + q / PR;
+        tk = tk < N ? tk : N - 1;
+        const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)((q % PR) * 16);
+        R.v[m * C::PPM + j] = *reinterpret_cast<const u32x4*>(base + off);
+      }
     }
     // the first NWT threads load the chunk's weights; the others load one
     // shared address (a single cache line)
@@ -138,17 +164,20 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
     const int wi = tid < C::NWT ? tid : 0;
     int tk = c0 + wi / HPW;
     tk = tk < N ? tk : N - 1;
-    const float* wp = has_w ? a.w + (it.row0 + tk) * a.H + it.h0 + wi % HPW
-                            : reinterpret_cast<const float*>(src0);
-    R.w = *wp;
+    const float* wb = has_w ? a.w + it.row0 * a.H + it.h0 : reinterpret_cast<const float*>(src0);
+    const unsigned woff = has_w ? __umul24((unsigned)tk, (unsigned)a.H) + (unsigned)(wi % HPW) : 0u;
+    R.w = wb[woff];
   };
   auto commit = [&](const Ring& R, int st, int nv) {   // nv: tokens of the chunk in the frame
 #pragma unroll
-    for (int j = 0; j < C::PPT; ++j) {
-      const int p = tid + NTH * j;
-      if (C::PIECES % NTH == 0 || p < C::PIECES)
-        *reinterpret_cast<u32x4*>(&stage[st][p * (16 / ES)]) = R.v[j];
-    }
+    for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < C::PPM; ++j) {
+        const int q = tid + NTH * j;
+        if (C::MPC % NTH == 0 || q < C::MPC)
+          *reinterpret_cast<u32x4*>(&stage[st][(m * CT + q / PR) * LDR + (q % PR) * (16 / ES)]) =
+              R.v[m * C::PPM + j];
+      }
     // tokens past the frame's end get weight 0 (their rows are re-read copies)
     if (tid < C::NWT) wstage[st][tid] = tid / HPW < nv ? (has_w ? R.w : 1.0f) : 0.0f;
   };
@@ -164,7 +193,7 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
   auto compute = [&](int st) {
     // this wave's head: its D features at offset hp * D of each row segment
     const E* xs = &stage[st][hp * D];
-    const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * CT * RW;
+    const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * CT * LDR;
     const float* ws = wstage[st];
     if constexpr (C::BF) {
       float wv[8];
@@ -180,7 +209,7 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
         // NT repeats tile NT - 1 and is dropped at the end
         const int m = j / C::RPM;
         const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
-        af[j] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(xs + m * CT * RW), RW, 0,
+        af[j] = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(xs + m * CT * LDR), LDR, 0,
                                   ft * 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -188,7 +217,7 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
       }
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        const bf16x8 bfr = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(ys), RW, 0, ct * 16);
+        const bf16x8 bfr = lds_col_frag_bf16(reinterpret_cast<const uint16_t*>(ys), LDR, 0, ct * 16);
 #pragma unroll
         for (int j = 0; j < C::RT; ++j) acc[j][ct] = mfma_bf16(af[j], bfr, acc[j][ct]);
       }
@@ -200,13 +229,13 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
         const float wv = ws[k * HPW + hp];
         float bfr[NT];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * RW + ct * 16 + li];
+        for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * LDR + ct * 16 + li];
 #pragma unroll
         for (int j = 0; j < C::RT; ++j) {
           const int m = j / C::RPM;   // see the bf16 path
           const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
           const float af =
-              reinterpret_cast<const float*>(xs + m * CT * RW)[k * RW + ft * 16 + li] * wv;
+              reinterpret_cast<const float*>(xs + m * CT * LDR)[k * LDR + ft * 16 + li] * wv;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_f32(af, bfr[ct], acc[j][ct]);
         }
@@ -235,30 +264,46 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
   // flight exact, so the next item's loads stay in flight across them): a
   // spare tile past NT is a bit-identical copy of tile NT - 1 (same inputs,
   // same operations) and rewrites its bytes.
-  auto epilogue = [&](const GramItem& it) {
+  // With `rehearse` the same stores all go to the lane's own first slot
+  // (ct = 0 of its first tile, which the item's real epilogue rewrites
+  // later): issued once after the prologue's loads, they give the first
+  // item the same memory operations in flight as every later item, whose
+  // loads were issued before the previous item's stores.  The compiler then
+  // waits at one count for both, not the smaller one for both.
+  auto epilogue = [&](const GramItem& it, bool rehearse) {
+    // an opaque zero: the compiler cannot merge the rehearsal's stores
+    int zero_s;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero_s));
+    const int jm = rehearse ? zero_s : 1;
     const int h = it.h0 + hp;
     const int t = a.t0 + it.tl;
-    const bool partial = a.P > 1;
     const long pbase =
         ((((long)it.sp * a.B + it.b) * a.H + h) * a.Tc + it.tl) * NR * (long)(D * D);
     const long obase = (((long)it.b * a.H + h) * a.T + t) * (long)(D * D);
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int j = 0; j < C::RT; ++j) {
-      const int m = j / C::RPM;
-      const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
-      const float sc = (m == 0 ? a.scale0 : a.scale1);
-      if (partial) {
+      for (int j = 0; j < C::RT; ++j) {
+        const int m = (j / C::RPM) * jm;
+        const int ft = min(wl + C::WPH * (j % C::RPM) * jm, NT - 1);
+        const float sc = (m == 0 ? a.scale0 : a.scale1);
         float* out = a.part + pbase + m * (long)(D * D) + (ft * NT * 64 + lane) * 4;
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) *reinterpret_cast<f32x4*>(out + ct * 256) = sc * acc[j][ct];
-      } else {
+        for (int ct = 0; ct < NT; ++ct)
+          *reinterpret_cast<f32x4*>(out + ct * 256 * jm) = sc * acc[j][ct];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::RT; ++j) {
+        const int m = (j / C::RPM) * jm;
+        const int ft = min(wl + C::WPH * (j % C::RPM) * jm, NT - 1);
+        const float sc = (m == 0 ? a.scale0 : a.scale1);
         E* out = static_cast<E*>(m == 0 ? a.out0 : a.out1) + obase;
         const bool tiles = (m == 0 ? a.layout0 : a.layout1) == LAYOUT_TILES;
         // tiles: tile [ft][ct], this lane's slot; row-major (transposed
         // tile): row 16 ct + i, columns 16 ft + 4g .. + 3.  Both are
         // base + ct * stride.
         E* base = tiles ? out + (ft * NT * 64 + lane) * 4 : out + li * D + ft * 16 + 4 * g;
-        const int stride = tiles ? 256 : 16 * D;
+        const int stride = (tiles ? 256 : 16 * D) * jm;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) pack(sc * acc[j][ct], base + ct * stride);
       }
@@ -268,39 +313,50 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
   // Persistent: this workgroup walks items v = blockIdx.x + k gridDim.x
   // (gridDim.x a multiple of 8 keeps them on this workgroup's XCD, and
   // xcd_item gives each XCD a contiguous range: neighbouring heads of one
-  // frame run together).  Each item takes nc2 ring steps (its chunk count
-  // rounded up to even; steps past its last chunk only keep the ring in
-  // step).  Step c: commit ring slot c % 2 to stage c % 2 (free: its last
-  // readers, step c - 2, finished before the previous barrier), barrier,
-  // reload the slot with the chunk two steps ahead - the next item's first
-  // chunks at the end of an item, so they are in flight while the item's
-  // results are stored - and multiply.
+  // frame run together).  Each item takes ncp ring steps, trips of PF (its
+  // chunk count rounded up; steps past its last chunk only keep the ring in
+  // step).  Step c: commit ring slot c % PF to the stage the previous real
+  // step did not use (free: its last readers finished before that step's
+  // barrier), barrier, reload the slot with the chunk PF steps ahead - the
+  // next item's first chunks at the end of an item, so they are in flight
+  // while the item's results are stored - and multiply.  The stage parity
+  // runs on across items: two consecutive real steps never share a stage
+  // whatever the chunk counts.
   const int G = gridDim.x;
   int v = blockIdx.x;
   if (v >= total) return;
   GramItem cur = decode(v);
   GramItem nxt = decode(v + G < total ? v + G : v);
-  Ring ring[2];
-  load(ring[0], cur, 0);
-  load(ring[1], cur, 1);
-  zero_acc();
-  for (;;) {
-    for (int c0 = 0; c0 < nc2; c0 += 2) {
+  Ring ring[PF];
+  int par = 0;
+  auto trip = [&](int c0) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int c = c0 + r;
-        const bool real = c < cur.n;
-        if (real) {
-          commit(ring[r], r, N - (cur.cbeg + c) * CT);
-          lds_barrier();
-        }
-        // two steps ahead: this item, or the next one's first chunks
-        const bool here = c + 2 < nc2;
-        load(ring[r], here ? cur : nxt, here ? c + 2 : c + 2 - nc2);
-        if (real) compute(r);
+    for (int r = 0; r < PF; ++r) {
+      const int c = c0 + r;
+      const bool real = c < cur.n;
+      if (real) {
+        commit(ring[r], par, N - (cur.cbeg + c) * CT);
+        lds_barrier();
+      }
+      // PF steps ahead: this item, or the next one's first chunks
+      const bool here = c + PF < ncp;
+      load(ring[r], here ? cur : nxt, here ? c + PF : c + PF - ncp);
+      if (real) {
+        compute(par);
+        par ^= 1;
       }
     }
-    epilogue(cur);
+  };
+#pragma unroll
+  for (int r = 0; r < PF; ++r) load(ring[r], cur, r);
+  zero_acc();
+  epilogue(cur, true);
+  for (;;) {
+    // the first trip runs after the stores on every path, the loop of the
+    // other trips after the first trip's waits
+    trip(0);
+    for (int c0 = PF; c0 < ncp; c0 += PF) trip(c0);
+    epilogue(cur, false);
     zero_acc();
     v += G;
     if (v >= total) break;
@@ -405,10 +461,17 @@ static void launch_gram_hpw(const GramArgs& a, int nr, hipStream_t s) {
   grid -= grid % 8;
   if (total < grid) grid = total;
   const dim3 block(64 * GRAM_WPH * HPW);
-  if (nr == 2)
-    hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW>), dim3(grid), block, 0, s, a);
-  else
-    hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW>), dim3(grid), block, 0, s, a);
+  if (a.P > 1) {
+    if (nr == 2)
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, true>), dim3(grid), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, true>), dim3(grid), block, 0, s, a);
+  } else {
+    if (nr == 2)
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, false>), dim3(grid), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, false>), dim3(grid), block, 0, s, a);
+  }
 }
 
 template <int IO, int NT>

@@ -40,7 +40,9 @@
  *     not overlap inputs, except where an entry point says so.
  *   - Reentrant: no mutable global state.
  *   - Supported shapes: Dk == Dv == D with D a multiple of 16 and <= 128;
- *     B, H, T, N >= 1; B*H*T and B*L*H must fit in int32.
+ *     B, H, T, N >= 1; B*H*T must fit in int32 and B*L*H be at most 2^40;
+ *     one frame's token rows (N*H*D io elements) under 2 GiB, and N and
+ *     H*D*(io element bytes) under 2^24.  Other sizes: GDN_ERR_BAD_SHAPE.
  */
 #ifndef LIBGDN_GDN_H
 #define LIBGDN_GDN_H

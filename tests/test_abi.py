@@ -78,6 +78,7 @@ def test_workspace_sizes(lib):
     ("Dk", 144, "GDN_ERR_UNSUPPORTED"), ("Dv", 64, "GDN_ERR_UNSUPPORTED"),
     ("io_dtype", 5, "GDN_ERR_BAD_DTYPE"), ("scan_chunk", -2, "GDN_ERR_BAD_SHAPE"),
     ("key_scale", float("nan"), "GDN_ERR_BAD_SHAPE"),
+    ("N", 1 << 24, "GDN_ERR_BAD_SHAPE"),       # token offsets use 24-bit multiplies
 ])
 def test_problem_validation(lib, field, value, status):
     p = gb.make_problem(1, 2, 4, 8, 32, "bf16")
@@ -110,3 +111,11 @@ def test_null_and_alignment_checks_before_any_launch(lib):
     assert gb.STATUS[code] == "GDN_ERR_BAD_SHAPE"                          # T != 1
     code = lib.gdn_backward(ctypes.byref(p), *([None] * 16), 0, None)
     assert gb.STATUS[code] == "GDN_ERR_NULL_POINTER"
+
+
+def test_frame_larger_than_2gib_is_rejected(lib):
+    # one frame's token rows must stay under 2 GiB (32-bit byte offsets)
+    p = gb.make_problem(1, 2000, 1, 300000, 128, "fp32")
+    assert gb.STATUS[_ws(p, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_BAD_SHAPE"
+    p = gb.make_problem(1, 2000, 1, 2000, 128, "fp32")
+    assert gb.STATUS[_ws(p, gb.GDN_OP_FORWARD)[0]] == "GDN_OK"

@@ -81,6 +81,16 @@ def test_forward_token_counts(io, N):
     check_forward(inp, N, io)
 
 
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_forward_items_with_odd_chunk_counts(io):
+    # 600 (frame, head pair) items over at most 256 persistent Gram
+    # workgroups, each item an odd number of token chunks: consecutive items
+    # of one workgroup must alternate their LDS stages across the item
+    # boundary as well
+    inp = gin.make_inputs(B=1, H=20, T=60, N=65, D=112, io=io, gamma="sigmoid", seed=4)
+    check_forward(inp, 65, io)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_forward_short_clip_bf16(seed):
     inp = gin.make_config("short", seed=seed)
