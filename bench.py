@@ -7,8 +7,8 @@ bf16 Q/K/V/O, fp32 gates and state), inputs resident in HBM.  Prints one JSON
 line: tokens/s, the roofline of the dominant kernel (phase times from HIP
 events recorded by the library between its kernels, on the stream they run
 on), and the float64 CPU oracle timed on a bounded sample of the same
-workload.  Extras: forward + backward at the same shape, and 121 streaming
-gdn_step calls.
+workload.  Extras: forward + backward at the same shape, 121 streaming
+gdn_step calls, and chunk-causal streaming by windows of latent frames.
 """
 
 import argparse
@@ -184,6 +184,8 @@ def main():
         extra["train"] = bench_train(gb, d, B, H, D, T, N, max(3, args.steps // 4))
         print("[bench] streaming steps", file=sys.stderr, flush=True)
         extra["stream"] = bench_stream(gb, d, B, H, D, T, N, ev)
+        print("[bench] streaming windows", file=sys.stderr, flush=True)
+        extra["windows"] = [bench_windows(gb, d, B, H, D, T, N, k) for k in (2, 8, 15)]
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -259,6 +261,42 @@ def bench_stream(gb, d, B, H, D, T, N, ev):
             "calls": T, "per_frame_ms_median": round(lat[T // 2], 4),
             "per_frame_ms_p90": round(lat[int(T * 0.9)], 4),
             "tokens_per_s": round(B * T * N / wall, 1)}
+
+
+def bench_windows(gb, d, B, H, D, T, N, k):
+    """Chunk-causal streaming: the first latent frame alone, then windows of
+    k latent frames (8k raw frames each), every window one gdn_forward that
+    carries the state in place."""
+    import torch
+    dev = d["q"].device
+    bounds = [(0, 1)] + [(t, min(t + k, T)) for t in range(1, T, k)]
+    plans = {}
+    for t0, t1 in bounds:
+        if t1 - t0 not in plans:
+            plans[t1 - t0] = gb.ForwardPlan(B, H, t1 - t0, N, D, "bf16", dev)
+    state = torch.zeros((B, H, D, D), dtype=torch.float32, device=dev)
+    wins = [(plans[t1 - t0], d["q"][:, t0 * N:t1 * N], d["k"][:, t0 * N:t1 * N],
+             d["v"][:, t0 * N:t1 * N], d["gamma"][:, t0:t1], d["beta"][:, t0 * N:t1 * N])
+            for t0, t1 in bounds]
+    for w in wins[:3]:
+        w[0](*w[1:], state_in=state, state_out=state)
+    state.zero_()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(wins) + 1)]
+    evs[0].record(stream)
+    t0 = time.perf_counter()
+    for i, w in enumerate(wins):
+        w[0](*w[1:], state_in=state, state_out=state)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(1, len(wins)))
+    n = len(lat)
+    return {"workload": "frame 0, then windows of %d latent frames (gdn_forward, state carried)"
+                        % k,
+            "calls": len(wins), "per_window_ms_median": round(lat[n // 2], 4),
+            "per_window_ms_max": round(lat[-1], 4), "tokens_per_s": round(B * T * N / wall, 1)}
 
 
 if __name__ == "__main__":

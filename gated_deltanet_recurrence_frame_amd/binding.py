@@ -173,18 +173,25 @@ class ForwardPlan:
                       if saved else None)
         self.device = device
 
-    def __call__(self, q, k, v, gamma, beta, state_in=None, events=None):
+    def __call__(self, q, k, v, gamma, beta, state_in=None, events=None, state_out=None):
         """events: None, or 4 raw hipEvent_t handles (ints) recorded around
-        the Gram/write, scan and output kernels (gdn_forward_events)."""
+        the Gram/write, scan and output kernels (gdn_forward_events).
+        state_out: None (the plan's own buffer), or a [B, H, D, D] fp32
+        tensor, which may be state_in itself (the state carried in place
+        from one call to the next)."""
+        so = self.state_out if state_out is None else state_out
+        if state_out is not None:
+            _need(state_out, "state_out", torch.float32, tuple(self.state_out.shape),
+                  self.device)
         args = (ctypes.byref(self.prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
-                _p(state_in), _p(self.o), _p(self.state_out), _p(self.saved), _p(self.ws),
+                _p(state_in), _p(self.o), _p(so), _p(self.saved), _p(self.ws),
                 self.ws.numel(), _stream(self.device))
         if events is None:
             _check(lib().gdn_forward(*args), "gdn_forward")
         else:
             ev = (_VP * 4)(*[_VP(int(e)) for e in events])
             _check(lib().gdn_forward_events(*args, ev), "gdn_forward_events")
-        return self.o, self.state_out
+        return self.o, so
 
 
 def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, scan_chunk=0,

@@ -225,6 +225,38 @@ def test_step_chain_equals_forward(io):
     assert rel_l2(f64(state.cpu()), rs) <= TOL[io]
 
 
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_chunk_causal_windows_equal_one_call(io):
+    # streaming by windows of frames: the first latent frame alone, then
+    # windows of 8, each a gdn_forward that carries the state in place
+    B, H, T, N, D = 1, 3, 17, 130, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=21,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    o_full, s_full = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                                state_in=d["state"])
+    state = d["state"].clone()
+    outs = []
+    for t0, t1 in [(0, 1), (1, 9), (9, 17)]:
+        sl = slice(t0 * N, t1 * N)
+        plan = gb.ForwardPlan(B, H, t1 - t0, N, D, io, torch.device(DEV))
+        o, st = plan(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                     d["v"][:, sl].contiguous(), d["gamma"][:, t0:t1].contiguous(),
+                     d["beta"][:, sl].contiguous(), state_in=state, state_out=state)
+        assert st.data_ptr() == state.data_ptr()
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    o_win = torch.cat(outs, dim=1)
+    # same kernels over fewer frames per launch: equal up to summation order
+    tol_same = 1e-6 if io == "fp32" else 2e-3
+    assert rel_l2(f64(o_win.cpu()), f64(o_full.cpu())) <= tol_same
+    assert rel_l2(f64(state.cpu()), f64(s_full.cpu())) <= tol_same
+    ro, rs = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                            f64(inp["beta"]), N, state_in=f64(inp["state"]))
+    assert rel_l2(f64(o_win.cpu()), ro) <= TOL[io]
+    assert rel_l2(f64(state.cpu()), rs) <= TOL[io]
+
+
 # -------------------------------------------------------------- backward
 def check_backward(inp, N, io, with_state=True, with_dstate=True, use_saved=False,
                    key_scale=0.0, scan_chunk=0):
