@@ -11,4 +11,5 @@ from .gdn_oracle import (  # noqa: F401
     forward,
     frame_terms,
     step,
+    tokenspace_forward,
 )

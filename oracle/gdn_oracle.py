@@ -59,6 +59,7 @@ __all__ = [
     "step",
     "backward",
     "composite_forward",
+    "tokenspace_forward",
 ]
 
 
@@ -298,4 +299,84 @@ def composite_forward(q, k, v, gamma, beta, n, chunk, state_in=None,
                 for t in range(t0, t1):
                     St = St @ Ms[t] + Us[t]
                     o[b, t * n:(t + 1) * n, h, :] = (St @ _frame_cols(q, b, t, h, n)).T
+    return o, state_out
+
+
+def tokenspace_forward(q, k, v, gamma, beta, n, frames_per_chunk, state_in=None,
+                       key_scale=0.0):
+    """Forward in token space, chunk by chunk, with the per-chunk triangular
+    system of the delta rule.
+
+    This is the same recurrence as ``forward`` (summary page, 前置知识 "Gated
+    DeltaNet" and 方法步骤详情 module 2) written over the tokens of a chunk of
+    F = ``frames_per_chunk`` consecutive frames instead of over D x D
+    matrices; 技术新颖性 point 1 describes frame-wise GDN as token-wise GDN
+    generalised to whole frames, and this is the token-wise algorithm with
+    frames as its steps.  It needs no D x D product per frame, which is what
+    makes it cheaper when a frame has fewer tokens than D.
+
+    Derivation (column form; E_f = state entering frame f of the chunk,
+    E_0 = the chunk's incoming state): each frame's update
+        S = S (gamma_f I - K^_f beta_f K^_f^T) + V_f beta_f K^_f^T
+          = gamma_f S + W_f K^_f^T,   W_f = (V_f - S K^_f) beta_f,
+    so with P(a, b) = gamma_a ... gamma_b (1 when a > b), for token t of
+    frame f(t):
+        E_f     = P(0, f-1) E_0 + sum_{u: f(u) < f} P(f(u)+1, f-1) w_u k^_u^T
+        w_t     = (v_t - E_{f(t)} k^_t) beta_t
+    i.e. W (I + L) = R with
+        R[:, t] = (v_t - P(0, f(t)-1) E_0 k^_t) beta_t
+        L[u, t] = P(f(u)+1, f(t)-1) (k^_u . k^_t) beta_t   for f(u) < f(t), else 0
+    (strictly upper triangular in token order: tokens of one frame do not
+    see each other).  Then
+        o_t     = P(0, f(t)) E_0 q_t + sum_{u: f(u) <= f(t)} P(f(u)+1, f(t)) w_u (k^_u . q_t)
+        E_F     = P(0, F-1) E_0 + sum_u P(f(u)+1, F-1) w_u k^_u^T.
+    The triangular solve is a library routine (numpy's solve on the unit
+    triangular matrix).
+
+    Returns (o, state_out) like ``forward``.
+    """
+    B, L, H, Dk, Dv, T = _shapes(q, k, v, gamma, beta, n)
+    F = int(frames_per_chunk)
+    if F < 1:
+        raise ValueError("frames_per_chunk must be >= 1")
+    s = _scale(key_scale, Dk, n)
+    o = np.zeros((B, L, H, Dv))
+    state_out = np.zeros((B, H, Dv, Dk))
+    for b in range(B):
+        for h in range(H):
+            E0 = (np.zeros((Dv, Dk)) if state_in is None
+                  else np.asarray(state_in[b, h], dtype=np.float64).copy())
+            for t0 in range(0, T, F):
+                t1 = min(t0 + F, T)
+                nf = t1 - t0
+                C = nf * n
+                sl = slice(t0 * n, t1 * n)
+                Kc = s * np.asarray(k[b, sl, h, :], dtype=np.float64).T     # Dk x C
+                Qc = np.asarray(q[b, sl, h, :], dtype=np.float64).T         # Dk x C
+                Vc = np.asarray(v[b, sl, h, :], dtype=np.float64).T         # Dv x C
+                bc = np.asarray(beta[b, sl, h], dtype=np.float64)           # C
+                g = np.asarray(gamma[b, t0:t1, h], dtype=np.float64)        # nf
+                fr = np.repeat(np.arange(nf), n)                            # frame of each token
+
+                def P(a, c):
+                    return float(np.prod(g[a:c + 1])) if a <= c else 1.0
+
+                Pd = np.array([[P(a + 1, c - 1) for c in range(nf)] for a in range(nf)])
+                Po = np.array([[P(a + 1, c) for c in range(nf)] for a in range(nf)])
+                before = np.array([P(0, f - 1) for f in range(nf)])         # P(0, f-1)
+                upto = np.array([P(0, f) for f in range(nf)])               # P(0, f)
+                tail = np.array([P(f + 1, nf - 1) for f in range(nf)])      # P(f+1, F-1)
+                KK = Kc.T @ Kc                                              # k^_u . k^_t
+                KQ = Kc.T @ Qc                                              # k^_u . q_t
+                earlier = fr[:, None] < fr[None, :]
+                Lm = np.where(earlier, Pd[fr][:, fr] * KK, 0.0) * bc[None, :]
+                R = (Vc - (E0 @ Kc) * before[fr][None, :]) * bc[None, :]
+                # W (I + L) = R  <=>  (I + L)^T W^T = R^T
+                W = np.linalg.solve((np.eye(C) + Lm).T, R.T).T              # Dv x C
+                seen = fr[:, None] <= fr[None, :]
+                Om = np.where(seen, Po[fr][:, fr] * KQ, 0.0)
+                Oc = (E0 @ Qc) * upto[fr][None, :] + W @ Om
+                o[b, sl, h, :] = Oc.T
+                E0 = P(0, nf - 1) * E0 + (W * tail[fr][None, :]) @ Kc.T
+            state_out[b, h] = E0
     return o, state_out

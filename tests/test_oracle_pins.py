@@ -436,3 +436,79 @@ def test_pins_catch_planted_mistakes(kind):
     assert np.max(np.abs(mut - ref)) > 1e-6
     ok = _mutant_forward("none", q, k, v, g, beta, 3, s0, s)
     assert np.max(np.abs(ok - ref)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# P13: the token-space form (chunks of frames, the delta rule's triangular
+# system per chunk) reproduces the unrolled products, for token-wise GDN
+# (N = 1) and for short frames, any chunk length, ragged last chunks,
+# gates far from 1.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("N,T,F", [(1, 9, 4), (1, 8, 8), (1, 5, 1), (2, 7, 3), (3, 6, 2),
+                                   (4, 5, 5)])
+def test_p13_tokenspace_equals_unrolled_products(N, T, F):
+    q, k, v, g, beta, s0 = _rand_problem(1, 2, T, N, 5, seed=30 + N * 10 + F,
+                                         gamma_lo=1e-3, gamma_hi=1.0)
+    s = 0.41
+    ref = _brute_force(q, k, v, g, beta, N, s0, s)
+    o, st = oracle.tokenspace_forward(q, k, v, g, beta, N, F, state_in=s0, key_scale=s)
+    assert np.max(np.abs(o - ref)) <= 1e-11 * max(1.0, np.max(np.abs(ref)))
+    _, st_ref = oracle.forward(q, k, v, g, beta, N, state_in=s0, key_scale=s)
+    assert np.max(np.abs(st - st_ref)) <= 1e-11 * max(1.0, np.max(np.abs(st_ref)))
+
+
+def _tokenspace_mutant(kind, q, k, v, g, beta, n, F, s0, s):
+    """A second, deliberately plain token-space implementation in which one
+    mistake can be planted; every mistake must break agreement with P1's
+    brute force."""
+    B, L, H, D = k.shape
+    T = L // n
+    o = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            E = s0[b, h].copy()
+            for t0 in range(0, T, F):
+                t1 = min(t0 + F, T)
+                toks = list(range(t0 * n, t1 * n))
+                fr = [l // n - t0 for l in toks]
+                gg = g[b, t0:t1, h]
+
+                def P(a, c):
+                    return float(np.prod(gg[a:c + 1])) if a <= c else 1.0
+
+                kh = [s * k[b, l, h] for l in toks]
+                w = []
+                for i, l in enumerate(toks):
+                    f = fr[i]
+                    r = v[b, l, h] - P(0, f - 1) * (E @ kh[i])
+                    for j in range(i):
+                        vis = fr[j] <= f if kind == "same_frame_visible" else fr[j] < f
+                        if vis:
+                            dec = 1.0 if kind == "no_decay" else P(fr[j] + 1, f - 1)
+                            r = r - dec * w[j] * (kh[j] @ kh[i])
+                    bt = beta[b, toks[i - 1] if (kind == "beta_shifted" and i) else l, h]
+                    w.append(r * bt)
+                for i, l in enumerate(toks):
+                    f = fr[i]
+                    out = P(0, f) * (E @ q[b, l, h])
+                    for j in range(len(toks)):
+                        vis = fr[j] < f if kind == "output_before_update" else fr[j] <= f
+                        if vis:
+                            out = out + P(fr[j] + 1, f) * w[j] * (kh[j] @ q[b, l, h])
+                    o[b, l, h] = out
+                nf = t1 - t0
+                E = P(0, nf - 1) * E + sum(P(fr[j] + 1, nf - 1) * np.outer(w[j], kh[j])
+                                           for j in range(len(toks)))
+    return o
+
+
+@pytest.mark.parametrize("kind", ["same_frame_visible", "no_decay", "beta_shifted",
+                                  "output_before_update"])
+def test_p13_pins_catch_planted_mistakes(kind):
+    q, k, v, g, beta, s0 = _rand_problem(1, 1, 6, 2, 4, seed=33, gamma_lo=0.3)
+    s = 0.45
+    ref = _brute_force(q, k, v, g, beta, 2, s0, s)
+    ok = _tokenspace_mutant("none", q, k, v, g, beta, 2, 3, s0, s)
+    assert np.max(np.abs(ok - ref)) < 1e-11
+    mut = _tokenspace_mutant(kind, q, k, v, g, beta, 2, 3, s0, s)
+    assert np.max(np.abs(mut - ref)) > 1e-6
