@@ -25,11 +25,14 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
           7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIASING"}
 
 
+ABI_VERSION = 2   # GDN_ABI_VERSION of include/gdn.h that GdnProblem mirrors
+
+
 class GdnProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("key_scale", ctypes.c_float),
-                ("scan_chunk", ctypes.c_int32)]
+                ("scan_chunk", ctypes.c_int32), ("algorithm", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -69,6 +72,9 @@ def lib():
     L.gdn_step.argtypes = [P] + [_VP] * 8 + [ctypes.c_size_t, _VP]
     L.gdn_backward.restype = ctypes.c_int
     L.gdn_backward.argtypes = [P] + [_VP] * 16 + [ctypes.c_size_t, _VP]
+    if L.gdn_abi_version() != ABI_VERSION:
+        raise RuntimeError("libgdn.so has ABI version %d, this binding expects %d; rebuild it"
+                           % (L.gdn_abi_version(), ABI_VERSION))
     _lib = L
     return L
 
@@ -101,10 +107,13 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def make_problem(B, H, T, N, D, io="bf16", key_scale=0.0, scan_chunk=0):
+ALGORITHMS = {"auto": 0, "frame": 1, "token": 2}
+
+
+def make_problem(B, H, T, N, D, io="bf16", key_scale=0.0, scan_chunk=0, algorithm="auto"):
     return GdnProblem(int(B), int(H), int(T), int(N), int(D), int(D),
                       GDN_BF16 if io == "bf16" else GDN_FP32, float(key_scale),
-                      int(scan_chunk))
+                      int(scan_chunk), ALGORITHMS[algorithm])
 
 
 def workspace_size(prob, op):
@@ -162,8 +171,9 @@ class ForwardPlan:
     one problem shape (used by the benchmark to keep allocation out of the
     timed region)."""
 
-    def __init__(self, B, H, T, N, D, io, device, key_scale=0.0, scan_chunk=0, saved=False):
-        self.prob = make_problem(B, H, T, N, D, io, key_scale, scan_chunk)
+    def __init__(self, B, H, T, N, D, io, device, key_scale=0.0, scan_chunk=0, saved=False,
+                 algorithm="auto"):
+        self.prob = make_problem(B, H, T, N, D, io, key_scale, scan_chunk, algorithm)
         dt = torch.bfloat16 if io == "bf16" else torch.float32
         self.o = torch.empty((B, T * N, H, D), dtype=dt, device=device)
         self.state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=device)
@@ -195,12 +205,13 @@ class ForwardPlan:
 
 
 def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, scan_chunk=0,
-            return_saved=False):
+            return_saved=False, algorithm="auto"):
     """o, state_out (and the saved A_t / S_t buffer) of gdn_forward."""
     B, L, H, D, T, dev = _shapes(q, k, v, gamma, beta, n)
     if state_in is not None:
         _need(state_in, "state_in", torch.float32, (B, H, D, D), dev)
-    plan = ForwardPlan(B, H, T, n, D, _io_of(q), dev, key_scale, scan_chunk, return_saved)
+    plan = ForwardPlan(B, H, T, n, D, _io_of(q), dev, key_scale, scan_chunk, return_saved,
+                       algorithm)
     o, st = plan(q, k, v, gamma, beta, state_in)
     if return_saved:
         return o, st, plan.saved

@@ -14,6 +14,9 @@ using namespace gdn;
 namespace {
 
 constexpr int kDefaultChunk = 1;   // sequential scan unless asked otherwise
+// GDN_ALGO_AUTO takes the token form for frames of at most this many tokens
+// (0: never; the frame form is the default everywhere)
+constexpr int kTokenAutoMaxN = 0;
 
 struct Shape {
   int64_t B, H, T, N, D, L;
@@ -24,6 +27,7 @@ struct Shape {
   int64_t mat;       // bytes of one [B, H, T] x D x D buffer of the intermediate
                      // type (bf16 for bf16 io, fp32 for fp32 io)
   int64_t parts;     // composite chunks per sequence
+  bool token;        // forward in token form (chunks of frames, no D x D per frame)
 };
 
 gdn_status check_problem(const gdn_problem* p, Shape* sh) {
@@ -34,6 +38,7 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (p->scan_chunk < 0) return GDN_ERR_BAD_SHAPE;
   if (!isfinite(p->key_scale)) return GDN_ERR_BAD_SHAPE;
   if (p->Dk != p->Dv || p->Dk % 16 != 0 || p->Dk > 128) return GDN_ERR_UNSUPPORTED;
+  if (p->algorithm < GDN_ALGO_AUTO || p->algorithm > GDN_ALGO_TOKEN) return GDN_ERR_UNSUPPORTED;
   Shape s;
   s.B = p->B; s.H = p->H; s.T = p->T; s.N = p->N; s.D = p->Dk;
   s.L = s.T * s.N;
@@ -53,6 +58,10 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (s.chunk > s.T) s.chunk = (int)s.T;
   s.mat = s.B * s.H * s.T * s.D * s.D * s.es;
   s.parts = s.chunk <= 1 ? 1 : (s.T + s.chunk - 1) / s.chunk;   // 1: sequential
+  const int64_t tok_max = s.io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
+  if (p->algorithm == GDN_ALGO_TOKEN && s.N > tok_max) return GDN_ERR_UNSUPPORTED;
+  s.token = p->algorithm == GDN_ALGO_TOKEN ||
+            (p->algorithm == GDN_ALGO_AUTO && s.N <= kTokenAutoMaxN);
   *sh = s;
   return GDN_OK;
 }
@@ -101,7 +110,7 @@ int64_t scratch_bytes(const Shape& s) {
   return a > b ? a : b;
 }
 
-int64_t forward_ws(const Shape& s) { return 3 * s.mat + scratch_bytes(s); }
+int64_t forward_ws(const Shape& s) { return s.token ? 0 : 3 * s.mat + scratch_bytes(s); }
 int64_t backward_ws(const Shape& s) { return 6 * s.mat + scratch_bytes(s); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -166,16 +175,38 @@ gdn_status run_scan(const Shape& s, const void* A, const void* U, const float* g
   return hip_status(launch_scan(sa, s.io, nt, mode, stream));
 }
 
-// Forward pipeline shared by gdn_forward and gdn_step.
 gdn_status record(void* const* events, int i, hipStream_t stream) {
   if (!events) return GDN_OK;
   return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), stream));
 }
 
+// Token-form forward: one kernel, no workspace.  The phase events of
+// gdn_forward_events bracket it as the output phase.
+gdn_status run_token(const Shape& s, const void* q, const void* k, const void* v,
+                     const float* gamma, const float* beta, const float* state_in, void* o,
+                     float* state_out, hipStream_t stream, void* const* events) {
+  TokArgs ta{};
+  ta.q = q; ta.k = k; ta.v = v; ta.gamma = gamma; ta.beta = beta;
+  ta.z0 = state_in; ta.o = o; ta.zT = state_out; ta.s = s.s;
+  ta.B = (int)s.B; ta.H = (int)s.H; ta.T = (int)s.T; ta.N = (int)s.N;
+  const int cp = s.io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
+  ta.F = (int)(cp / s.N);
+  gdn_status st = GDN_OK;
+  for (int i = 0; i < 3 && st == GDN_OK; ++i) st = record(events, i, stream);
+  if (st != GDN_OK) return st;
+  st = hip_status(launch_token(ta, s.io, (int)(s.D / 16), stream));
+  if (st != GDN_OK) return st;
+  return record(events, 3, stream);
+}
+
+// Forward pipeline shared by gdn_forward and gdn_step.
+
 gdn_status run_forward(const Shape& s, const void* q, const void* k, const void* v,
                        const float* gamma, const float* beta, const float* state_in,
                        void* o, float* state_out, void* saved, void* workspace,
                        hipStream_t stream, void* const* events = nullptr) {
+  if (s.token)
+    return run_token(s, q, k, v, gamma, beta, state_in, o, state_out, stream, events);
   char* ws = static_cast<char*>(workspace);
   void* A = saved ? saved : ws;
   void* S = saved ? static_cast<char*>(saved) + s.mat : ws + s.mat;
@@ -229,7 +260,9 @@ const char* gdn_status_string(int status) {
     case GDN_ERR_BAD_DTYPE: return "unknown io dtype";
     case GDN_ERR_MISALIGNED: return "a pointer is misaligned (16 bytes; 4 for gates)";
     case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-    case GDN_ERR_UNSUPPORTED: return "unsupported head dimension (need Dk == Dv, multiple of 16, <= 128)";
+    case GDN_ERR_UNSUPPORTED:
+      return "unsupported: head dims (need Dk == Dv, a multiple of 16, <= 128), algorithm, "
+             "or the token form's limits (N <= 64 bf16 / 32 fp32, no saved buffer)";
     case GDN_ERR_HIP: return "HIP kernel launch failed";
     case GDN_ERR_ALIASING: return "an output overlaps an input";
   }
@@ -257,6 +290,7 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes) {
   Shape s;
   gdn_status st = check_problem(p, &s);
   if (st != GDN_OK) return st;
+  if (s.token) return GDN_ERR_UNSUPPORTED;   // the token form keeps no A_t, S_t
   *bytes = (size_t)(2 * s.mat);
   return GDN_OK;
 }
@@ -269,12 +303,14 @@ static gdn_status forward_checked(const gdn_problem* p, const void* q, const voi
   Shape s;
   gdn_status st = check_problem(p, &s);
   if (st != GDN_OK) return st;
-  if (!q || !k || !v || !gamma || !beta || !o || !workspace) return GDN_ERR_NULL_POINTER;
+  if (!q || !k || !v || !gamma || !beta || !o || (!workspace && forward_ws(s) > 0))
+    return GDN_ERR_NULL_POINTER;
   const void* ptrs[] = {q, k, v, state_in, o, state_out, saved, workspace};
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return GDN_ERR_MISALIGNED;
   if (!aligned4(gamma) || !aligned4(beta)) return GDN_ERR_MISALIGNED;
   if ((int64_t)workspace_bytes < forward_ws(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
+  if (s.token && saved) return GDN_ERR_UNSUPPORTED;   // no per-frame intermediates
   const int64_t tok = s.B * s.L * s.H * s.D * s.es;
   const int64_t stb = s.B * s.H * s.D * s.D * 4;
   const Span ins[] = {{q, tok}, {k, tok}, {v, tok}, {gamma, s.B * s.T * s.H * 4},

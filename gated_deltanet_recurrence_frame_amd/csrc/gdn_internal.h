@@ -116,4 +116,24 @@ struct BwdTokArgs {
 };
 hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
 
+// Token-space forward (frames with few tokens): one workgroup per (b, h),
+// chunks of F frames of N tokens, F N <= TokCfg<io>::CP.
+template <int IO> struct TokCfg {
+  static constexpr int CP = IO == IO_BF16 ? 64 : 32;   // tokens per chunk at most
+};
+struct TokArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;   // [B, T, H]
+  const float* beta;    // [B, L, H]
+  const float* z0;      // [B, H, D, D] fp32 initial state or nullptr (zero)
+  void* o;              // [B, L, H, D] io dtype
+  float* zT;            // [B, H, D, D] fp32 final state or nullptr; may equal z0
+  float s;              // key scale
+  int B, H, T, N;
+  int F;                // frames per chunk
+};
+hipError_t launch_token(const TokArgs& a, int io, int nt, hipStream_t s);
+
 }  // namespace gdn

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -63,7 +63,9 @@ typedef enum {
     GDN_ERR_BAD_DTYPE = 3,           /* io_dtype not a gdn_dtype              */
     GDN_ERR_MISALIGNED = 4,          /* a pointer misaligned (16 B; gates 4 B) */
     GDN_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < required            */
-    GDN_ERR_UNSUPPORTED = 6,         /* D not a multiple of 16, > 128, Dk!=Dv */
+    GDN_ERR_UNSUPPORTED = 6,         /* D not a multiple of 16, > 128, Dk!=Dv;
+                                        unknown algorithm; token form outside
+                                        its limits (see gdn_algorithm)        */
     GDN_ERR_HIP = 7,                 /* a kernel launch failed                */
     GDN_ERR_ALIASING = 8             /* an output overlaps an input           */
 } gdn_status;
@@ -71,6 +73,22 @@ typedef enum {
 typedef enum { GDN_BF16 = 0, GDN_FP32 = 1 } gdn_dtype;
 
 typedef enum { GDN_OP_FORWARD = 0, GDN_OP_STEP = 1, GDN_OP_BACKWARD = 2 } gdn_op;
+
+/* How gdn_forward / gdn_step evaluate the recurrence (same result up to
+ * rounding order):
+ *   GDN_ALGO_FRAME  the frame form: per frame A_t = K^_t beta_t K^_t^T and
+ *                   U_t = V_t beta_t K^_t^T (D x D), a scan over frames,
+ *                   then O_t = S_t Q^_t.  Any N.  Fills `saved`.
+ *   GDN_ALGO_TOKEN  the token form: chunks of F = floor(64 / N) frames
+ *                   (bf16; 32 / N for fp32) whose corrected values solve the
+ *                   delta rule's unit triangular system over the chunk's
+ *                   tokens; no D x D product per frame, no workspace.  For
+ *                   frames of few tokens (token-wise GDN is N = 1).
+ *                   Requires N <= 64 (bf16) / 32 (fp32) and saved == NULL.
+ *   GDN_ALGO_AUTO   currently the frame form.
+ * gdn_backward always uses the frame form (recomputing A_t, S_t when no
+ * saved buffer is given). */
+typedef enum { GDN_ALGO_AUTO = 0, GDN_ALGO_FRAME = 1, GDN_ALGO_TOKEN = 2 } gdn_algorithm;
 
 typedef struct {
     int32_t B, H, T, N;   /* batch, heads, latent frames, tokens per frame   */
@@ -83,6 +101,7 @@ typedef struct {
                              c >= 2 => composite prefix over chunks of c
                              frames (novelty point 1); same result up to
                              rounding order                                  */
+    int32_t algorithm;    /* gdn_algorithm of the forward                    */
 } gdn_problem;
 
 /* Version of this interface (GDN_ABI_VERSION). */
@@ -100,7 +119,8 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes);
  * *bytes).  Layout: A_t = K^_t beta_t K^_t^T as [B, H, T, Dk, Dk], followed
  * by the states S_t after every frame as [B, H, T, Dv, Dk], row-major, in
  * the intermediate type: bf16 (round to nearest even) when io_dtype is
- * GDN_BF16, fp32 when it is GDN_FP32. */
+ * GDN_BF16, fp32 when it is GDN_FP32.  GDN_ERR_UNSUPPORTED for the token
+ * form, which keeps neither. */
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
 
 /* Whole-sequence forward (module 2 recurrence over t = 1..T):
@@ -111,7 +131,8 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
  *   state_out  S_T; NULL => not written; may equal state_in (in place).
  *   saved      NULL, or gdn_saved_size bytes that receive A_t and S_t for
  *              gdn_backward.
- *   workspace  gdn_workspace_size(p, GDN_OP_FORWARD) bytes of scratch. */
+ *   workspace  gdn_workspace_size(p, GDN_OP_FORWARD) bytes of scratch (0
+ *              for the token form, which then accepts workspace == NULL). */
 gdn_status gdn_forward(const gdn_problem* p,
                        const void* q, const void* k, const void* v,
                        const float* gamma, const float* beta,

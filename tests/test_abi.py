@@ -33,7 +33,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2 == gb.ABI_VERSION
     for code in range(9):
         s = lib.gdn_status_string(code).decode()
         assert s and s != "unknown status"
@@ -119,3 +119,32 @@ def test_frame_larger_than_2gib_is_rejected(lib):
     assert gb.STATUS[_ws(p, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_BAD_SHAPE"
     p = gb.make_problem(1, 2000, 1, 2000, 128, "fp32")
     assert gb.STATUS[_ws(p, gb.GDN_OP_FORWARD)[0]] == "GDN_OK"
+
+
+def test_algorithm_field(lib):
+    vp = ctypes.c_void_p
+    p = gb.make_problem(1, 2, 4, 8, 32, "bf16", algorithm="token")
+    assert _ws(p, gb.GDN_OP_FORWARD) == (0, 0)          # the token form needs no workspace
+    n = ctypes.c_size_t(0)
+    assert gb.STATUS[lib.gdn_saved_size(ctypes.byref(p), ctypes.byref(n))] == "GDN_ERR_UNSUPPORTED"
+    # the backward is the frame form whatever the forward's algorithm
+    assert _ws(p, gb.GDN_OP_BACKWARD)[1] == _ws(gb.make_problem(1, 2, 4, 8, 32, "bf16"),
+                                                gb.GDN_OP_BACKWARD)[1]
+    good = [vp(0x100000 * (i + 1)) for i in range(10)]
+    # no saved buffer in the token form; a NULL workspace is fine there
+    code = lib.gdn_forward(ctypes.byref(p), *good[:9], None, 0, None)
+    assert gb.STATUS[code] == "GDN_ERR_UNSUPPORTED"
+    for io, nmax in (("bf16", 64), ("fp32", 32)):
+        ok = gb.make_problem(1, 2, 3, nmax, 16, io, algorithm="token")
+        assert _ws(ok, gb.GDN_OP_FORWARD)[0] == 0
+        big = gb.make_problem(1, 2, 3, nmax + 1, 16, io, algorithm="token")
+        assert gb.STATUS[_ws(big, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
+        # the frame form takes any N
+        assert _ws(gb.make_problem(1, 2, 3, nmax + 1, 16, io, algorithm="frame"),
+                   gb.GDN_OP_FORWARD)[0] == 0
+    bad = gb.make_problem(1, 2, 4, 8, 32, "bf16")
+    bad.algorithm = 3
+    assert gb.STATUS[_ws(bad, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
+    # auto is currently the frame form
+    auto = gb.make_problem(1, 2, 4, 1, 32, "bf16")
+    assert _ws(auto, gb.GDN_OP_FORWARD)[1] > 0

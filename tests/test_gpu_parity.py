@@ -35,11 +35,12 @@ def f64(t):
     return gin.as_f64(t)
 
 
-def run_forward_pair(inp, N, io, key_scale=0.0, scan_chunk=0, with_state=False):
+def run_forward_pair(inp, N, io, key_scale=0.0, scan_chunk=0, with_state=False,
+                     algorithm="auto"):
     d = {k: to_dev(v) for k, v in inp.items()}
     st = d.get("state") if with_state else None
     o, so = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, state_in=st,
-                       key_scale=key_scale, scan_chunk=scan_chunk)
+                       key_scale=key_scale, scan_chunk=scan_chunk, algorithm=algorithm)
     torch.cuda.synchronize()
     ro, rs = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
                             f64(inp["beta"]), N,
@@ -255,6 +256,56 @@ def test_chunk_causal_windows_equal_one_call(io):
                             f64(inp["beta"]), N, state_in=f64(inp["state"]))
     assert rel_l2(f64(o_win.cpu()), ro) <= TOL[io]
     assert rel_l2(f64(state.cpu()), rs) <= TOL[io]
+
+
+# ------------------------------------------------------------ token form
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("N,T,D", [(1, 150, 112), (2, 70, 112), (3, 50, 48), (5, 27, 112),
+                                   (7, 20, 128), (16, 9, 112), (32, 5, 16), (1, 100, 16),
+                                   (2, 40, 32)])
+def test_token_form_matches_oracle(io, N, T, D):
+    # chunks of floor(CP / N) frames, a ragged last chunk, a carried state;
+    # small D leaves fewer waves than 16-token blocks of a chunk
+    inp = gin.make_inputs(B=1, H=3, T=T, N=N, D=D, io=io, gamma="sigmoid", seed=40 + N,
+                          with_state=True)
+    check_forward(inp, N, io, with_state=True, algorithm="token")
+
+
+@pytest.mark.parametrize("N", [33, 64])
+def test_token_form_long_frames_bf16(N):
+    # frames longer than half a chunk: one frame per chunk (fp32 stops at 32)
+    inp = gin.make_inputs(B=2, H=2, T=6, N=N, D=112, io="bf16", gamma="uniform", seed=50 + N,
+                          with_state=True)
+    check_forward(inp, N, "bf16", with_state=True, algorithm="token")
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_token_form_equals_frame_form_in_place(io):
+    B, H, T, N, D = 1, 4, 40, 4, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=60,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    o_f, s_f = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                          state_in=d["state"], algorithm="frame")
+    plan = gb.ForwardPlan(B, H, T, N, D, io, torch.device(DEV), algorithm="token")
+    st = d["state"].clone()
+    o_t, s_t = plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"], state_in=st, state_out=st)
+    torch.cuda.synchronize()
+    assert s_t.data_ptr() == st.data_ptr()
+    tol = 1e-5 if io == "fp32" else 2e-2
+    assert rel_l2(f64(o_t.cpu()), f64(o_f.cpu())) <= tol
+    assert rel_l2(f64(st.cpu()), f64(s_f.cpu())) <= tol
+
+
+def test_token_form_gates_far_from_one_fp32():
+    # gamma down to ~0.05 inside a chunk of 64 one-token frames: the decay
+    # table's products must not lose the small ones
+    B, H, T, N, D = 1, 2, 96, 1, 32
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io="fp32", gamma="uniform", seed=61,
+                          with_state=True)
+    rng = np.random.default_rng(62)
+    inp["gamma"] = torch.from_numpy(rng.uniform(0.05, 1.0, (B, T, H)).astype(np.float32))
+    check_forward(inp, N, "fp32", with_state=True, algorithm="token")
 
 
 # -------------------------------------------------------------- backward
