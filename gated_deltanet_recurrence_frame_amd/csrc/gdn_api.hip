@@ -110,7 +110,15 @@ int64_t scratch_bytes(const Shape& s) {
   return a > b ? a : b;
 }
 
-int64_t forward_ws(const Shape& s) { return s.token ? 0 : 3 * s.mat + scratch_bytes(s); }
+// Token form: per-chunk operators of F = CP / N frames for every (b, h).
+int64_t token_frames(const Shape& s) {
+  return (s.io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP) / s.N;
+}
+int64_t token_ws(const Shape& s) {
+  const int64_t F = token_frames(s);
+  return s.B * s.H * ((s.T + F - 1) / F) * token_record_bytes(s.io);
+}
+int64_t forward_ws(const Shape& s) { return s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s); }
 int64_t backward_ws(const Shape& s) { return 6 * s.mat + scratch_bytes(s); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -180,17 +188,21 @@ gdn_status record(void* const* events, int i, hipStream_t stream) {
   return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), stream));
 }
 
-// Token-form forward: one kernel, no workspace.  The phase events of
-// gdn_forward_events bracket it as the output phase.
+// Token-form forward: the per-chunk operators into the workspace, then the
+// state pass.  The phase events of gdn_forward_events bracket both as the
+// output phase.
 gdn_status run_token(const Shape& s, const void* q, const void* k, const void* v,
                      const float* gamma, const float* beta, const float* state_in, void* o,
-                     float* state_out, hipStream_t stream, void* const* events) {
+                     float* state_out, void* workspace, hipStream_t stream,
+                     void* const* events) {
   TokArgs ta{};
   ta.q = q; ta.k = k; ta.v = v; ta.gamma = gamma; ta.beta = beta;
   ta.z0 = state_in; ta.o = o; ta.zT = state_out; ta.s = s.s;
   ta.B = (int)s.B; ta.H = (int)s.H; ta.T = (int)s.T; ta.N = (int)s.N;
-  const int cp = s.io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
-  ta.F = (int)(cp / s.N);
+  ta.F = (int)token_frames(s);
+  ta.nck = (int)((s.T + ta.F - 1) / ta.F);
+  ta.ws = workspace;
+  ta.rec_bytes = token_record_bytes(s.io);
   gdn_status st = GDN_OK;
   for (int i = 0; i < 3 && st == GDN_OK; ++i) st = record(events, i, stream);
   if (st != GDN_OK) return st;
@@ -206,7 +218,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
                        void* o, float* state_out, void* saved, void* workspace,
                        hipStream_t stream, void* const* events = nullptr) {
   if (s.token)
-    return run_token(s, q, k, v, gamma, beta, state_in, o, state_out, stream, events);
+    return run_token(s, q, k, v, gamma, beta, state_in, o, state_out, workspace, stream, events);
   char* ws = static_cast<char*>(workspace);
   void* A = saved ? saved : ws;
   void* S = saved ? static_cast<char*>(saved) + s.mat : ws + s.mat;
@@ -303,8 +315,7 @@ static gdn_status forward_checked(const gdn_problem* p, const void* q, const voi
   Shape s;
   gdn_status st = check_problem(p, &s);
   if (st != GDN_OK) return st;
-  if (!q || !k || !v || !gamma || !beta || !o || (!workspace && forward_ws(s) > 0))
-    return GDN_ERR_NULL_POINTER;
+  if (!q || !k || !v || !gamma || !beta || !o || !workspace) return GDN_ERR_NULL_POINTER;
   const void* ptrs[] = {q, k, v, state_in, o, state_out, saved, workspace};
   for (const void* x : ptrs)
     if (x && !aligned16(x)) return GDN_ERR_MISALIGNED;

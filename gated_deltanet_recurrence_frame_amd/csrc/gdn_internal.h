@@ -133,7 +133,11 @@ struct TokArgs {
   float s;              // key scale
   int B, H, T, N;
   int F;                // frames per chunk
+  int nck;              // chunks per sequence, ceil(T / F)
+  void* ws;             // B H nck records of token_record_bytes(io) bytes
+  int64_t rec_bytes;
 };
+int64_t token_record_bytes(int io);
 hipError_t launch_token(const TokArgs& a, int io, int nt, hipStream_t s);
 
 }  // namespace gdn

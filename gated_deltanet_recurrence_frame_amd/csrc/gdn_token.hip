@@ -12,16 +12,22 @@
 //   o_t     = P(0, f(t)) E_0 q_t + sum_{f(u) <= f(t)} P(f(u)+1, f(t)) w_u (k^_u . q_t)
 //   E_F     = P(0, F-1) E_0 + sum_u P(f(u)+1, F-1) w_u k^_u^T.
 // L is strictly upper triangular in token order (a frame's tokens do not see
-// each other), so I + L is unit upper triangular: its inverse is formed per
-// chunk by substitution on the 16 x 16 diagonal blocks and block
-// back-substitution above them (fp32), and W = R (I + L)^-1.
+// each other), so I + L is unit upper triangular.
 //
-// One workgroup per (b, h) sequence, one wave per 16 state rows (rows of S
-// evolve independently); the token x token products of a chunk (K K^T,
-// K Q^T, the triangular inverse) are shared by the waves through LDS.
-// bf16 io: bf16 MFMA 16x16x32 with fp32 accumulation, the state and the
-// corrected values rounded to bf16 as MFMA operands (as in the frame form's
-// scan); fp32 io: fp32 MFMA 16x16x4 throughout.
+// Two kernels.  Everything that depends only on a chunk's own K, Q, beta
+// and gamma - the inverse (I + L)^-1 (substitution on 16 x 16 diagonal
+// blocks, block back-substitution above them, fp32), the output mixing
+// Om[u, t] = P(f(u)+1, f(t)) (k^_u . q_t) and the per-token decays - is
+// computed for all chunks at once (token_prep_kernel, one workgroup per
+// (b, h, chunk)) into the workspace.  The state pass (token_scan_kernel,
+// one workgroup per (b, h), one wave per 16 state rows) then only does
+// what depends on the state, chunk after chunk:
+//   SK = E_0 K^T, SQ = E_0 Q^T, R, W = R (I + L)^-1, O = P(0, f) SQ + W Om,
+//   E_F = P(0, F-1) E_0 + s (W tail) K,
+// with the next chunk's inputs in flight in a register ring.
+// bf16 io: bf16 MFMA 16x16x32 with fp32 accumulation, the state and W
+// rounded to bf16 as MFMA operands (as in the frame form's scan); fp32 io:
+// fp32 MFMA 16x16x4 throughout.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -30,35 +36,227 @@
 namespace gdn {
 
 template <int IO, int NT>
-__global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
+struct TokLayout {
   typedef typename Io<IO>::elem E;
-  constexpr bool BF = (IO == IO_BF16);
-  constexpr int D = 16 * NT;
-  constexpr int CP = TokCfg<IO>::CP;          // tokens per chunk at most
-  constexpr int NB = CP / 16;                 // 16-token blocks
-  constexpr int KS = BF ? 32 : 4;             // MFMA contraction depth
-  constexpr int DP = (D + KS - 1) / KS * KS;  // feature dim padded to KS (zeros)
-  constexpr int PAD = BF ? 8 : 4;             // 16 bytes
-  constexpr int KLD = DP + PAD;               // K, Q rows in LDS
-  constexpr int ZW = DP > 2 * CP ? DP : 2 * CP;
-  constexpr int ZLD = ZW + PAD;               // a wave's staged rows
-  constexpr int FLD = CP + 1;                 // fp32 token x token matrices
-  constexpr int TLD = CP + PAD;               // their transposed MFMA copies
-  constexpr int DLD = CP + 1;                 // decay table
-  constexpr int NTH = 64 * NT;
-  constexpr int PR = D * Io<IO>::bytes / 16;  // 16-byte pieces of a token row
-  constexpr int EP = 16 / Io<IO>::bytes;      // elements per piece
+  static constexpr bool BF = (IO == IO_BF16);
+  static constexpr int D = 16 * NT;
+  static constexpr int CP = TokCfg<IO>::CP;
+  static constexpr int NB = CP / 16;
+  static constexpr int KS = BF ? 32 : 4;              // MFMA contraction depth
+  static constexpr int DP = (D + KS - 1) / KS * KS;   // feature dim padded to KS (zeros)
+  static constexpr int PAD = BF ? 8 : 4;              // 16 bytes
+  static constexpr int KLD = DP + PAD;                // K, Q rows in LDS
+  static constexpr int FLD = CP + 1;                  // fp32 token x token matrices
+  static constexpr int TLD = CP + PAD;                // MFMA copies of them
+  static constexpr int DLD = CP + 1;                  // decay table
+  static constexpr int ES = Io<IO>::bytes;
+  static constexpr int PR = D * ES / 16;              // 16-byte pieces of a token row
+  static constexpr int EP = 16 / ES;                  // elements per piece
+  static constexpr int CPR = CP * ES / 16;            // pieces of a CP-element row
+};
+
+// ---------------------------------------------------------------------------
+// Per-chunk operators, one workgroup of 4 waves per (b, h, chunk).  Record
+// (b, h, chunk) of the workspace: TiT[t][u] = (I + L)^-1[u][t], OmT[t][u] =
+// Om[u][t] (CP x CP each, io type), then 5 x CP floats: P(0, f(t) - 1),
+// P(0, f(t)), P(f(t) + 1, F - 1), beta_t, and P(0, F - 1) first in the last.
+template <int IO, int NT>
+__global__ __launch_bounds__(256) void token_prep_kernel(TokArgs a) {
+  typedef TokLayout<IO, NT> Y;
+  typedef typename Y::E E;
+  constexpr bool BF = Y::BF;
+  constexpr int D = Y::D, CP = Y::CP, NB = Y::NB, KS = Y::KS, DP = Y::DP, KLD = Y::KLD;
+  constexpr int FLD = Y::FLD, DLD = Y::DLD, EP = Y::EP;
+  constexpr int NW = 4, NTH = 256;
 
   __shared__ __attribute__((aligned(16))) E Ks[CP * KLD];
   __shared__ __attribute__((aligned(16))) E Qs[CP * KLD];
-  __shared__ __attribute__((aligned(16))) E Zs[NT][16 * ZLD];
   __shared__ float KKs[CP * FLD];      // K^ K^^T, then L in place
   __shared__ float KQs[CP * FLD];      // K Q^T, then (I + L)^-1
-  __shared__ __attribute__((aligned(16))) E TiT[CP * TLD];   // (I + L)^-1, transposed
-  __shared__ __attribute__((aligned(16))) E OmT[CP * TLD];   // output mixing, transposed
   __shared__ float Dt[(CP + 1) * DLD];  // Dt[x][c] = P(x, c - 1)
   __shared__ float Ys[NB][256];
   __shared__ float gs[CP], bs[CP];
+  __shared__ int fr[CP];
+
+  const int total = a.B * a.H * a.nck;
+  const int item = xcd_item(blockIdx.x, total);
+  const int ck = item % a.nck, bh = item / a.nck;
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, li = lane & 15;
+  const int N = a.N, T = a.T;
+  const long L = (long)T * N;
+  const int t0 = ck * a.F;
+  const int nf = min(a.F, T - t0);
+  const int C = nf * N;
+  const long tok0 = (long)t0 * N;
+  const float s = a.s, s2 = a.s * a.s;
+  const E* K = static_cast<const E*>(a.k);
+  const E* Q = static_cast<const E*>(a.q);
+
+  auto toE = [](float x) -> E {
+    if constexpr (BF) return f32_to_bf16_bits(x); else return x;
+  };
+  auto fragA = [&](const E* M, int ld, int m0, int k0) {
+    if constexpr (BF) return load_bf16x8(M + (m0 + li) * ld + k0 + 8 * g);
+    else return M[(m0 + li) * ld + k0 + g];
+  };
+  auto mma = [&](auto x, auto y, f32x4 c) {
+    if constexpr (BF) return mfma_bf16(x, y, c); else return mfma_f32(x, y, c);
+  };
+  auto fence = []() {   // a wave's LDS writes land before its lanes read them back
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+  };
+
+  // 1. the chunk's K and Q rows (zero past C and in the feature padding), gates
+  for (int p = tid; p < CP * (DP / EP); p += NTH) {
+    const int u = p / (DP / EP), c = (p % (DP / EP)) * EP;
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
+    if (u < C && c < D) {
+      const long off = (((long)b * L + tok0 + u) * a.H + h) * D + c;
+      kv = *reinterpret_cast<const u32x4*>(K + off);
+      qv = *reinterpret_cast<const u32x4*>(Q + off);
+    }
+    *reinterpret_cast<u32x4*>(&Ks[u * KLD + c]) = kv;
+    *reinterpret_cast<u32x4*>(&Qs[u * KLD + c]) = qv;
+  }
+  if (tid < CP) {
+    gs[tid] = tid < nf ? a.gamma[((long)b * T + t0 + tid) * a.H + h] : 0.f;
+    bs[tid] = tid < C ? a.beta[((long)b * L + tok0 + tid) * a.H + h] : 0.f;
+    fr[tid] = tid / N;
+  }
+  block_sync();
+
+  // 2. decay table (a thread per row); K^ K^^T on blocks i <= j and K Q^T
+  for (int x = tid; x <= nf; x += NTH) {
+    float p = 1.f;
+    Dt[x * DLD + x] = 1.f;
+    for (int c = x + 1; c <= nf; ++c) {
+      p *= gs[c - 1];
+      Dt[x * DLD + c] = p;
+    }
+  }
+  {
+    constexpr int NP = NB * (NB + 1) / 2;
+    for (int q = w; q < NP + NB * NB; q += NW) {
+      int i, j;
+      const bool kq = q >= NP;
+      if (kq) {
+        i = (q - NP) / NB; j = (q - NP) % NB;
+      } else {
+        int rem = q; i = 0;
+        while (rem >= NB - i) { rem -= NB - i; ++i; }
+        j = i + rem;
+      }
+      const E* Bm = kq ? Qs : Ks;
+      f32x4 acc = zero4();
+      for (int kb = 0; kb < DP / KS; ++kb)
+        acc = mma(fragA(Ks, KLD, 16 * i, kb * KS), fragA(Bm, KLD, 16 * j, kb * KS), acc);
+      float* dst = kq ? KQs : KKs;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * FLD + 16 * j + li] = acc[r];
+    }
+  }
+  block_sync();
+
+  // 3. L (in place of K K^T); the output mixing and the vector to the record
+  E* rec = reinterpret_cast<E*>(static_cast<char*>(a.ws) + ((long)bh * a.nck + ck) * a.rec_bytes);
+  E* TiT = rec;
+  E* OmT = rec + CP * CP;
+  float* vec = reinterpret_cast<float*>(rec + 2 * CP * CP);
+  for (int e = tid; e < CP * CP; e += NTH) {
+    const int t = e / CP, u = e % CP;   // consecutive threads: consecutive u
+    const bool valid = u < C && t < C;
+    const int fu = fr[u], ft = fr[t];
+    const float kk = KKs[u * FLD + t], kq = KQs[u * FLD + t];
+    KKs[u * FLD + t] = (valid && fu < ft) ? s2 * kk * Dt[(fu + 1) * DLD + ft] * bs[t] : 0.f;
+    OmT[t * CP + u] = toE((valid && fu <= ft) ? s * kq * Dt[(fu + 1) * DLD + ft + 1] : 0.f);
+  }
+  if (tid < CP) {
+    const int t = tid, f = fr[t];
+    const bool valid = t < C;
+    vec[t] = valid ? Dt[f] : 0.f;                            // P(0, f(t) - 1)
+    vec[CP + t] = valid ? Dt[f + 1] : 0.f;                   // P(0, f(t))
+    vec[2 * CP + t] = valid ? Dt[(f + 1) * DLD + nf] : 0.f;  // P(f(t) + 1, F - 1)
+    vec[3 * CP + t] = bs[t];                                 // beta_t
+    vec[4 * CP + t] = t == 0 ? Dt[nf] : 0.f;                 // P(0, F - 1)
+  }
+  block_sync();
+
+  // 4. (I + L)^-1 into KQs: diagonal blocks by substitution (lane c holds
+  // column c), then block back-substitution by distance
+  for (int I = w; I < NB; I += NW) {
+    if (g == 0) {
+      const float* Lb = &KKs[16 * I * FLD + 16 * I];
+      float x[16];
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        float acc = (i == li) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = i + 1; j < 16; ++j) acc -= Lb[i * FLD + j] * x[j];
+        x[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) KQs[(16 * I + i) * FLD + 16 * I + li] = x[i];
+    }
+  }
+  block_sync();
+  for (int d = 1; d < NB; ++d) {
+    for (int I = w; I < NB - d; I += NW) {
+      const int J = I + d;
+      f32x4 y = zero4();
+      for (int Kb = I + 1; Kb <= J; ++Kb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          y = mfma_f32(KKs[(16 * I + li) * FLD + 16 * Kb + 4 * kk + g],
+                       KQs[(16 * Kb + 4 * kk + g) * FLD + 16 * J + li], y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ys[I][(4 * g + r) * 16 + li] = y[r];
+      fence();
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        x = mfma_f32(KQs[(16 * I + li) * FLD + 16 * I + 4 * kk + g], Ys[I][(4 * kk + g) * 16 + li], x);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) KQs[(16 * I + 4 * g + r) * FLD + 16 * J + li] = -x[r];
+    }
+    block_sync();
+  }
+  // 5. the inverse, transposed: TiT[t][u] = (I + L)^-1[u][t]
+  for (int e = tid; e < CP * CP; e += NTH) {
+    const int t = e / CP, u = e % CP;
+    TiT[t * CP + u] = toE((u >> 4) <= (t >> 4) ? KQs[u * FLD + t] : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The state pass: one workgroup per (b, h), wave w owns state rows
+// 16 w .. 16 w + 15 (in fp32 registers), chunks in order.
+template <int IO, int NT>
+__global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
+  typedef TokLayout<IO, NT> Y;
+  typedef typename Y::E E;
+  constexpr bool BF = Y::BF;
+  constexpr int D = Y::D, CP = Y::CP, NB = Y::NB, KS = Y::KS, DP = Y::DP, PAD = Y::PAD;
+  constexpr int KLD = Y::KLD, TLD = Y::TLD, PR = Y::PR, EP = Y::EP, CPR = Y::CPR;
+  constexpr int ZW = DP > 2 * CP ? DP : 2 * CP;
+  constexpr int ZLD = ZW + PAD;               // a wave's staged rows
+  constexpr int NTH = 64 * NT;
+  constexpr int VEC = 5 * CP;                 // floats of a chunk's decay/gate vector
+  // ring pieces (16 bytes): K and Q rows, the two CP x CP operators, the vector
+  constexpr int NKQ = 2 * CP * PR, NOP = 2 * CP * CPR, NVEC = VEC * 4 / 16;
+  constexpr int NPC = NKQ + NOP + NVEC;
+  constexpr int PPT = (NPC + NTH - 1) / NTH;
+
+  __shared__ __attribute__((aligned(16))) E Ks[CP * KLD];
+  __shared__ __attribute__((aligned(16))) E Qs[CP * KLD];
+  __shared__ __attribute__((aligned(16))) E TiT[CP * TLD];
+  __shared__ __attribute__((aligned(16))) E OmT[CP * TLD];
+  __shared__ __attribute__((aligned(16))) float vec[VEC];
+  __shared__ __attribute__((aligned(16))) E Zs[NT][16 * ZLD];
 
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh % a.H;
@@ -67,7 +265,7 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
   const int g = lane >> 4, li = lane & 15;
   const int N = a.N, T = a.T;
   const long L = (long)T * N;
-  const float s = a.s, s2 = a.s * a.s;
+  const float s = a.s;
   const E* K = static_cast<const E*>(a.k);
   const E* Q = static_cast<const E*>(a.q);
   const E* V = static_cast<const E*>(a.v);
@@ -77,8 +275,6 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
   auto toE = [](float x) -> E {
     if constexpr (BF) return f32_to_bf16_bits(x); else return x;
   };
-  // MFMA operands.  A[m][k] = M[m0 + m][k0 + k]; Bt: B[k][n] = M[n0 + n][k0 + k];
-  // Bn: B[k][n] = M[k0 + k][n0 + n] (M row-major with row stride ld).
   auto fragA = [&](const E* M, int ld, int m0, int k0) {
     if constexpr (BF) return load_bf16x8(M + (m0 + li) * ld + k0 + 8 * g);
     else return M[(m0 + li) * ld + k0 + g];
@@ -90,17 +286,60 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
   auto mma = [&](auto x, auto y, f32x4 c) {
     if constexpr (BF) return mfma_bf16(x, y, c); else return mfma_f32(x, y, c);
   };
-  // 16 x 16 tile of (rows of A) x (rows of Bm)^T over kn contraction steps
-  auto tile_nt = [&](const E* Am, int lda, int m0, const E* Bm, int ldb, int n0, int kn) {
-    f32x4 acc = zero4();
-    for (int kb = 0; kb < kn; ++kb) acc = mma(fragA(Am, lda, m0, kb * KS), fragA(Bm, ldb, n0, kb * KS), acc);
-    return acc;
-  };
-  // a wave's own LDS writes complete before it reads them back in other lanes
-  auto fence = []() {
+  auto fence = []() {   // a wave's LDS writes land before its lanes read them back
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
     asm volatile("" ::: "memory");
+  };
+
+  // Register ring, one chunk ahead: 16-byte pieces p = tid + NTH j of
+  // [K rows | Q rows | TiT, OmT | vector], and this lane's V values.
+  typedef typename std::conditional<BF, u32x2, f32x4>::type VP;
+  struct Pre {
+    u32x4 pc[PPT];
+    VP v[NB];
+  };
+  auto prefetch = [&](Pre& P, int ck) {
+    const int t0 = ck * a.F;
+    const int Cn = min(a.F, T - t0) * N;
+    const long tok0 = (long)t0 * N;
+    const char* rec = static_cast<const char*>(a.ws) + ((long)bh * a.nck + ck) * a.rec_bytes;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      P.pc[j] = u32x4{0u, 0u, 0u, 0u};
+      if (p < NKQ) {
+        const int m = p / (CP * PR), q = p % (CP * PR), u = q / PR;
+        if (u < Cn)
+          P.pc[j] = *reinterpret_cast<const u32x4*>(
+              (m ? Q : K) + (((long)b * L + tok0 + u) * a.H + h) * D + (q % PR) * EP);
+      } else if (p < NPC) {
+        P.pc[j] = *reinterpret_cast<const u32x4*>(rec + (long)(p - NKQ) * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = 16 * j + li;
+      P.v[j] = VP{};
+      if (t < Cn)
+        P.v[j] = *reinterpret_cast<const VP*>(V + (((long)b * L + tok0 + t) * a.H + h) * D +
+                                               16 * w + 4 * g);
+    }
+  };
+  auto commit = [&](const Pre& P) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      if (p < NKQ) {
+        const int m = p / (CP * PR), q = p % (CP * PR);
+        *reinterpret_cast<u32x4*>(&(m ? Qs : Ks)[(q / PR) * KLD + (q % PR) * EP]) = P.pc[j];
+      } else if (p < NKQ + NOP) {
+        const int o = p - NKQ, m = o / (CP * CPR), q = o % (CP * CPR);
+        *reinterpret_cast<u32x4*>(&(m ? OmT : TiT)[(q / CPR) * TLD + (q % CPR) * EP]) = P.pc[j];
+      } else if (p < NPC) {
+        *reinterpret_cast<u32x4*>(&vec[(p - NKQ - NOP) * 4]) = P.pc[j];
+      }
+    }
   };
 
   // the state: wave w holds rows 16 w .. 16 w + 15, tile n in Sreg[n]
@@ -114,7 +353,7 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
         Sreg[n][r] = a.z0[((long)bh * D + 16 * w + 4 * g + r) * D + 16 * n + li];
     }
   }
-  // zero feature padding of K and Q rows once (never written again)
+  // feature padding of K and Q rows: zero once, never written again
   if constexpr (DP > D) {
     for (int e = tid; e < CP * (DP - D); e += NTH) {
       const int u = e / (DP - D), c = D + e % (DP - D);
@@ -123,27 +362,16 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
     }
   }
 
-  for (int t0 = 0; t0 < T; t0 += a.F) {
-    const int nf = min(a.F, T - t0);
-    const int C = nf * N;
+  Pre cur, nxt;
+  prefetch(cur, 0);
+  for (int ck = 0; ck < a.nck; ++ck) {
+    const int t0 = ck * a.F;
+    const int C = min(a.F, T - t0) * N;
     const long tok0 = (long)t0 * N;
 
-    // 1. the chunk's K, Q rows (zero past C), gates, and this wave's state rows
-    for (int p = tid; p < CP * PR; p += NTH) {
-      const int u = p / PR, c = (p % PR) * EP;
-      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
-      if (u < C) {
-        const long off = (((long)b * L + tok0 + u) * a.H + h) * D + c;
-        kv = *reinterpret_cast<const u32x4*>(K + off);
-        qv = *reinterpret_cast<const u32x4*>(Q + off);
-      }
-      *reinterpret_cast<u32x4*>(&Ks[u * KLD + c]) = kv;
-      *reinterpret_cast<u32x4*>(&Qs[u * KLD + c]) = qv;
-    }
-    if (tid < CP) {
-      gs[tid] = tid < nf ? a.gamma[((long)b * T + t0 + tid) * a.H + h] : 0.f;
-      bs[tid] = tid < C ? a.beta[((long)b * L + tok0 + tid) * a.H + h] : 0.f;
-    }
+    // 1. this chunk's inputs into LDS, the state rows staged; next chunk's
+    // loads in flight
+    commit(cur);
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -152,134 +380,68 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Zw[(4 * g + r) * ZLD + D + li] = toE(0.f);
     }
+    if (ck + 1 < a.nck) prefetch(nxt, ck + 1);
     block_sync();
 
-    // 2. decay table; token x token products; this wave's E_0 K^T and E_0 Q^T
-    for (int x = tid; x <= nf; x += NTH) {
-      float p = 1.f;
-      Dt[x * DLD + x] = 1.f;
-      for (int c = x + 1; c <= nf; ++c) {
-        p *= gs[c - 1];
-        Dt[x * DLD + c] = p;
-      }
-    }
-    {
-      constexpr int NP = NB * (NB + 1) / 2;   // K K^T: blocks i <= j
-      for (int q = w; q < NP + NB * NB; q += NT) {
-        int i, j;
-        const bool kq = q >= NP;
-        if (kq) {
-          i = (q - NP) / NB; j = (q - NP) % NB;
-        } else {
-          int rem = q; i = 0;
-          while (rem >= NB - i) { rem -= NB - i; ++i; }
-          j = i + rem;
-        }
-        const f32x4 acc = tile_nt(Ks, KLD, 16 * i, kq ? Qs : Ks, KLD, 16 * j, DP / KS);
-        float* dst = kq ? KQs : KKs;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * FLD + 16 * j + li] = acc[r];
-      }
-    }
+    // 2. SK = E_0 K^T, SQ = E_0 Q^T (the staged rows are the A operand of all)
     f32x4 SK[NB], SQ[NB];
+    {
+      decltype(fragA(Zw, ZLD, 0, 0)) af[DP / KS];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      SK[j] = tile_nt(Zw, ZLD, 0, Ks, KLD, 16 * j, DP / KS);
-      SQ[j] = tile_nt(Zw, ZLD, 0, Qs, KLD, 16 * j, DP / KS);
-    }
-    block_sync();
-
-    // 3. L (in place of K K^T) and the output mixing Om (transposed copy)
-    for (int e = tid; e < CP * CP; e += NTH) {
-      const int u = e / CP, t = e % CP;
-      const bool valid = u < C && t < C;
-      const int fu = u / N, ft = t / N;
-      const float kk = KKs[u * FLD + t], kq = KQs[u * FLD + t];
-      KKs[u * FLD + t] = (valid && fu < ft) ? s2 * kk * Dt[(fu + 1) * DLD + ft] * bs[t] : 0.f;
-      OmT[t * TLD + u] = toE((valid && fu <= ft) ? s * kq * Dt[(fu + 1) * DLD + ft + 1] : 0.f);
-    }
-    block_sync();
-
-    // 4. (I + L)^-1 into KQs: diagonal blocks by substitution (lane c of
-    // the wave handling block I holds column c), then block
-    // back-substitution by distance; blocks are dealt to the waves in turn
-    for (int I = w; I < NB; I += NT) {
-      if (g == 0) {
-        const float* Lb = &KKs[16 * I * FLD + 16 * I];
-        float x[16];
+      for (int kb = 0; kb < DP / KS; ++kb) af[kb] = fragA(Zw, ZLD, 0, kb * KS);
 #pragma unroll
-        for (int i = 15; i >= 0; --i) {
-          float acc = (i == li) ? 1.f : 0.f;
+      for (int j = 0; j < NB; ++j) {
+        f32x4 sk = zero4(), sq = zero4();
 #pragma unroll
-          for (int j = i + 1; j < 16; ++j) acc -= Lb[i * FLD + j] * x[j];
-          x[i] = acc;
+        for (int kb = 0; kb < DP / KS; ++kb) {
+          sk = mma(af[kb], fragA(Ks, KLD, 16 * j, kb * KS), sk);
+          sq = mma(af[kb], fragA(Qs, KLD, 16 * j, kb * KS), sq);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) KQs[(16 * I + i) * FLD + 16 * I + li] = x[i];
+        SK[j] = sk;
+        SQ[j] = sq;
       }
     }
-    block_sync();
-    for (int d = 1; d < NB; ++d) {
-      for (int I = w; I < NB - d; I += NT) {
-        const int J = I + d;
-        f32x4 y = zero4();
-        for (int Kb = I + 1; Kb <= J; ++Kb)
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            y = mfma_f32(KKs[(16 * I + li) * FLD + 16 * Kb + 4 * kk + g],
-                         KQs[(16 * Kb + 4 * kk + g) * FLD + 16 * J + li], y);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ys[I][(4 * g + r) * 16 + li] = y[r];
-        fence();
-        f32x4 x = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          x = mfma_f32(KQs[(16 * I + li) * FLD + 16 * I + 4 * kk + g], Ys[I][(4 * kk + g) * 16 + li], x);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) KQs[(16 * I + 4 * g + r) * FLD + 16 * J + li] = -x[r];
-      }
-      block_sync();
-    }
-    for (int e = tid; e < CP * CP; e += NTH) {
-      const int u = e / CP, t = e % CP;
-      TiT[t * TLD + u] = toE((u >> 4) <= (t >> 4) ? KQs[u * FLD + t] : 0.f);
-    }
-    block_sync();
+    fence();
 
-    // 5. R for this wave's rows, then W = R (I + L)^-1
-    f32x4 Wr[NB];
+    // 3. R = (V - P(0, f - 1) s SK) beta, staged; W = R (I + L)^-1
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int t = 16 * j + li;
-      f32x4 vv = zero4();
-      if (t < C) {
-        const long off = (((long)b * L + tok0 + t) * a.H + h) * D + 16 * w + 4 * g;
-        if constexpr (BF) {
-          const u32x2 pv = *reinterpret_cast<const u32x2*>(V + off);
-          vv[0] = bf16_bits_to_f32((uint16_t)(pv[0] & 0xffff));
-          vv[1] = bf16_bits_to_f32((uint16_t)(pv[0] >> 16));
-          vv[2] = bf16_bits_to_f32((uint16_t)(pv[1] & 0xffff));
-          vv[3] = bf16_bits_to_f32((uint16_t)(pv[1] >> 16));
-        } else {
-          vv = *reinterpret_cast<const f32x4*>(V + off);
-        }
+      f32x4 vv;
+      if constexpr (BF) {
+        vv[0] = bf16_bits_to_f32((uint16_t)(cur.v[j][0] & 0xffff));
+        vv[1] = bf16_bits_to_f32((uint16_t)(cur.v[j][0] >> 16));
+        vv[2] = bf16_bits_to_f32((uint16_t)(cur.v[j][1] & 0xffff));
+        vv[3] = bf16_bits_to_f32((uint16_t)(cur.v[j][1] >> 16));
+      } else {
+        vv = cur.v[j];
       }
-      const float before = t < C ? Dt[t / N] : 0.f;   // P(0, f(t) - 1)
-      const float bt = bs[t];
+      const float before = vec[t], bt = vec[3 * CP + t];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         Zw[(4 * g + r) * ZLD + t] = toE((vv[r] - s * before * SK[j][r]) * bt);
     }
     fence();
+    f32x4 Wr[NB];
+    {
+      decltype(fragA(Zw, ZLD, 0, 0)) rf[CP / KS];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) Wr[j] = tile_nt(Zw, ZLD, 0, TiT, TLD, 16 * j, CP / KS);
+      for (int kb = 0; kb < CP / KS; ++kb) rf[kb] = fragA(Zw, ZLD, 0, kb * KS);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < CP / KS; ++kb) acc = mma(rf[kb], fragA(TiT, TLD, 16 * j, kb * KS), acc);
+        Wr[j] = acc;
+      }
+    }
     fence();
 
-    // 6. outputs: O = P(0, f(t)) E_0 Q + W Om
+    // 4. W and W tail staged; O = P(0, f) SQ + W Om
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int t = 16 * j + li;
-      const float tail = t < C ? Dt[(t / N + 1) * DLD + nf] : 0.f;   // P(f(t)+1, F-1)
+      const float tail = vec[2 * CP + t];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         Zw[(4 * g + r) * ZLD + t] = toE(Wr[j][r]);
@@ -287,38 +449,47 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
       }
     }
     fence();
+    {
+      decltype(fragA(Zw, ZLD, 0, 0)) wf[CP / KS];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const f32x4 acc = tile_nt(Zw, ZLD, 0, OmT, TLD, 16 * j, CP / KS);
-      const int t = 16 * j + li;
-      if (t < C) {
-        const float upto = Dt[t / N + 1];   // P(0, f(t))
-        f32x4 ov;
+      for (int kb = 0; kb < CP / KS; ++kb) wf[kb] = fragA(Zw, ZLD, 0, kb * KS);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = upto * SQ[j][r] + acc[r];
-        const long off = (((long)b * L + tok0 + t) * a.H + h) * D + 16 * w + 4 * g;
-        if constexpr (BF) {
-          u32x2 pk;
-          pk[0] = (uint32_t)f32_to_bf16_bits(ov[0]) | ((uint32_t)f32_to_bf16_bits(ov[1]) << 16);
-          pk[1] = (uint32_t)f32_to_bf16_bits(ov[2]) | ((uint32_t)f32_to_bf16_bits(ov[3]) << 16);
-          *reinterpret_cast<u32x2*>(O + off) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(O + off) = ov;
+      for (int j = 0; j < NB; ++j) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < CP / KS; ++kb) acc = mma(wf[kb], fragA(OmT, TLD, 16 * j, kb * KS), acc);
+        const int t = 16 * j + li;
+        if (t < C) {
+          const float upto = vec[CP + t];
+          f32x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = upto * SQ[j][r] + acc[r];
+          const long off = (((long)b * L + tok0 + t) * a.H + h) * D + 16 * w + 4 * g;
+          if constexpr (BF) {
+            u32x2 pk;
+            pk[0] = (uint32_t)f32_to_bf16_bits(ov[0]) | ((uint32_t)f32_to_bf16_bits(ov[1]) << 16);
+            pk[1] = (uint32_t)f32_to_bf16_bits(ov[2]) | ((uint32_t)f32_to_bf16_bits(ov[3]) << 16);
+            *reinterpret_cast<u32x2*>(O + off) = pk;
+          } else {
+            *reinterpret_cast<f32x4*>(O + off) = ov;
+          }
         }
       }
     }
 
-    // 7. E_F = P(0, F-1) E_0 + (W tail) K^
-    const float total = Dt[nf];
+    // 5. E_F = P(0, F-1) E_0 + s (W tail) K
+    const float total = vec[4 * CP];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       f32x4 acc = zero4();
+#pragma unroll
       for (int kb = 0; kb < CP / KS; ++kb)
         acc = mma(fragA(Zw + CP, ZLD, 0, kb * KS), fragBn(Ks, KLD, kb * KS, 16 * n), acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Sreg[n][r] = total * Sreg[n][r] + s * acc[r];
     }
-    block_sync();
+    cur = nxt;
+    block_sync();   // every wave is done with this chunk's LDS inputs
   }
 
   if (a.zT) {
@@ -330,12 +501,22 @@ __global__ __launch_bounds__(64 * NT) void token_kernel(TokArgs a) {
   }
 }
 
+int64_t token_record_bytes(int io) {
+  const int cp = io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
+  const int es = io == IO_BF16 ? 2 : 4;
+  return (int64_t)2 * cp * cp * es + 5 * cp * 4;
+}
+
 template <int IO>
 static hipError_t launch_token_io(const TokArgs& a, int nt, hipStream_t s) {
-  const dim3 grid(a.B * a.H), block(64 * nt);
+  const dim3 pgrid(a.B * a.H * a.nck), pblock(256);
+  const dim3 sgrid(a.B * a.H), sblock(64 * nt);
   switch (nt) {
-#define GDN_TOK_CASE(n) \
-  case n: hipLaunchKernelGGL((token_kernel<IO, n>), grid, block, 0, s, a); break;
+#define GDN_TOK_CASE(n)                                                               \
+  case n:                                                                             \
+    hipLaunchKernelGGL((token_prep_kernel<IO, n>), pgrid, pblock, 0, s, a);           \
+    hipLaunchKernelGGL((token_scan_kernel<IO, n>), sgrid, sblock, 0, s, a);           \
+    break;
     GDN_TOK_CASE(1) GDN_TOK_CASE(2) GDN_TOK_CASE(3) GDN_TOK_CASE(4)
     GDN_TOK_CASE(5) GDN_TOK_CASE(6) GDN_TOK_CASE(7) GDN_TOK_CASE(8)
 #undef GDN_TOK_CASE
@@ -345,7 +526,9 @@ static hipError_t launch_token_io(const TokArgs& a, int nt, hipStream_t s) {
 }
 
 hipError_t launch_token(const TokArgs& a, int io, int nt, hipStream_t s) {
-  if (a.N < 1 || a.F < 1 || a.F * a.N > (io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP))
+  const int cp = io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
+  if (a.N < 1 || a.F < 1 || a.F * a.N > cp || a.nck != (a.T + a.F - 1) / a.F ||
+      a.rec_bytes != token_record_bytes(io) || !a.ws)
     return hipErrorInvalidValue;
   return io == IO_BF16 ? launch_token_io<IO_BF16>(a, nt, s) : launch_token_io<IO_F32>(a, nt, s);
 }

@@ -82,8 +82,10 @@ typedef enum { GDN_OP_FORWARD = 0, GDN_OP_STEP = 1, GDN_OP_BACKWARD = 2 } gdn_op
  *   GDN_ALGO_TOKEN  the token form: chunks of F = floor(64 / N) frames
  *                   (bf16; 32 / N for fp32) whose corrected values solve the
  *                   delta rule's unit triangular system over the chunk's
- *                   tokens; no D x D product per frame, no workspace.  For
- *                   frames of few tokens (token-wise GDN is N = 1).
+ *                   tokens; no D x D product per frame.  Its workspace
+ *                   holds each chunk's operators (17.25 KiB per chunk,
+ *                   head and batch in bf16).  For frames of few tokens
+ *                   (token-wise GDN is N = 1).
  *                   Requires N <= 64 (bf16) / 32 (fp32) and saved == NULL.
  *   GDN_ALGO_AUTO   currently the frame form.
  * gdn_backward always uses the frame form (recomputing A_t, S_t when no
@@ -131,8 +133,7 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
  *   state_out  S_T; NULL => not written; may equal state_in (in place).
  *   saved      NULL, or gdn_saved_size bytes that receive A_t and S_t for
  *              gdn_backward.
- *   workspace  gdn_workspace_size(p, GDN_OP_FORWARD) bytes of scratch (0
- *              for the token form, which then accepts workspace == NULL). */
+ *   workspace  gdn_workspace_size(p, GDN_OP_FORWARD) bytes of scratch. */
 gdn_status gdn_forward(const gdn_problem* p,
                        const void* q, const void* k, const void* v,
                        const float* gamma, const float* beta,

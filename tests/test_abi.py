@@ -124,19 +124,25 @@ def test_frame_larger_than_2gib_is_rejected(lib):
 def test_algorithm_field(lib):
     vp = ctypes.c_void_p
     p = gb.make_problem(1, 2, 4, 8, 32, "bf16", algorithm="token")
-    assert _ws(p, gb.GDN_OP_FORWARD) == (0, 0)          # the token form needs no workspace
+    # chunks of 64 / 8 = 8 frames: one chunk per (b, h), each a record of
+    # two 64 x 64 bf16 operators and 5 x 64 fp32 values
+    assert _ws(p, gb.GDN_OP_FORWARD) == (0, 2 * 1 * (2 * 64 * 64 * 2 + 5 * 64 * 4))
+    pf = gb.make_problem(2, 3, 10, 1, 32, "fp32", algorithm="token")   # 32 frames a chunk
+    assert _ws(pf, gb.GDN_OP_FORWARD) == (0, 6 * 1 * (2 * 32 * 32 * 4 + 5 * 32 * 4))
+    pl = gb.make_problem(1, 1, 130, 1, 32, "bf16", algorithm="token")  # 3 chunks
+    assert _ws(pl, gb.GDN_OP_FORWARD)[1] == 3 * (2 * 64 * 64 * 2 + 5 * 64 * 4)
     n = ctypes.c_size_t(0)
     assert gb.STATUS[lib.gdn_saved_size(ctypes.byref(p), ctypes.byref(n))] == "GDN_ERR_UNSUPPORTED"
     # the backward is the frame form whatever the forward's algorithm
     assert _ws(p, gb.GDN_OP_BACKWARD)[1] == _ws(gb.make_problem(1, 2, 4, 8, 32, "bf16"),
                                                 gb.GDN_OP_BACKWARD)[1]
     good = [vp(0x100000 * (i + 1)) for i in range(10)]
-    # no saved buffer in the token form; a NULL workspace is fine there
-    code = lib.gdn_forward(ctypes.byref(p), *good[:9], None, 0, None)
+    # no saved buffer in the token form
+    code = lib.gdn_forward(ctypes.byref(p), *good, 1 << 30, None)
     assert gb.STATUS[code] == "GDN_ERR_UNSUPPORTED"
     for io, nmax in (("bf16", 64), ("fp32", 32)):
         ok = gb.make_problem(1, 2, 3, nmax, 16, io, algorithm="token")
-        assert _ws(ok, gb.GDN_OP_FORWARD)[0] == 0
+        assert _ws(ok, gb.GDN_OP_FORWARD)[0] == 0   # one frame a chunk
         big = gb.make_problem(1, 2, 3, nmax + 1, 16, io, algorithm="token")
         assert gb.STATUS[_ws(big, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
         # the frame form takes any N
