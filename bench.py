@@ -8,7 +8,8 @@ line: tokens/s, the roofline of the dominant kernel (phase times from HIP
 events recorded by the library between its kernels, on the stream they run
 on), and the float64 CPU oracle timed on a bounded sample of the same
 workload.  Extras: forward + backward at the same shape, 121 streaming
-gdn_step calls, and chunk-causal streaming by windows of latent frames.
+gdn_step calls, chunk-causal streaming by windows of latent frames, and
+token-wise GDN (one token per frame) in the token form.
 """
 
 import argparse
@@ -186,6 +187,8 @@ def main():
         extra["stream"] = bench_stream(gb, d, B, H, D, T, N, ev)
         print("[bench] streaming windows", file=sys.stderr, flush=True)
         extra["windows"] = [bench_windows(gb, d, B, H, D, T, N, k) for k in (2, 8, 15)]
+        print("[bench] token-wise GDN (token form)", file=sys.stderr, flush=True)
+        extra["tokenwise"] = bench_tokenwise(gb, d, B, H, D, T * N)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -261,6 +264,36 @@ def bench_stream(gb, d, B, H, D, T, N, ev):
             "calls": T, "per_frame_ms_median": round(lat[T // 2], 4),
             "per_frame_ms_p90": round(lat[int(T * 0.9)], 4),
             "tokens_per_s": round(B * T * N / wall, 1)}
+
+
+def bench_tokenwise(gb, d, B, H, D, L):
+    """Token-wise GDN (one token per step, N = 1) over the same 106,480 tokens
+    per head, in the token form (chunks of 64 one-token frames); the frame
+    form is timed beside it on the first 8192 tokens (its per-frame D x D
+    intermediates for all 106,480 steps would take 160 GB)."""
+    import torch
+    dev = d["q"].device
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    gam = (0.9 + 0.1 * torch.rand((B, L, H), generator=gen)).to(dev)
+    out = {"workload": "token-wise GDN: %d one-token frames, %d heads, D=%d, bf16" % (L, H, D)}
+    for name, T, algo in (("token_form", L, "token"), ("token_form_8192", 8192, "token"),
+                          ("frame_form_8192", 8192, "frame")):
+        plan = gb.ForwardPlan(B, H, T, 1, D, "bf16", dev, algorithm=algo)
+        args = (d["q"][:, :T], d["k"][:, :T], d["v"][:, :T], gam[:, :T].contiguous(),
+                d["beta"][:, :T])
+        plan(*args)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            plan(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"tokens": B * T, "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1)}
+        del plan
+    return out
 
 
 def bench_windows(gb, d, B, H, D, T, N, k):

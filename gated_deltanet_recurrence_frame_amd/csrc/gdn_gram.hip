@@ -39,7 +39,7 @@
 
 namespace gdn {
 
-constexpr int GRAM_WPH = 4;   // waves per head: 4 x 64 threads share a head's row tiles
+constexpr int GRAM_WPH = 8;   // waves per head: 8 x 64 threads share a head's row tiles
 
 template <int IO, int NT, int NR, bool Y_IS_X0, int HPW>
 struct GramCfg {
