@@ -26,8 +26,10 @@
 
 namespace gdn {
 
+// bf16: registers kept to 128 so that two workgroups share a CU (4 waves per
+// SIMD; the LDS stages allow it), which hides more of the per-chunk chain.
 template <int IO, int NT, bool TRANS, int HPW>
-__global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
+__global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(OutArgs a) {
   typedef typename Io<IO>::elem E;
   constexpr bool BF = (IO == IO_BF16);
   constexpr int D = 16 * NT;
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(64 * NT) void output_kernel(OutArgs a) {
   constexpr int PR = RW * ES / 16;               // 16-byte pieces per row segment
   constexpr int NTH = 64 * NT;
   constexpr int PPT = CT * PR / NTH;             // pieces per thread per chunk (2)
-  constexpr int PF = 4;                          // chunks in flight
+  constexpr int PF = 3;                          // chunks in flight
   static_assert(PPT * NTH == CT * PR, "pieces must split evenly over the threads");
   // contraction blocks: bf16 32-deep (the last one zero past D), fp32 4-deep
   constexpr int KF = BF ? (D + 31) / 32 : D / 4;
