@@ -114,9 +114,22 @@ int64_t scratch_bytes(const Shape& s) {
 int64_t token_frames(const Shape& s) {
   return (s.io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP) / s.N;
 }
-int64_t token_ws(const Shape& s) {
+int64_t token_chunks(const Shape& s) {
   const int64_t F = token_frames(s);
-  return s.B * s.H * ((s.T + F - 1) / F) * token_record_bytes(s.io);
+  return (s.T + F - 1) / F;
+}
+// Segments walked in parallel: about 128 (b, h, segment) items (two walks
+// each in the composite pass), at least 8 chunks per segment.
+int64_t token_segments(const Shape& s) {
+  int64_t n = 128 / (s.B * s.H);
+  const int64_t most = token_chunks(s) / 8;
+  if (n > most) n = most;
+  return n < 1 ? 1 : n;
+}
+int64_t token_ws(const Shape& s) {
+  const int64_t seg = token_segments(s);
+  const int64_t comp = seg > 1 ? 3 * s.B * s.H * seg * s.D * s.D * 4 : 0;
+  return s.B * s.H * token_chunks(s) * token_record_bytes(s.io) + comp;
 }
 int64_t forward_ws(const Shape& s) { return s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s); }
 int64_t backward_ws(const Shape& s) { return 6 * s.mat + scratch_bytes(s); }
@@ -200,16 +213,48 @@ gdn_status run_token(const Shape& s, const void* q, const void* k, const void* v
   ta.z0 = state_in; ta.o = o; ta.zT = state_out; ta.s = s.s;
   ta.B = (int)s.B; ta.H = (int)s.H; ta.T = (int)s.T; ta.N = (int)s.N;
   ta.F = (int)token_frames(s);
-  ta.nck = (int)((s.T + ta.F - 1) / ta.F);
+  ta.nck = (int)token_chunks(s);
   ta.ws = workspace;
   ta.rec_bytes = token_record_bytes(s.io);
+  const int nt = (int)(s.D / 16);
+  const int nseg = (int)token_segments(s);
+  ta.nseg = nseg;
+  ta.cps = (ta.nck + nseg - 1) / nseg;
+  ta.nseg = (ta.nck + ta.cps - 1) / ta.cps;   // no empty segment
   gdn_status st = GDN_OK;
   for (int i = 0; i < 3 && st == GDN_OK; ++i) st = record(events, i, stream);
   if (st != GDN_OK) return st;
-  st = hip_status(launch_token(ta, s.io, (int)(s.D / 16), stream));
+  if (ta.nseg == 1) {
+    ta.mode = TOK_PLAIN;
+    st = hip_status(launch_token(ta, s.io, nt, true, stream));
+    if (st != GDN_OK) return st;
+    return record(events, 3, stream);
+  }
+  // composites of every segment, the fold, then the replay of every segment
+  const int64_t cm = s.B * s.H * ta.nseg * s.D * s.D;   // floats per buffer
+  float* comp = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         s.B * s.H * ta.nck * ta.rec_bytes);
+  ta.compH = comp;
+  ta.compC = comp + cm;
+  float* zmid = comp + 2 * cm;
+  ta.mode = TOK_COMPOSITE;
+  st = hip_status(launch_token(ta, s.io, nt, true, stream));
+  if (st != GDN_OK) return st;
+  ScanArgs fa{};
+  fa.A = ta.compC; fa.U = ta.compH; fa.gamma = nullptr; fa.z0 = state_in;
+  fa.emit = zmid + s.D * s.D;   // slot p + 1 receives the state after segment p
+  fa.emit_entry = 1;            // slot 0 receives z0 itself
+  fa.B = (int)s.B; fa.H = (int)s.H; fa.T = ta.nseg;
+  fa.t0 = 0; fa.Tc = ta.nseg - 1;
+  st = hip_status(launch_scan(fa, IO_F32, nt, SCAN_FWD, stream));
+  if (st != GDN_OK) return st;
+  ta.mode = TOK_REPLAY;
+  ta.zin = zmid;
+  st = hip_status(launch_token(ta, s.io, nt, false, stream));
   if (st != GDN_OK) return st;
   return record(events, 3, stream);
 }
+
 
 // Forward pipeline shared by gdn_forward and gdn_step.
 

@@ -136,8 +136,16 @@ struct TokArgs {
   int nck;              // chunks per sequence, ceil(T / F)
   void* ws;             // B H nck records of token_record_bytes(io) bytes
   int64_t rec_bytes;
+  // Segments: nseg segments of cps chunks (the last may be shorter).
+  int mode;             // TOK_PLAIN (nseg == 1), TOK_COMPOSITE, TOK_REPLAY
+  int nseg, cps;
+  float* compH;         // composite pass: [B, H, nseg] x D x D fp32, MFMA tile order
+  float* compC;         // composite pass: -Phi^T, row-major
+  const float* zin;     // replay: entering states [B, H, nseg] x D x D fp32
 };
+enum TokMode { TOK_PLAIN = 0, TOK_COMPOSITE = 1, TOK_REPLAY = 2 };
 int64_t token_record_bytes(int io);
-hipError_t launch_token(const TokArgs& a, int io, int nt, hipStream_t s);
+// prep: also run the per-chunk operator kernel first
+hipError_t launch_token(const TokArgs& a, int io, int nt, bool prep, hipStream_t s);
 
 }  // namespace gdn

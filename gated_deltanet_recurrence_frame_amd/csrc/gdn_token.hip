@@ -24,7 +24,13 @@
 // what depends on the state, chunk after chunk:
 //   SK = E_0 K^T, SQ = E_0 Q^T, R, W = R (I + L)^-1, O = P(0, f) SQ + W Om,
 //   E_F = P(0, F-1) E_0 + s (W tail) K,
-// with the next chunk's inputs in flight in a register ring.
+// with the next chunk's inputs in flight in a register ring.  Long
+// sequences are cut into segments of chunks walked in parallel: a composite
+// pass per segment (the input composite H from a zero state, the transition
+// composite Phi from the identity without inputs - [RB] 技术新颖性 point 1's
+// context-parallel composites, with segments in place of devices), the
+// frame form's fold of the composites, and a replay of every segment from
+// its entering state.
 // bf16 io: bf16 MFMA 16x16x32 with fp32 accumulation, the state and W
 // rounded to bf16 as MFMA operands (as in the frame form's scan); fp32 io:
 // fp32 MFMA 16x16x4 throughout.
@@ -258,10 +264,19 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
   __shared__ __attribute__((aligned(16))) float vec[VEC];
   __shared__ __attribute__((aligned(16))) E Zs[NT][16 * ZLD];
 
-  const int bh = blockIdx.x;
+  // Work item: (b, h) with a.nseg == 1; else (b, h, segment) and, in the
+  // composite pass, which of the two walks (input composite H from zero
+  // with V, transition composite Phi from the identity without V).
+  const int nwalk = a.mode == TOK_COMPOSITE ? 2 : 1;
+  const int walk = blockIdx.x % nwalk;
+  const int seg = (blockIdx.x / nwalk) % a.nseg;
+  const int bh = blockIdx.x / nwalk / a.nseg;
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
   const int lane = lane_id(), w = wave_id();
+  const bool phi = walk == 1;               // the transition walk: no inputs, no outputs
+  const int ck_beg = seg * a.cps;
+  const int ck_end = min(a.nck, ck_beg + a.cps);
   const int g = lane >> 4, li = lane & 15;
   const int N = a.N, T = a.T;
   const long L = (long)T * N;
@@ -304,6 +319,7 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
     const int Cn = min(a.F, T - t0) * N;
     const long tok0 = (long)t0 * N;
     const char* rec = static_cast<const char*>(a.ws) + ((long)bh * a.nck + ck) * a.rec_bytes;
+    const bool with_v = !phi;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int p = tid + NTH * j;
@@ -321,7 +337,7 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
     for (int j = 0; j < NB; ++j) {
       const int t = 16 * j + li;
       P.v[j] = VP{};
-      if (t < Cn)
+      if (with_v && t < Cn)
         P.v[j] = *reinterpret_cast<const VP*>(V + (((long)b * L + tok0 + t) * a.H + h) * D +
                                                16 * w + 4 * g);
     }
@@ -343,15 +359,17 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
   };
 
   // the state: wave w holds rows 16 w .. 16 w + 15, tile n in Sreg[n]
+  // Entering state: the initial state (one segment), the fold's entering
+  // state of the segment (replay), zero (H walk) or the identity (Phi walk).
+  const float* zs = a.mode == TOK_REPLAY ? a.zin + ((long)bh * a.nseg + seg) * D * D
+                  : a.mode == TOK_PLAIN && a.z0 ? a.z0 + (long)bh * D * D : nullptr;
   f32x4 Sreg[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    Sreg[n] = zero4();
-    if (a.z0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Sreg[n][r] = a.z0[((long)bh * D + 16 * w + 4 * g + r) * D + 16 * n + li];
-    }
+    for (int r = 0; r < 4; ++r)
+      Sreg[n][r] = zs ? zs[(16 * w + 4 * g + r) * D + 16 * n + li]
+                      : (phi && 16 * w + 4 * g + r == 16 * n + li ? 1.f : 0.f);
   }
   // feature padding of K and Q rows: zero once, never written again
   if constexpr (DP > D) {
@@ -363,8 +381,8 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
   }
 
   Pre cur, nxt;
-  prefetch(cur, 0);
-  for (int ck = 0; ck < a.nck; ++ck) {
+  prefetch(cur, ck_beg);
+  for (int ck = ck_beg; ck < ck_end; ++ck) {
     const int t0 = ck * a.F;
     const int C = min(a.F, T - t0) * N;
     const long tok0 = (long)t0 * N;
@@ -380,7 +398,7 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Zw[(4 * g + r) * ZLD + D + li] = toE(0.f);
     }
-    if (ck + 1 < a.nck) prefetch(nxt, ck + 1);
+    if (ck + 1 < ck_end) prefetch(nxt, ck + 1);
     block_sync();
 
     // 2. SK = E_0 K^T, SQ = E_0 Q^T (the staged rows are the A operand of all)
@@ -459,7 +477,7 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
 #pragma unroll
         for (int kb = 0; kb < CP / KS; ++kb) acc = mma(wf[kb], fragA(OmT, TLD, 16 * j, kb * KS), acc);
         const int t = 16 * j + li;
-        if (t < C) {
+        if (!phi && a.mode != TOK_COMPOSITE && t < C) {
           const float upto = vec[CP + t];
           f32x4 ov;
 #pragma unroll
@@ -492,7 +510,18 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
     block_sync();   // every wave is done with this chunk's LDS inputs
   }
 
-  if (a.zT) {
+  if (a.mode == TOK_COMPOSITE) {
+    // H in the MFMA tile order, -Phi^T row-major: the layouts the frame
+    // form's fold reads its composites in
+    const long base = ((long)bh * a.nseg + seg) * D * D;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (!phi)
+        *reinterpret_cast<f32x4*>(a.compH + base + ((w * NT + n) * 64 + lane) * 4) = Sreg[n];
+      else
+        *reinterpret_cast<f32x4*>(a.compC + base + (16 * n + li) * D + 16 * w + 4 * g) = -Sreg[n];
+    }
+  } else if (a.zT && seg == a.nseg - 1) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -508,13 +537,13 @@ int64_t token_record_bytes(int io) {
 }
 
 template <int IO>
-static hipError_t launch_token_io(const TokArgs& a, int nt, hipStream_t s) {
+static hipError_t launch_token_io(const TokArgs& a, int nt, bool prep, hipStream_t s) {
   const dim3 pgrid(a.B * a.H * a.nck), pblock(256);
-  const dim3 sgrid(a.B * a.H), sblock(64 * nt);
+  const dim3 sgrid(a.B * a.H * a.nseg * (a.mode == TOK_COMPOSITE ? 2 : 1)), sblock(64 * nt);
   switch (nt) {
 #define GDN_TOK_CASE(n)                                                               \
   case n:                                                                             \
-    hipLaunchKernelGGL((token_prep_kernel<IO, n>), pgrid, pblock, 0, s, a);           \
+    if (prep) hipLaunchKernelGGL((token_prep_kernel<IO, n>), pgrid, pblock, 0, s, a); \
     hipLaunchKernelGGL((token_scan_kernel<IO, n>), sgrid, sblock, 0, s, a);           \
     break;
     GDN_TOK_CASE(1) GDN_TOK_CASE(2) GDN_TOK_CASE(3) GDN_TOK_CASE(4)
@@ -525,12 +554,16 @@ static hipError_t launch_token_io(const TokArgs& a, int nt, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_token(const TokArgs& a, int io, int nt, hipStream_t s) {
+hipError_t launch_token(const TokArgs& a, int io, int nt, bool prep, hipStream_t s) {
   const int cp = io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
   if (a.N < 1 || a.F < 1 || a.F * a.N > cp || a.nck != (a.T + a.F - 1) / a.F ||
-      a.rec_bytes != token_record_bytes(io) || !a.ws)
+      a.rec_bytes != token_record_bytes(io) || !a.ws || a.nseg < 1 || a.cps < 1 ||
+      (long)a.nseg * a.cps < a.nck || (long)(a.nseg - 1) * a.cps >= a.nck ||
+      (a.mode == TOK_COMPOSITE && (!a.compH || !a.compC)) || (a.mode == TOK_REPLAY && !a.zin) ||
+      (a.mode == TOK_PLAIN && a.nseg != 1))
     return hipErrorInvalidValue;
-  return io == IO_BF16 ? launch_token_io<IO_BF16>(a, nt, s) : launch_token_io<IO_F32>(a, nt, s);
+  return io == IO_BF16 ? launch_token_io<IO_BF16>(a, nt, prep, s)
+                       : launch_token_io<IO_F32>(a, nt, prep, s);
 }
 
 }  // namespace gdn

@@ -271,6 +271,17 @@ def test_token_form_matches_oracle(io, N, T, D):
     check_forward(inp, N, io, with_state=True, algorithm="token")
 
 
+@pytest.mark.parametrize("io,N,T,D", [("bf16", 1, 2000, 32), ("fp32", 1, 1000, 32),
+                                      ("bf16", 3, 700, 48), ("bf16", 1, 1500, 112),
+                                      ("fp32", 2, 600, 16)])
+def test_token_form_segments(io, N, T, D):
+    # long sequences: segments of chunks walked in parallel (composites, the
+    # fold, a replay), with a carried state and a ragged last segment
+    inp = gin.make_inputs(B=1, H=2, T=T, N=N, D=D, io=io, gamma="sigmoid", seed=70 + N,
+                          with_state=True)
+    check_forward(inp, N, io, with_state=True, algorithm="token")
+
+
 @pytest.mark.parametrize("N", [33, 64])
 def test_token_form_long_frames_bf16(N):
     # frames longer than half a chunk: one frame per chunk (fp32 stops at 32)
@@ -279,9 +290,10 @@ def test_token_form_long_frames_bf16(N):
     check_forward(inp, N, "bf16", with_state=True, algorithm="token")
 
 
-@pytest.mark.parametrize("io", ["fp32", "bf16"])
-def test_token_form_equals_frame_form_in_place(io):
-    B, H, T, N, D = 1, 4, 40, 4, 112
+@pytest.mark.parametrize("io,T", [("fp32", 40), ("bf16", 40), ("bf16", 700)])
+def test_token_form_equals_frame_form_in_place(io, T):
+    # T = 700 four-token frames: 44 chunks in 4 segments, state in place
+    B, H, N, D = 1, 4, 4, 112
     inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=60,
                           with_state=True)
     d = {k: to_dev(v) for k, v in inp.items()}
