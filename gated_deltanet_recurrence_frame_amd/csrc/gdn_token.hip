@@ -62,21 +62,19 @@ struct TokLayout {
 };
 
 // ---------------------------------------------------------------------------
-// Per-chunk operators, one workgroup of 4 waves per (b, h, chunk).  Record
+// Per-chunk operators, one workgroup of 8 waves per (b, h, chunk).  Record
 // (b, h, chunk) of the workspace: TiT[t][u] = (I + L)^-1[u][t], OmT[t][u] =
 // Om[u][t] (CP x CP each, io type), then 5 x CP floats: P(0, f(t) - 1),
 // P(0, f(t)), P(f(t) + 1, F - 1), beta_t, and P(0, F - 1) first in the last.
 template <int IO, int NT>
-__global__ __launch_bounds__(256) void token_prep_kernel(TokArgs a) {
+__global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
   typedef TokLayout<IO, NT> Y;
   typedef typename Y::E E;
   constexpr bool BF = Y::BF;
-  constexpr int D = Y::D, CP = Y::CP, NB = Y::NB, KS = Y::KS, DP = Y::DP, KLD = Y::KLD;
-  constexpr int FLD = Y::FLD, DLD = Y::DLD, EP = Y::EP;
-  constexpr int NW = 4, NTH = 256;
+  constexpr int D = Y::D, CP = Y::CP, NB = Y::NB, KS = Y::KS, DP = Y::DP;
+  constexpr int FLD = Y::FLD, DLD = Y::DLD;
+  constexpr int NW = 8, NTH = 512;
 
-  __shared__ __attribute__((aligned(16))) E Ks[CP * KLD];
-  __shared__ __attribute__((aligned(16))) E Qs[CP * KLD];
   __shared__ float KKs[CP * FLD];      // K^ K^^T, then L in place
   __shared__ float KQs[CP * FLD];      // K Q^T, then (I + L)^-1
   __shared__ float Dt[(CP + 1) * DLD];  // Dt[x][c] = P(x, c - 1)
@@ -117,18 +115,7 @@ __global__ __launch_bounds__(256) void token_prep_kernel(TokArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // 1. the chunk's K and Q rows (zero past C and in the feature padding), gates
-  for (int p = tid; p < CP * (DP / EP); p += NTH) {
-    const int u = p / (DP / EP), c = (p % (DP / EP)) * EP;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
-    if (u < C && c < D) {
-      const long off = (((long)b * L + tok0 + u) * a.H + h) * D + c;
-      kv = *reinterpret_cast<const u32x4*>(K + off);
-      qv = *reinterpret_cast<const u32x4*>(Q + off);
-    }
-    *reinterpret_cast<u32x4*>(&Ks[u * KLD + c]) = kv;
-    *reinterpret_cast<u32x4*>(&Qs[u * KLD + c]) = qv;
-  }
+  // 1. the chunk's gates
   if (tid < CP) {
     gs[tid] = tid < nf ? a.gamma[((long)b * T + t0 + tid) * a.H + h] : 0.f;
     bs[tid] = tid < C ? a.beta[((long)b * L + tok0 + tid) * a.H + h] : 0.f;
@@ -136,18 +123,37 @@ __global__ __launch_bounds__(256) void token_prep_kernel(TokArgs a) {
   }
   block_sync();
 
-  // 2. decay table (a thread per row); K^ K^^T on blocks i <= j and K Q^T
+  // 2. decay table: thread x runs the product over the chunk's gates, all
+  // of them first read into registers; K^ K^^T on blocks i <= j and K Q^T,
+  // their fragments read straight from the token rows (zero past C and D)
   for (int x = tid; x <= nf; x += NTH) {
+    float gv[CP];
+#pragma unroll
+    for (int c = 0; c < CP; ++c) gv[c] = gs[c];
     float p = 1.f;
     Dt[x * DLD + x] = 1.f;
-    for (int c = x + 1; c <= nf; ++c) {
-      p *= gs[c - 1];
-      Dt[x * DLD + c] = p;
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
+      const bool in = c >= x && c < nf;
+      p = in ? p * gv[c] : p;
+      if (in) Dt[x * DLD + c + 1] = p;
     }
   }
+  auto gfrag = [&](const E* M, int u, int kb) {   // row u of the chunk, k block kb
+    const int k = kb * KS + (BF ? 8 * g : g);
+    const bool ok = u < C && k < D;
+    const long off = (((long)b * L + tok0 + (ok ? u : 0)) * a.H + h) * D + (ok ? k : 0);
+    if constexpr (BF) return ok ? load_bf16x8(M + off) : zero_bf16x8();
+    else return ok ? M[off] : 0.f;
+  };
   {
     constexpr int NP = NB * (NB + 1) / 2;
-    for (int q = w; q < NP + NB * NB; q += NW) {
+    // a fixed trip count, so the loads of consecutive tiles overlap
+    constexpr int TRIPS = (NP + NB * NB + NW - 1) / NW;
+#pragma unroll 2
+    for (int it = 0; it < TRIPS; ++it) {
+      const int q = w + NW * it;
+      if (q >= NP + NB * NB) break;
       int i, j;
       const bool kq = q >= NP;
       if (kq) {
@@ -157,10 +163,10 @@ __global__ __launch_bounds__(256) void token_prep_kernel(TokArgs a) {
         while (rem >= NB - i) { rem -= NB - i; ++i; }
         j = i + rem;
       }
-      const E* Bm = kq ? Qs : Ks;
+      const E* Bm = kq ? Q : K;
       f32x4 acc = zero4();
       for (int kb = 0; kb < DP / KS; ++kb)
-        acc = mma(fragA(Ks, KLD, 16 * i, kb * KS), fragA(Bm, KLD, 16 * j, kb * KS), acc);
+        acc = mma(gfrag(K, 16 * i + li, kb), gfrag(Bm, 16 * j + li, kb), acc);
       float* dst = kq ? KQs : KKs;
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * FLD + 16 * j + li] = acc[r];
@@ -538,7 +544,7 @@ int64_t token_record_bytes(int io) {
 
 template <int IO>
 static hipError_t launch_token_io(const TokArgs& a, int nt, bool prep, hipStream_t s) {
-  const dim3 pgrid(a.B * a.H * a.nck), pblock(256);
+  const dim3 pgrid(a.B * a.H * a.nck), pblock(512);
   const dim3 sgrid(a.B * a.H * a.nseg * (a.mode == TOK_COMPOSITE ? 2 : 1)), sblock(64 * nt);
   switch (nt) {
 #define GDN_TOK_CASE(n)                                                               \
