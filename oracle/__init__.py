@@ -10,6 +10,8 @@ from .gdn_oracle import (  # noqa: F401
     default_key_scale,
     forward,
     frame_terms,
+    prologue,
+    prologue_backward,
     step,
     tokenspace_forward,
 )

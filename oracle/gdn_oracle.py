@@ -60,6 +60,8 @@ __all__ = [
     "backward",
     "composite_forward",
     "tokenspace_forward",
+    "prologue",
+    "prologue_backward",
 ]
 
 
@@ -115,8 +117,54 @@ def frame_terms(k, v, beta, n, key_scale=0.0):
     return A, U
 
 
+def prologue(q, k, gamma, beta, normalize_qk=False, gate_logits=False):
+    """Optional prologue of the GDN block, applied before the recurrence.
+
+    The hats on Q^ and K^ (summary page, 方法步骤详情 module 2) are read as
+    per-token normalisation; with ``normalize_qk`` every query and key row
+    (one token, one head) is divided by its L2 norm over the head dimension
+    (the key scale is applied afterwards, as without the prologue).  With
+    ``gate_logits`` gamma and beta arrive as logits and become sigmoid(x),
+    the (0, 1) gates the recurrence uses.  Returns (q, k, gamma, beta).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    if normalize_qk:
+        q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+        k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    if gate_logits:
+        gamma = 1.0 / (1.0 + np.exp(-gamma))
+        beta = 1.0 / (1.0 + np.exp(-beta))
+    return q, k, gamma, beta
+
+
+def prologue_backward(q, k, gamma, beta, dq, dk, dgamma, dbeta, normalize_qk=False,
+                      gate_logits=False):
+    """Chain rule through ``prologue``: gradients with respect to the raw
+    inputs from those with respect to the prologue's outputs.  For
+    x^ = x / |x|: dx = (dx^ - x^ (x^ . dx^)) / |x|; for p = sigmoid(z):
+    dz = dp p (1 - p).  Returns (dq, dk, dgamma, dbeta)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if normalize_qk:
+        out = []
+        for x, dx in ((q, dq), (k, dk)):
+            nrm = np.linalg.norm(x, axis=-1, keepdims=True)
+            xh = x / nrm
+            out.append((dx - xh * np.sum(xh * dx, axis=-1, keepdims=True)) / nrm)
+        dq, dk = out
+    if gate_logits:
+        pg = 1.0 / (1.0 + np.exp(-np.asarray(gamma, dtype=np.float64)))
+        pb = 1.0 / (1.0 + np.exp(-np.asarray(beta, dtype=np.float64)))
+        dgamma = dgamma * pg * (1.0 - pg)
+        dbeta = dbeta * pb * (1.0 - pb)
+    return dq, dk, dgamma, dbeta
+
+
 def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, erase=1.0,
-            keep=False):
+            keep=False, normalize_qk=False, gate_logits=False):
     """Whole-sequence frame-wise GDN.
 
     For every (batch, head), in frame order t = 1..T:
@@ -129,7 +177,10 @@ def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, erase=1.0,
 
     Returns (o [B, L, H, Dv], state_out [B, H, Dv, Dk]); with keep=True also a
     dict of the per-frame intermediates A_t, U_t, S_t ([B, H, T, D, D]).
+    ``normalize_qk`` / ``gate_logits`` run ``prologue`` first.
     """
+    if normalize_qk or gate_logits:
+        q, k, gamma, beta = prologue(q, k, gamma, beta, normalize_qk, gate_logits)
     B, L, H, Dk, Dv, T = _shapes(q, k, v, gamma, beta, n)
     s = _scale(key_scale, Dk, n)
     o = np.zeros((B, L, H, Dv))
@@ -162,7 +213,7 @@ def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, erase=1.0,
     return o, state_out
 
 
-def step(q, k, v, gamma, beta, state, key_scale=0.0):
+def step(q, k, v, gamma, beta, state, key_scale=0.0, normalize_qk=False, gate_logits=False):
     """Streaming step: advance the carried state by one latent frame.
 
     The autoregressive / streaming variant carries the GDN state across calls
@@ -171,11 +222,12 @@ def step(q, k, v, gamma, beta, state, key_scale=0.0):
     [B, N, H, D], gamma [B, 1, H], beta [B, N, H].  Returns (o, new_state).
     """
     n = k.shape[1]
-    return forward(q, k, v, gamma, beta, n, state_in=state, key_scale=key_scale)
+    return forward(q, k, v, gamma, beta, n, state_in=state, key_scale=key_scale,
+                   normalize_qk=normalize_qk, gate_logits=gate_logits)
 
 
 def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None,
-             key_scale=0.0, erase=1.0):
+             key_scale=0.0, erase=1.0, normalize_qk=False, gate_logits=False):
     """Reverse-mode gradients of ``forward`` (the pages give no backward; this
     is the chain rule applied to the module-2 recurrence, step by step).
 
@@ -190,8 +242,18 @@ def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None,
         dK_t     = s dK^_t              (K^ = s K)
         dS_0     = G_1 M_1^T
     Returns dict with dq, dk, dv ([B, L, H, D]), dgamma [B, T, H],
-    dbeta [B, L, H], dstate_in [B, H, Dv, Dk].
+    dbeta [B, L, H], dstate_in [B, H, Dv, Dk].  With ``normalize_qk`` /
+    ``gate_logits`` the gradients are with respect to the raw inputs of
+    ``prologue`` (``prologue_backward``).
     """
+    if normalize_qk or gate_logits:
+        qp, kp, gp, bp = prologue(q, k, gamma, beta, normalize_qk, gate_logits)
+        gr = backward(qp, kp, v, gp, bp, n, d_o, state_in=state_in, d_state_out=d_state_out,
+                      key_scale=key_scale, erase=erase)
+        gr["dq"], gr["dk"], gr["dgamma"], gr["dbeta"] = prologue_backward(
+            q, k, gamma, beta, gr["dq"], gr["dk"], gr["dgamma"], gr["dbeta"], normalize_qk,
+            gate_logits)
+        return gr
     B, L, H, Dk, Dv, T = _shapes(q, k, v, gamma, beta, n)
     s = _scale(key_scale, Dk, n)
     dq = np.zeros((B, L, H, Dk))

@@ -512,3 +512,97 @@ def test_p13_pins_catch_planted_mistakes(kind):
     assert np.max(np.abs(ok - ref)) < 1e-11
     mut = _tokenspace_mutant(kind, q, k, v, g, beta, 2, 3, s0, s)
     assert np.max(np.abs(mut - ref)) > 1e-6
+
+
+# --------------------------------------------------------------------------
+# P14: the optional prologue (normalised queries and keys, gates as
+# logits).  Invariance under positive row scaling, the logit closed form,
+# idempotence on normalised inputs, and finite differences of the whole
+# block (prologue + recurrence) against the oracle's chained backward.
+# --------------------------------------------------------------------------
+def test_p14_normalisation_invariant_to_row_scaling():
+    q, k, v, g, beta, s0 = _rand_problem(1, 2, 4, 3, 5, seed=40)
+    rng = np.random.default_rng(41)
+    cq = rng.uniform(0.2, 5.0, q.shape[:3] + (1,))
+    ck = rng.uniform(0.2, 5.0, k.shape[:3] + (1,))
+    o1, s1 = oracle.forward(q, k, v, g, beta, 3, state_in=s0, key_scale=0.4, normalize_qk=True)
+    o2, s2 = oracle.forward(q * cq, k * ck, v, g, beta, 3, state_in=s0, key_scale=0.4,
+                            normalize_qk=True)
+    assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(s1 - s2)) < 1e-12
+    # and it is not the identity on raw inputs
+    o3, _ = oracle.forward(q, k, v, g, beta, 3, state_in=s0, key_scale=0.4)
+    assert np.max(np.abs(o1 - o3)) > 1e-3
+
+
+def test_p14_normalisation_idempotent_and_logit_closed_form():
+    q, k, v, g, beta, s0 = _rand_problem(1, 2, 5, 2, 4, seed=42)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o1, s1 = oracle.forward(qn, kn, v, g, beta, 2, state_in=s0, normalize_qk=True)
+    o2, s2 = oracle.forward(qn, kn, v, g, beta, 2, state_in=s0)
+    assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(s1 - s2)) < 1e-12
+    # logits z = log(p / (1 - p)) give exactly the gates p
+    zg, zb = np.log(g / (1 - g)), np.log(beta / (1 - beta))
+    o3, s3 = oracle.forward(q, k, v, zg, zb, 2, state_in=s0, gate_logits=True)
+    o4, s4 = oracle.forward(q, k, v, g, beta, 2, state_in=s0)
+    assert np.max(np.abs(o3 - o4)) < 1e-12 and np.max(np.abs(s3 - s4)) < 1e-12
+
+
+def _loss_pro(args, d_o, d_st, n, s, nq, gl):
+    q, k, v, g, beta, s0 = args
+    o, st = oracle.forward(q, k, v, g, beta, n, state_in=s0, key_scale=s, normalize_qk=nq,
+                           gate_logits=gl)
+    return np.sum(o * d_o) + np.sum(st * d_st)
+
+
+@pytest.mark.parametrize("nq,gl", [(True, False), (False, True), (True, True)])
+def test_p14_finite_differences_through_prologue(nq, gl):
+    B, H, T, N, D = 1, 2, 3, 2, 4
+    args = list(_rand_problem(B, H, T, N, D, seed=43))
+    if gl:
+        rng0 = np.random.default_rng(44)
+        args[3] = rng0.normal(2.0, 1.0, args[3].shape)      # gate logits
+        args[4] = rng0.normal(0.0, 1.0, args[4].shape)
+    rng = np.random.default_rng(45)
+    d_o = rng.standard_normal(args[2].shape)
+    d_st = rng.standard_normal(args[5].shape)
+    s = 0.45
+    gr = oracle.backward(*args[:5], N, d_o, state_in=args[5], d_state_out=d_st, key_scale=s,
+                         normalize_qk=nq, gate_logits=gl)
+    names = ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]
+    h = 1e-6
+    for i, name in enumerate(names):
+        for _ in range(3):
+            dirn = rng.standard_normal(args[i].shape)
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[i] += h * dirn
+            minus[i] -= h * dirn
+            fd = (_loss_pro(plus, d_o, d_st, N, s, nq, gl) -
+                  _loss_pro(minus, d_o, d_st, N, s, nq, gl)) / (2 * h)
+            an = np.sum(gr[name] * dirn)
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_p14_finite_differences_catch_a_dropped_projection():
+    # planted mistake: the normalisation's backward without its projection
+    # term, dx = dx^ / |x|; the directional derivative must disagree
+    B, H, T, N, D = 1, 1, 3, 2, 4
+    args = list(_rand_problem(B, H, T, N, D, seed=46))
+    rng = np.random.default_rng(47)
+    d_o = rng.standard_normal(args[2].shape)
+    d_st = rng.standard_normal(args[5].shape)
+    s = 0.45
+    qp, kp, gp, bp = oracle.prologue(args[0], args[1], args[3], args[4], True, False)
+    gr = oracle.backward(qp, kp, args[2], gp, bp, N, d_o, state_in=args[5], d_state_out=d_st,
+                         key_scale=s)
+    wrong_dk = gr["dk"] / np.linalg.norm(args[1], axis=-1, keepdims=True)
+    h = 1e-6
+    dirn = rng.standard_normal(args[1].shape)
+    plus = [a.copy() for a in args]
+    minus = [a.copy() for a in args]
+    plus[1] += h * dirn
+    minus[1] -= h * dirn
+    fd = (_loss_pro(plus, d_o, d_st, N, s, True, False) -
+          _loss_pro(minus, d_o, d_st, N, s, True, False)) / (2 * h)
+    assert abs(fd - np.sum(wrong_dk * dirn)) > 1e-4 * max(1.0, abs(fd))
