@@ -25,14 +25,15 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
           7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIASING"}
 
 
-ABI_VERSION = 2   # GDN_ABI_VERSION of include/gdn.h that GdnProblem mirrors
+ABI_VERSION = 3   # GDN_ABI_VERSION of include/gdn.h that GdnProblem mirrors
 
 
 class GdnProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("key_scale", ctypes.c_float),
-                ("scan_chunk", ctypes.c_int32), ("algorithm", ctypes.c_int32)]
+                ("scan_chunk", ctypes.c_int32), ("algorithm", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -108,12 +109,20 @@ def _stream(dev):
 
 
 ALGORITHMS = {"auto": 0, "frame": 1, "token": 2}
+GDN_FLAG_NORMALIZE_QK, GDN_FLAG_GATE_LOGITS = 1, 2
 
 
-def make_problem(B, H, T, N, D, io="bf16", key_scale=0.0, scan_chunk=0, algorithm="auto"):
+def flags_of(normalize_qk=False, gate_logits=False):
+    return ((GDN_FLAG_NORMALIZE_QK if normalize_qk else 0) |
+            (GDN_FLAG_GATE_LOGITS if gate_logits else 0))
+
+
+def make_problem(B, H, T, N, D, io="bf16", key_scale=0.0, scan_chunk=0, algorithm="auto",
+                 flags=0):
+    """gdn_problem; `flags` is an OR of GDN_FLAG_* (see flags_of)."""
     return GdnProblem(int(B), int(H), int(T), int(N), int(D), int(D),
                       GDN_BF16 if io == "bf16" else GDN_FP32, float(key_scale),
-                      int(scan_chunk), ALGORITHMS[algorithm])
+                      int(scan_chunk), ALGORITHMS[algorithm], int(flags))
 
 
 def workspace_size(prob, op):
@@ -172,8 +181,8 @@ class ForwardPlan:
     timed region)."""
 
     def __init__(self, B, H, T, N, D, io, device, key_scale=0.0, scan_chunk=0, saved=False,
-                 algorithm="auto"):
-        self.prob = make_problem(B, H, T, N, D, io, key_scale, scan_chunk, algorithm)
+                 algorithm="auto", flags=0):
+        self.prob = make_problem(B, H, T, N, D, io, key_scale, scan_chunk, algorithm, flags)
         dt = torch.bfloat16 if io == "bf16" else torch.float32
         self.o = torch.empty((B, T * N, H, D), dtype=dt, device=device)
         self.state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=device)
@@ -205,25 +214,28 @@ class ForwardPlan:
 
 
 def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, scan_chunk=0,
-            return_saved=False, algorithm="auto"):
-    """o, state_out (and the saved A_t / S_t buffer) of gdn_forward."""
+            return_saved=False, algorithm="auto", normalize_qk=False, gate_logits=False):
+    """o, state_out (and the saved A_t / S_t buffer) of gdn_forward.
+    normalize_qk / gate_logits: the block's prologue (GDN_FLAG_*)."""
     B, L, H, D, T, dev = _shapes(q, k, v, gamma, beta, n)
     if state_in is not None:
         _need(state_in, "state_in", torch.float32, (B, H, D, D), dev)
     plan = ForwardPlan(B, H, T, n, D, _io_of(q), dev, key_scale, scan_chunk, return_saved,
-                       algorithm)
+                       algorithm, flags_of(normalize_qk, gate_logits))
     o, st = plan(q, k, v, gamma, beta, state_in)
     if return_saved:
         return o, st, plan.saved
     return o, st
 
 
-def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None):
+def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None,
+         normalize_qk=False, gate_logits=False):
     """One streaming frame: q, k, v [B, N, H, D], gamma [B, 1, H], beta
     [B, N, H]; `state` [B, H, D, D] fp32 is updated in place.  Returns o."""
     B, N, H, D, T, dev = _shapes(q, k, v, gamma, beta, q.shape[1])
     _need(state, "state", torch.float32, (B, H, D, D), dev)
-    prob = make_problem(B, H, 1, N, D, _io_of(q), key_scale, 0)
+    prob = make_problem(B, H, 1, N, D, _io_of(q), key_scale, 0,
+                        flags=flags_of(normalize_qk, gate_logits))
     o = out if out is not None else torch.empty_like(v)
     if workspace is None:
         workspace = torch.empty(max(16, workspace_size(prob, GDN_OP_STEP)), dtype=torch.uint8,
@@ -235,15 +247,18 @@ def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None):
 
 
 def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None, saved=None,
-             key_scale=0.0, workspace=None, scan_chunk=0):
-    """Gradients dict (dq, dk, dv, dgamma, dbeta, dstate_in) of gdn_backward."""
+             key_scale=0.0, workspace=None, scan_chunk=0, normalize_qk=False,
+             gate_logits=False):
+    """Gradients dict (dq, dk, dv, dgamma, dbeta, dstate_in) of gdn_backward
+    (with the prologue flags: with respect to the raw q, k, gate logits)."""
     B, L, H, D, T, dev = _shapes(q, k, v, gamma, beta, n)
     _need(d_o, "d_o", q.dtype, (B, L, H, D), dev)
     if state_in is not None:
         _need(state_in, "state_in", torch.float32, (B, H, D, D), dev)
     if d_state_out is not None:
         _need(d_state_out, "d_state_out", torch.float32, (B, H, D, D), dev)
-    prob = make_problem(B, H, T, n, D, _io_of(q), key_scale, scan_chunk)
+    prob = make_problem(B, H, T, n, D, _io_of(q), key_scale, scan_chunk,
+                        flags=flags_of(normalize_qk, gate_logits))
     if saved is not None and saved.numel() != saved_size(prob):
         raise ValueError("saved buffer has the wrong size")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

@@ -28,6 +28,8 @@ struct Shape {
                      // type (bf16 for bf16 io, fp32 for fp32 io)
   int64_t parts;     // composite chunks per sequence
   bool token;        // forward in token form (chunks of frames, no D x D per frame)
+  bool norm;         // GDN_FLAG_NORMALIZE_QK
+  bool gates;        // GDN_FLAG_GATE_LOGITS
 };
 
 gdn_status check_problem(const gdn_problem* p, Shape* sh) {
@@ -39,6 +41,7 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (!isfinite(p->key_scale)) return GDN_ERR_BAD_SHAPE;
   if (p->Dk != p->Dv || p->Dk % 16 != 0 || p->Dk > 128) return GDN_ERR_UNSUPPORTED;
   if (p->algorithm < GDN_ALGO_AUTO || p->algorithm > GDN_ALGO_TOKEN) return GDN_ERR_UNSUPPORTED;
+  if (p->flags & ~(GDN_FLAG_NORMALIZE_QK | GDN_FLAG_GATE_LOGITS)) return GDN_ERR_UNSUPPORTED;
   Shape s;
   s.B = p->B; s.H = p->H; s.T = p->T; s.N = p->N; s.D = p->Dk;
   s.L = s.T * s.N;
@@ -62,6 +65,8 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (p->algorithm == GDN_ALGO_TOKEN && s.N > tok_max) return GDN_ERR_UNSUPPORTED;
   s.token = p->algorithm == GDN_ALGO_TOKEN ||
             (p->algorithm == GDN_ALGO_AUTO && s.N <= kTokenAutoMaxN);
+  s.norm = (p->flags & GDN_FLAG_NORMALIZE_QK) != 0;
+  s.gates = (p->flags & GDN_FLAG_GATE_LOGITS) != 0;
   *sh = s;
   return GDN_OK;
 }
@@ -131,8 +136,52 @@ int64_t token_ws(const Shape& s) {
   const int64_t comp = seg > 1 ? 3 * s.B * s.H * seg * s.D * s.D * 4 : 0;
   return s.B * s.H * token_chunks(s) * token_record_bytes(s.io) + comp;
 }
-int64_t forward_ws(const Shape& s) { return s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s); }
-int64_t backward_ws(const Shape& s) { return 6 * s.mat + scratch_bytes(s); }
+// Prologue (gdn_flag) buffers, after everything else in the workspace:
+// the gates from logits (gamma [B, T, H], beta [B, L, H], fp32) and, where
+// the kernels take normalised rows as input (`copies`: the token form, the
+// backward), q / |q| and k / |k| as [B, L, H, D] io dtype.
+int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+struct Prologue {
+  int64_t gamma, beta, q, k, end;   // offsets from the region's start; end = bytes
+};
+Prologue prologue_layout(const Shape& s, bool copies) {
+  Prologue r{};
+  int64_t o = 0;
+  if (s.gates) {
+    r.gamma = o; o += round256(s.B * s.T * s.H * 4);
+    r.beta = o;  o += round256(s.B * s.L * s.H * 4);
+  }
+  if (s.norm && copies) {
+    const int64_t tok = round256(s.B * s.L * s.H * s.D * s.es);
+    r.q = o; o += tok;
+    r.k = o; o += tok;
+  }
+  r.end = o;
+  return r;
+}
+// (the region starts 256-aligned after the entry point's own buffers)
+int64_t forward_base(const Shape& s) {
+  return round256(s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
+}
+int64_t backward_base(const Shape& s) { return round256(6 * s.mat + scratch_bytes(s)); }
+int64_t forward_ws(const Shape& s) {
+  const int64_t pro = prologue_layout(s, s.token).end;
+  return pro ? forward_base(s) + pro : (s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
+}
+int64_t backward_ws(const Shape& s) {
+  const int64_t pro = prologue_layout(s, true).end;
+  return pro ? backward_base(s) + pro : 6 * s.mat + scratch_bytes(s);
+}
+
+// Inputs of the recurrence after the prologue: the caller's tensors, or
+// the workspace copies the prologue's kernels write (gates from logits;
+// normalised rows when `copies`).
+struct Inputs {
+  const void* q;
+  const void* k;
+  const float* gamma;
+  const float* beta;
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
@@ -157,6 +206,32 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
 }
 
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* k,
+                        const float* gamma, const float* beta, char* region, Inputs* in,
+                        hipStream_t stream) {
+  const Prologue pl = prologue_layout(s, copies);
+  *in = Inputs{q, k, gamma, beta};
+  hipError_t e = hipSuccess;
+  if (s.gates) {
+    float* g = reinterpret_cast<float*>(region + pl.gamma);
+    float* b = reinterpret_cast<float*>(region + pl.beta);
+    e = launch_sigmoid(gamma, g, s.B * s.T * s.H, stream);
+    if (e == hipSuccess) e = launch_sigmoid(beta, b, s.B * s.L * s.H, stream);
+    in->gamma = g;
+    in->beta = b;
+  }
+  if (e == hipSuccess && s.norm && copies) {
+    void* qn = region + pl.q;
+    void* kn = region + pl.k;
+    const int64_t rows = s.B * s.L * s.H;
+    e = launch_rows_normalize(q, qn, rows, (int)s.D, s.io, stream);
+    if (e == hipSuccess) e = launch_rows_normalize(k, kn, rows, (int)s.D, s.io, stream);
+    in->q = qn;
+    in->k = kn;
+  }
+  return hip_status(e);
+}
 
 // Inter-frame scan over the whole sequence, sequential or chunked
 // (composites, a fold over chunks, then a parallel replay of every chunk).
@@ -203,7 +278,7 @@ gdn_status record(void* const* events, int i, hipStream_t stream) {
 
 // Token-form forward: the per-chunk operators into the workspace, then the
 // state pass.  The phase events of gdn_forward_events bracket both as the
-// output phase.
+// output phase (the caller records the first three).
 gdn_status run_token(const Shape& s, const void* q, const void* k, const void* v,
                      const float* gamma, const float* beta, const float* state_in, void* o,
                      float* state_out, void* workspace, hipStream_t stream,
@@ -222,8 +297,6 @@ gdn_status run_token(const Shape& s, const void* q, const void* k, const void* v
   ta.cps = (ta.nck + nseg - 1) / nseg;
   ta.nseg = (ta.nck + ta.cps - 1) / ta.cps;   // no empty segment
   gdn_status st = GDN_OK;
-  for (int i = 0; i < 3 && st == GDN_OK; ++i) st = record(events, i, stream);
-  if (st != GDN_OK) return st;
   if (ta.nseg == 1) {
     ta.mode = TOK_PLAIN;
     st = hip_status(launch_token(ta, s.io, nt, true, stream));
@@ -262,9 +335,19 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
                        const float* gamma, const float* beta, const float* state_in,
                        void* o, float* state_out, void* saved, void* workspace,
                        hipStream_t stream, void* const* events = nullptr) {
+  char* ws = static_cast<char*>(workspace);
+  // phases: the token form's prologue and passes all count as the output
+  // phase; the frame form's prologue as part of the Gram/write phase
+  gdn_status st = GDN_OK;
+  for (int i = 0; i < (s.token ? 3 : 1) && st == GDN_OK; ++i) st = record(events, i, stream);
+  if (st != GDN_OK) return st;
+  // the prologue's gates (and, for the token form, normalised rows)
+  Inputs in;
+  st = run_prologue(s, s.token, q, k, gamma, beta, ws + forward_base(s), &in, stream);
+  if (st != GDN_OK) return st;
+  q = in.q; k = in.k; gamma = in.gamma; beta = in.beta;
   if (s.token)
     return run_token(s, q, k, v, gamma, beta, state_in, o, state_out, workspace, stream, events);
-  char* ws = static_cast<char*>(workspace);
   void* A = saved ? saved : ws;
   void* S = saved ? static_cast<char*>(saved) + s.mat : ws + s.mat;
   void* U = ws + 2 * s.mat;
@@ -279,8 +362,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   ga.t0 = 0; ga.Tc = (int)s.T;
   ga.P = gram_splits(s);
   ga.part = reinterpret_cast<float*>(ws + 3 * s.mat);
-  gdn_status st = record(events, 0, stream);
-  if (st != GDN_OK) return st;
+  ga.norm = s.norm;   // fused: norms of the staged key rows
   st = hip_status(launch_gram(ga, s.io, nt, 2, stream));
   if (st != GDN_OK) return st;
   if (ga.P > 1 && (st = hip_status(launch_gram_reduce(ga, s.io, nt, 2, stream))) != GDN_OK)
@@ -298,6 +380,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
   oa.t0 = 0; oa.Tc = (int)s.T;
   oa.P = out_splits(s);
+  oa.norm = s.norm;   // fused: norms of the staged query rows
   st = hip_status(launch_output(oa, s.io, nt, false, stream));
   if (st != GDN_OK) return st;
   return record(events, 3, stream);
@@ -448,6 +531,17 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   hipStream_t stream_ = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const int nt = (int)(s.D / 16);
+  // The prologue's outputs (normalised q, k and the gates, in the
+  // workspace) are the inputs of the recurrence's reverse pass; its chain
+  // rule runs at the end on dq, dk, dgamma, dbeta in place.
+  const void* q_raw = q;
+  const void* k_raw = k;
+  const float* gamma_raw = gamma;
+  const float* beta_raw = beta;
+  Inputs in;
+  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_);
+  if (st != GDN_OK) return st;
+  q = in.q; k = in.k; gamma = in.gamma; beta = in.beta;
   const void* A;
   const void* S;
   if (saved) {
@@ -517,7 +611,21 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   ba.k = k; ba.v = v; ba.beta = beta; ba.G = G; ba.W = W;
   ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
   ba.B = (int)s.B; ba.H = (int)s.H; ba.T = (int)s.T; ba.N = (int)s.N;
-  return hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
+  st = hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
+  if (st != GDN_OK) return st;
+
+  // Chain rule through the prologue.
+  hipError_t e = hipSuccess;
+  if (s.norm) {
+    const int64_t rows = s.B * s.L * s.H;
+    e = launch_rows_normalize_bwd(q_raw, dq, rows, (int)s.D, s.io, stream_);
+    if (e == hipSuccess) e = launch_rows_normalize_bwd(k_raw, dk, rows, (int)s.D, s.io, stream_);
+  }
+  if (e == hipSuccess && s.gates) {
+    e = launch_sigmoid_bwd(gamma_raw, dgamma, s.B * s.T * s.H, stream_);
+    if (e == hipSuccess) e = launch_sigmoid_bwd(beta_raw, dbeta, s.B * s.L * s.H, stream_);
+  }
+  return hip_status(e);
 }
 
 }  // extern "C"

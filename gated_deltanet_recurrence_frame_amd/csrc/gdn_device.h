@@ -97,6 +97,23 @@ __device__ __forceinline__ bf16x8 lds_col_frag_bf16(const uint16_t* M, int ld, i
   return __builtin_bit_cast(bf16x8, ab);
 }
 
+// Sum over the 16 lanes of v's DPP row (lanes 16r .. 16r + 15), returned to
+// all 16 with the same rounding: lane ^ 1, lane ^ 2 (quad permutes), then
+// the mirror within each half row and within the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+// Reciprocal of the L2 norm from a sum of squares; 0 for a zero row.
+__device__ __forceinline__ float inv_norm(float ss) { return ss > 0.f ? rsqrtf(ss) : 0.f; }
+
 // Block-wide barrier.
 __device__ __forceinline__ void block_sync() { __syncthreads(); }
 

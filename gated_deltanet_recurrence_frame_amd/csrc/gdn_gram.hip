@@ -32,6 +32,13 @@
 // are read with the gfx950 transposing LDS read.  The weight w multiplies
 // the X operand in fp32 before rounding to bf16.  Tail tokens of the last
 // chunk re-read the frame's last row and get weight 0, so they add exactly 0.
+// Normalised keys (NORM, forward only): K^ = s K / |K| per token row, with
+// the norms taken from the rows being staged, no pass over K of its own.
+// At commit every thread also stores the sum of squares of its 16-byte
+// key piece; a wave then adds, per token it weights, the pieces of its
+// head's row (one per lane of a DPP row, summed across it).  A_t gets
+// w / |k|^2 on the K rows, U_t gets w / |k| on the V rows, and the raw keys
+// stay the Y operand.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -57,6 +64,8 @@ struct GramCfg {
   static constexpr int PPM = (MPC + NTH - 1) / NTH;         // of them per thread
   static constexpr int PPT = NMAT * PPM;                    // pieces per thread
   static constexpr int NWT = CT * HPW;                      // weights per chunk
+  static constexpr int PH = D * ES / 16;                    // 16-byte pieces per head row
+  static constexpr int NU = (PH + 15) / 16;                 // of them per lane of a DPP row
   // LDS row stride (elements).  A fragment read takes the same 16 bf16 (or
   // 16 fp32) columns of 4 consecutive token rows per group of lanes; rows
   // are padded so that those rows start on different banks of the 32
@@ -87,14 +96,17 @@ struct GramItem {
 // SPLIT: the launch splits frames' tokens (a.P > 1) and stores fp32
 // partials; a compile-time choice, so that no branch joins stores of the two
 // kinds (the compiler would lose its count of the stores in flight).
-template <int IO, int NT, int NR, bool Y_IS_X0, int HPW, bool SPLIT>
+template <int IO, int NT, int NR, bool Y_IS_X0, int HPW, bool SPLIT, bool NORM>
 __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_kernel(GramArgs a) {
   typedef GramCfg<IO, NT, NR, Y_IS_X0, HPW> C;
+  static_assert(!NORM || (NR == 2 && Y_IS_X0), "normalised keys: X_0 == Y == K, X_1 == V");
   typedef typename Io<IO>::elem E;
   constexpr int D = C::D, CT = C::CT, ES = C::ES, PR = C::PR, NTH = C::NTH;
   constexpr int LDR = C::LDR;
   __shared__ __attribute__((aligned(16))) E stage[2][C::STAGE_ELEMS];
   __shared__ float wstage[2][C::NWT];
+  // NORM: sums of squares of the key pieces, [token][piece of the row segment]
+  __shared__ float nstage[2][NORM ? CT * PR : 1];
 
   const int HG = a.H / HPW;                        // head groups
   const int total = a.B * a.Tc * HG * a.P;
@@ -178,6 +190,26 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
           *reinterpret_cast<u32x4*>(&stage[st][(m * CT + q / PR) * LDR + (q % PR) * (16 / ES)]) =
               R.v[m * C::PPM + j];
       }
+    if constexpr (NORM) {   // matrix 0: the keys
+#pragma unroll
+      for (int j = 0; j < C::PPM; ++j) {
+        const int q = tid + NTH * j;
+        const u32x4 pc = R.v[j];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (C::BF) {
+            const float lo = __uint_as_float(pc[e] << 16), hi = __uint_as_float(pc[e] & 0xffff0000u);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+          } else {
+            const float x = __uint_as_float(pc[e]);
+            ss = fmaf(x, x, ss);
+          }
+        }
+        if (C::MPC % NTH == 0 || q < C::MPC) nstage[st][q] = ss;
+      }
+    }
     // tokens past the frame's end get weight 0 (their rows are re-read copies)
     if (tid < C::NWT) wstage[st][tid] = tid / HPW < nv ? (has_w ? R.w : 1.0f) : 0.0f;
   };
@@ -190,15 +222,38 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
       for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
   };
 
+  // NORM: this lane's share of |k|^2 for token tk of the chunk and this
+  // wave's head: pieces i, i + 16, .. of the head's row (lane i of its DPP row)
+  auto key_piece_sum = [&](int st, int tk) {
+    float ss = 0.f;
+    if constexpr (NORM) {
+#pragma unroll
+      for (int u = 0; u < C::NU; ++u) {
+        const int pc = li + 16 * u;
+        const float x = nstage[st][tk * PR + hp * C::PH + min(pc, C::PH - 1)];
+        ss += pc < C::PH ? x : 0.f;
+      }
+    }
+    return ss;
+  };
+
   auto compute = [&](int st) {
     // this wave's head: its D features at offset hp * D of each row segment
     const E* xs = &stage[st][hp * D];
     const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * CT * LDR;
     const float* ws = wstage[st];
     if constexpr (C::BF) {
-      float wv[8];
+      float wv[8], wv1[8];   // weights of the X_0 and X_1 rows: token 8 g + e
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wv[e] = ws[(8 * g + e) * HPW + hp];
+      for (int e = 0; e < 8; ++e) wv[e] = wv1[e] = ws[(8 * g + e) * HPW + hp];
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float r = inv_norm(row_sum16(key_piece_sum(st, 8 * g + e)));
+          wv1[e] = wv[e] * r;
+          wv[e] = wv1[e] * r;
+        }
+      }
       // the wave's weighted row fragments first, then one column fragment at
       // a time (few fragments live next to the accumulators)
       bf16x8 af[C::RT];
@@ -213,7 +268,7 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
                                   ft * 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          af[j][e] = static_cast<__bf16>(static_cast<float>(af[j][e]) * wv[e]);
+          af[j][e] = static_cast<__bf16>(static_cast<float>(af[j][e]) * (m == 0 ? wv[e] : wv1[e]));
       }
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
@@ -226,16 +281,22 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
 #pragma unroll 1
       for (int kb = 0; kb < CT / 4; ++kb) {
         const int k = kb * 4 + g;
-        const float wv = ws[k * HPW + hp];
+        float wv = ws[k * HPW + hp], wv1 = wv;
         float bfr[NT];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * LDR + ct * 16 + li];
+        if constexpr (NORM) {
+          const float r = inv_norm(row_sum16(key_piece_sum(st, k)));
+          wv1 = wv * r;
+          wv = wv1 * r;
+        }
 #pragma unroll
         for (int j = 0; j < C::RT; ++j) {
           const int m = j / C::RPM;   // see the bf16 path
           const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
           const float af =
-              reinterpret_cast<const float*>(xs + m * CT * LDR)[k * LDR + ft * 16 + li] * wv;
+              reinterpret_cast<const float*>(xs + m * CT * LDR)[k * LDR + ft * 16 + li] *
+              (m == 0 ? wv : wv1);
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_f32(af, bfr[ct], acc[j][ct]);
         }
@@ -462,15 +523,19 @@ static void launch_gram_hpw(const GramArgs& a, int nr, hipStream_t s) {
   if (total < grid) grid = total;
   const dim3 block(64 * GRAM_WPH * HPW);
   if (a.P > 1) {
-    if (nr == 2)
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, true>), dim3(grid), block, 0, s, a);
+    if (nr == 2 && a.norm)
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, true, true>), dim3(grid), block, 0, s, a);
+    else if (nr == 2)
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, true, false>), dim3(grid), block, 0, s, a);
     else
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, true>), dim3(grid), block, 0, s, a);
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, true, false>), dim3(grid), block, 0, s, a);
   } else {
-    if (nr == 2)
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, false>), dim3(grid), block, 0, s, a);
+    if (nr == 2 && a.norm)
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, false, true>), dim3(grid), block, 0, s, a);
+    else if (nr == 2)
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, false, false>), dim3(grid), block, 0, s, a);
     else
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, false>), dim3(grid), block, 0, s, a);
+      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, false, false>), dim3(grid), block, 0, s, a);
   }
 }
 
@@ -501,6 +566,7 @@ static hipError_t launch_gram_io(const GramArgs& a, int nt, int nr, hipStream_t 
 }
 
 hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s) {
+  if (a.norm && nr != 2) return hipErrorInvalidValue;
   return io == IO_BF16 ? launch_gram_io<IO_BF16>(a, nt, nr, s)
                        : launch_gram_io<IO_F32>(a, nt, nr, s);
 }

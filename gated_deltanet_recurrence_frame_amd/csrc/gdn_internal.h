@@ -34,6 +34,10 @@ struct GramArgs {
   // launch_gram_reduce then sums them in a fixed order into out0 / out1.
   int P;
   float* part;
+  // Normalised keys (NR == 2, Y == X_0 == K, X_1 == V): every token's row is
+  // taken as k / |k|, so X_0's weight becomes w / |k|^2 and X_1's w / |k|,
+  // with |k| from the staged rows of Y (a zero row gets weight 0).
+  int norm;
 };
 hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
 hipError_t launch_gram_reduce(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
@@ -86,6 +90,7 @@ struct OutArgs {
   int B, H, T, N;
   int t0, Tc;           // frames t0 .. t0 + Tc - 1
   int P;                // token splits: each frame's chunks over P workgroups
+  int norm;             // O_t = S_t (q / |q|) per token (forward only; 0 for a zero row)
 };
 hipError_t launch_output(const OutArgs& a, int io, int nt, bool trans, hipStream_t s);
 
@@ -115,6 +120,20 @@ struct BwdTokArgs {
   int B, H, T, N;
 };
 hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
+
+// Prologue of the GDN block (gdn_flag).
+//   sigmoid:        y[i] = 1 / (1 + exp(-x[i])), i < n (fp32)
+//   sigmoid_bwd:    g[i] <- g[i] p (1 - p), p = sigmoid(x[i])
+//   rows_normalize: y[r] = x[r] / |x[r]| for rows of d io elements (0 for a
+//                   zero row)
+//   rows_normalize_bwd: g[r] <- (g[r] - x^ (x^ . g[r])) / |x[r]| in place,
+//                   x^ = x[r] / |x[r]| (0 for a zero row)
+hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s);
+hipError_t launch_sigmoid_bwd(const float* x, float* g, int64_t n, hipStream_t s);
+hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, int io,
+                                 hipStream_t s);
+hipError_t launch_rows_normalize_bwd(const void* x, void* g, int64_t rows, int d, int io,
+                                     hipStream_t s);
 
 // Token-space forward (frames with few tokens): one workgroup per (b, h),
 // chunks of F frames of N tokens, F N <= TokCfg<io>::CP.

@@ -19,6 +19,10 @@
 // while stores are pending), and the barriers are LDS-only, so the PF - 1
 // chunks ahead stay in flight across them.  The loop over whole chunks is
 // straight-line; the frame's last, partial chunk is finished after it.
+// Normalised queries (NORM, forward only): o = S_t q / |q|.  A lane's
+// query fragments hold a quarter of its token's features, so the squares
+// it sums over them, added over the token's four lanes, give |q|^2; the
+// accumulators are scaled by 1 / |q| before rounding.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -28,8 +32,9 @@ namespace gdn {
 
 // bf16: registers kept to 128 so that two workgroups share a CU (4 waves per
 // SIMD; the LDS stages allow it), which hides more of the per-chunk chain.
-template <int IO, int NT, bool TRANS, int HPW>
+template <int IO, int NT, bool TRANS, int HPW, bool NORM>
 __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(OutArgs a) {
+  static_assert(!(NORM && TRANS), "normalised queries belong to the forward");
   typedef typename Io<IO>::elem E;
   constexpr bool BF = (IO == IO_BF16);
   constexpr int D = 16 * NT;
@@ -143,6 +148,7 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
       for (int tt = 0; tt < CT / 16; ++tt) {
         f32x4 acc = zero4();
         const E* trow = ts + (tt * 16 + li) * RW + hp * D;
+        float ss = 0.f;   // NORM: squares of this lane's query features
         if constexpr (BF) {
 #pragma unroll
           for (int kb = 0; kb < KF; ++kb) {
@@ -151,10 +157,26 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
             bf16x8 q = load_bf16x8(reinterpret_cast<const uint16_t*>(trow) + kb * 32 + 8 * g);
             if (KTAIL && kb == KF - 1 && kb * 32 + 8 * g >= D) q = zero_bf16x8();
             acc = mfma_bf16(sf[hp][kb], q, acc);
+            if constexpr (NORM) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float x = static_cast<float>(q[e]);
+                ss = fmaf(x, x, ss);
+              }
+            }
           }
         } else {
 #pragma unroll
-          for (int kb = 0; kb < KF; ++kb) acc = mfma_f32(sf[hp][kb], trow[kb * 4 + g], acc);
+          for (int kb = 0; kb < KF; ++kb) {
+            const float x = trow[kb * 4 + g];
+            acc = mfma_f32(sf[hp][kb], x, acc);
+            if constexpr (NORM) ss = fmaf(x, x, ss);
+          }
+        }
+        if constexpr (NORM) {   // token tt * 16 + i sits in lanes i, i + 16, i + 32, i + 48
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          acc *= inv_norm(ss);
         }
         E* dst = ob + (tt * 16 + li) * RW + hp * D + ft * 16 + 4 * g;
         if constexpr (BF) {
@@ -233,17 +255,28 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
     store_tail(nchunks - 1);
 }
 
-template <int IO, int NT, bool TRANS>
-static hipError_t launch_output_nt(const OutArgs& a, hipStream_t s) {
+template <int IO, int NT, bool TRANS, bool NORM>
+static hipError_t launch_output_norm(const OutArgs& a, hipStream_t s) {
   // adjacent head pairs when H is even: 2 D-wide row segments per token are
   // contiguous and 64-byte aligned, where one head's rows are not
   if (a.H % 2 == 0)
-    hipLaunchKernelGGL((output_kernel<IO, NT, TRANS, 2>), dim3(a.B * a.Tc * (a.H / 2) * a.P),
+    hipLaunchKernelGGL((output_kernel<IO, NT, TRANS, 2, NORM>), dim3(a.B * a.Tc * (a.H / 2) * a.P),
                        dim3(64 * NT), 0, s, a);
   else
-    hipLaunchKernelGGL((output_kernel<IO, NT, TRANS, 1>), dim3(a.B * a.Tc * a.H * a.P),
+    hipLaunchKernelGGL((output_kernel<IO, NT, TRANS, 1, NORM>), dim3(a.B * a.Tc * a.H * a.P),
                        dim3(64 * NT), 0, s, a);
   return hipGetLastError();
+}
+
+template <int IO, int NT, bool TRANS>
+static hipError_t launch_output_nt(const OutArgs& a, hipStream_t s) {
+  if constexpr (TRANS) {
+    if (a.norm) return hipErrorInvalidValue;
+    return launch_output_norm<IO, NT, true, false>(a, s);
+  } else {
+    return a.norm ? launch_output_norm<IO, NT, false, true>(a, s)
+                  : launch_output_norm<IO, NT, false, false>(a, s);
+  }
 }
 
 template <int IO, bool TRANS>

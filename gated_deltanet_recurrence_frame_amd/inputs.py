@@ -14,6 +14,11 @@ then dO, dS_T and S_0 when asked for.  Q and K are L2-normalised per
 (token, head) over the head dimension in float32, then every io tensor is
 cast to the io dtype (bf16 round-to-nearest-even through torch).  Gates and
 states stay float32.
+
+``raw=True`` draws the inputs of the block's prologue instead: Q and K rows
+are not normalised but multiplied by per-row factors exp(N(0, 1)) (drawn
+after beta, Q's then K's), and gamma, beta are the logits themselves:
+gamma ~ N(3, 0.5), beta ~ N(0, 1).
 """
 
 import numpy as np
@@ -46,7 +51,7 @@ def _to_io(x, io):
 
 def make_inputs(B, H, T, N, D, io="bf16", gamma="uniform", seed=0,
                 with_do=False, with_dstate=False, with_state=False,
-                state_std=0.1, **_unused):
+                state_std=0.1, raw=False, **_unused):
     """Draw one problem.  Returns a dict of CPU torch tensors:
     q, k, v [B, L, H, D] (io dtype), gamma [B, T, H] and beta [B, L, H]
     (float32), and optionally d_o [B, L, H, D] (io dtype), d_state
@@ -58,7 +63,9 @@ def make_inputs(B, H, T, N, D, io="bf16", gamma="uniform", seed=0,
     q = rng.standard_normal((B, L, H, D), dtype=np.float32)
     k = rng.standard_normal((B, L, H, D), dtype=np.float32)
     v = rng.standard_normal((B, L, H, D), dtype=np.float32)
-    if gamma == "sigmoid":
+    if raw:
+        g = rng.normal(3.0, 0.5, size=(B, T, H)).astype(np.float32)
+    elif gamma == "sigmoid":
         g = _sigmoid(rng.normal(3.0, 0.5, size=(B, T, H)))
     elif gamma == "uniform":
         g = rng.uniform(0.9, 1.0, size=(B, T, H)).astype(np.float32)
@@ -66,9 +73,14 @@ def make_inputs(B, H, T, N, D, io="bf16", gamma="uniform", seed=0,
         g = np.ones((B, T, H), dtype=np.float32)
     else:
         raise ValueError(gamma)
-    beta = _sigmoid(rng.standard_normal((B, L, H), dtype=np.float32))
-    _l2_normalise(q)
-    _l2_normalise(k)
+    beta = rng.standard_normal((B, L, H), dtype=np.float32)
+    if raw:
+        q *= np.exp(rng.standard_normal((B, L, H, 1), dtype=np.float32))
+        k *= np.exp(rng.standard_normal((B, L, H, 1), dtype=np.float32))
+    else:
+        beta = _sigmoid(beta)
+        _l2_normalise(q)
+        _l2_normalise(k)
     out = {"q": _to_io(q, io), "k": _to_io(k, io), "v": _to_io(v, io),
            "gamma": torch.from_numpy(g), "beta": torch.from_numpy(beta)}
     del q, k, v

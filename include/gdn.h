@@ -22,8 +22,9 @@
  *   beta            [B, L, H]        fp32   (one write strength per token)
  *   state_*         [B, H, Dv, Dk]   fp32
  *   dgamma [B,T,H], dbeta [B,L,H]    fp32
- * Queries and keys are used as given: the library does not normalise them;
- * it applies only the key scale.
+ * By default queries and keys are used as given (the library applies only
+ * the key scale) and gamma, beta are the gates themselves; the problem's
+ * `flags` can ask for the block's prologue instead (gdn_flag).
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -64,8 +65,8 @@ typedef enum {
     GDN_ERR_MISALIGNED = 4,          /* a pointer misaligned (16 B; gates 4 B) */
     GDN_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < required            */
     GDN_ERR_UNSUPPORTED = 6,         /* D not a multiple of 16, > 128, Dk!=Dv;
-                                        unknown algorithm; token form outside
-                                        its limits (see gdn_algorithm)        */
+                                        unknown algorithm or flag; token form
+                                        outside its limits (gdn_algorithm)    */
     GDN_ERR_HIP = 7,                 /* a kernel launch failed                */
     GDN_ERR_ALIASING = 8             /* an output overlaps an input           */
 } gdn_status;
@@ -92,6 +93,21 @@ typedef enum { GDN_OP_FORWARD = 0, GDN_OP_STEP = 1, GDN_OP_BACKWARD = 2 } gdn_op
  * saved buffer is given). */
 typedef enum { GDN_ALGO_AUTO = 0, GDN_ALGO_FRAME = 1, GDN_ALGO_TOKEN = 2 } gdn_algorithm;
 
+/* Optional prologue of the GDN block, fused into the entry points (bits of
+ * gdn_problem.flags; any other bit is GDN_ERR_UNSUPPORTED).  The hats on
+ * Q^_t and K^_t (summary page, 方法步骤详情 module 2) read as per-token
+ * normalisation:
+ *   GDN_FLAG_NORMALIZE_QK  every query and key row (one token, one head) is
+ *                          divided by its L2 norm over the head dimension
+ *                          before the key scale; a row of zeros stays zero.
+ *                          The frame form's forward takes the norms from the
+ *                          rows it already stages (no extra pass over q, k).
+ *   GDN_FLAG_GATE_LOGITS   gamma and beta arrive as logits x and the
+ *                          recurrence uses sigmoid(x) = 1 / (1 + exp(-x)).
+ * gdn_backward then returns the gradients with respect to these raw inputs
+ * (chain rule through the prologue). */
+typedef enum { GDN_FLAG_NORMALIZE_QK = 1, GDN_FLAG_GATE_LOGITS = 2 } gdn_flag;
+
 typedef struct {
     int32_t B, H, T, N;   /* batch, heads, latent frames, tokens per frame   */
     int32_t Dk, Dv;       /* head dims; must be equal                        */
@@ -104,6 +120,7 @@ typedef struct {
                              frames (novelty point 1); same result up to
                              rounding order                                  */
     int32_t algorithm;    /* gdn_algorithm of the forward                    */
+    int32_t flags;        /* OR of gdn_flag; 0 => no prologue                */
 } gdn_problem;
 
 /* Version of this interface (GDN_ABI_VERSION). */
@@ -127,7 +144,9 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
 
 /* Whole-sequence forward (module 2 recurrence over t = 1..T):
  *   S_t = S_{t-1} (gamma_t I - K^_t beta_t K^_t^T) + V_t beta_t K^_t^T,
- *   O_t = S_t Q^_t,  K^ = key_scale * K.
+ *   O_t = S_t Q^_t,  K^ = key_scale * K,  Q^ = Q
+ * (with GDN_FLAG_NORMALIZE_QK: K^ = key_scale * K / |K|, Q^ = Q / |Q| per
+ * row; with GDN_FLAG_GATE_LOGITS gamma, beta are logits, see gdn_flag).
  *   state_in   S_0; NULL => zero.
  *   o          output [B, L, H, Dv], io dtype.
  *   state_out  S_T; NULL => not written; may equal state_in (in place).
@@ -178,7 +197,11 @@ gdn_status gdn_step(const gdn_problem* p,
  *                NULL to recompute it inside the workspace.
  *   dq, dk, dv   io dtype, layouts of q, k, v.  dgamma, dbeta fp32.
  *   d_state_in   dLoss/dS_0; NULL => not written.
- *   workspace    gdn_workspace_size(p, GDN_OP_BACKWARD) bytes. */
+ *   workspace    gdn_workspace_size(p, GDN_OP_BACKWARD) bytes.
+ * With p->flags set, q, k, gamma, beta are the raw inputs of the forward
+ * and dq, dk, dgamma, dbeta the gradients with respect to them:
+ * dx = (dx^ - x^ (x^ . dx^)) / |x| for a normalised row x^ = x / |x| (0 for
+ * a zero row), dz = dp p (1 - p) for a gate p = sigmoid(z). */
 gdn_status gdn_backward(const gdn_problem* p,
                         const void* q, const void* k, const void* v,
                         const float* gamma, const float* beta,

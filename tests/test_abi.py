@@ -33,7 +33,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2 == gb.ABI_VERSION
+    assert lib.gdn_abi_version() == 3 == gb.ABI_VERSION
     for code in range(9):
         s = lib.gdn_status_string(code).decode()
         assert s and s != "unknown status"
@@ -154,3 +154,32 @@ def test_algorithm_field(lib):
     # auto is currently the frame form
     auto = gb.make_problem(1, 2, 4, 1, 32, "bf16")
     assert _ws(auto, gb.GDN_OP_FORWARD)[1] > 0
+
+
+def test_prologue_flags(lib):
+    """The prologue's flags: unknown bits rejected; the gates from logits
+    need fp32 copies of gamma and beta in the workspace; normalised rows
+    need q / |q| and k / |k| copies where the kernels take them as input
+    (the backward, the token form), not in the frame form's forward, which
+    takes the norms from the rows it stages."""
+    B, H, T, N, D = 1, 20, 121, 880, 112
+    L = T * N
+    mat = B * H * T * D * D * 2
+    r256 = lambda n: (n + 255) // 256 * 256
+    gates = r256(B * T * H * 4) + r256(B * L * H * 4)
+    copies = 2 * r256(B * L * H * D * 2)
+    for flags, fwd, bwd in ((gb.GDN_FLAG_NORMALIZE_QK, 0, copies),
+                            (gb.GDN_FLAG_GATE_LOGITS, gates, gates),
+                            (3, gates, gates + copies)):
+        p = gb.make_problem(B, H, T, N, D, "bf16", flags=flags)
+        assert _ws(p, gb.GDN_OP_FORWARD) == (0, 3 * mat + fwd)
+        assert _ws(p, gb.GDN_OP_BACKWARD) == (0, 6 * mat + bwd)
+    pt = gb.make_problem(1, 2, 4, 8, 32, "bf16", algorithm="token", flags=3)
+    base = 2 * (2 * 64 * 64 * 2 + 5 * 64 * 4)
+    assert _ws(pt, gb.GDN_OP_FORWARD) == (
+        0, r256(base) + r256(4 * 2 * 4) + r256(32 * 2 * 4) + 2 * r256(32 * 2 * 32 * 2))
+    for bit in (4, 1 << 30, -1):
+        bad = gb.make_problem(1, 2, 4, 8, 32, "bf16")
+        bad.flags = bit
+        assert gb.STATUS[_ws(bad, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
+    assert gb.flags_of(True, False) == 1 and gb.flags_of(False, True) == 2

@@ -1,0 +1,188 @@
+"""GPU parity of the block's prologue (gdn_flag) against the float64 oracle.
+
+The hats on Q^ and K^ (summary page, 方法步骤详情 module 2) read as per-token
+L2 normalisation, gates given as logits: gdn_forward, gdn_step and
+gdn_backward with GDN_FLAG_NORMALIZE_QK / GDN_FLAG_GATE_LOGITS against
+``oracle.forward / step / backward(..., normalize_qk, gate_logits)`` on raw
+inputs (rows of widely varying norm, gate logits), same bars as the plain
+path: relative L2 <= 1e-5 (fp32 io), <= 2e-2 (bf16 io).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_recurrence_frame_amd import binding as gb
+from gated_deltanet_recurrence_frame_amd import inputs as gin
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+DEV = "cuda:0"
+FLAGS = {"norm": (True, False), "gates": (False, True), "both": (True, True)}
+
+
+def rel_l2(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    return np.linalg.norm((gpu - ref).ravel()) / (den if den > 0 else 1.0)
+
+
+def f64(t):
+    return gin.as_f64(t)
+
+
+def dev(inp):
+    return {k: v.to(DEV).contiguous() for k, v in inp.items()}
+
+
+def oracle_forward(inp, N, nq, gl, with_state, key_scale=0.0):
+    return oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                          f64(inp["beta"]), N,
+                          state_in=f64(inp["state"]) if with_state else None,
+                          key_scale=key_scale, normalize_qk=nq, gate_logits=gl)
+
+
+def check_forward(inp, N, io, nq, gl, with_state=True, **kw):
+    d = dev(inp)
+    o, so = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                       state_in=d["state"] if with_state else None, normalize_qk=nq,
+                       gate_logits=gl, **kw)
+    torch.cuda.synchronize()
+    ro, rs = oracle_forward(inp, N, nq, gl, with_state, kw.get("key_scale", 0.0))
+    eo, es = rel_l2(f64(o.cpu()), ro), rel_l2(f64(so.cpu()), rs)
+    print("prologue forward rel_l2: o %.3e state %.3e" % (eo, es))
+    assert np.all(np.isfinite(f64(o.cpu())))
+    assert eo <= TOL[io], eo
+    assert es <= TOL[io], es
+    return eo, es
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("flags", list(FLAGS))
+@pytest.mark.parametrize("B,H,T,N,D", [
+    (2, 3, 5, 100, 112),   # single heads, ragged token chunks
+    (1, 4, 6, 65, 64),     # head pairs
+    (1, 2, 4, 37, 16),
+    (1, 2, 3, 50, 128),
+])
+def test_forward_prologue(io, flags, B, H, T, N, D):
+    nq, gl = FLAGS[flags]
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, seed=50 + D, with_state=True,
+                          raw=True)
+    check_forward(inp, N, io, nq, gl)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_forward_prologue_differs_from_plain(io):
+    # the flags change the result (raw rows are far from unit norm)
+    inp = gin.make_inputs(B=1, H=2, T=4, N=40, D=32, io=io, seed=60, raw=True)
+    d = dev(inp)
+    o_on, _ = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], 40,
+                         normalize_qk=True, gate_logits=True)
+    ro_off, _ = oracle.forward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]),
+                               1.0 / (1.0 + np.exp(-f64(inp["gamma"]))),
+                               1.0 / (1.0 + np.exp(-f64(inp["beta"]))), 40)
+    assert rel_l2(f64(o_on.cpu()), ro_off) > 0.1
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_forward_prologue_chunked_scan(io):
+    inp = gin.make_inputs(B=1, H=3, T=11, N=70, D=112, io=io, seed=61, with_state=True,
+                          raw=True)
+    check_forward(inp, 70, io, True, True, scan_chunk=3)
+
+
+def test_forward_prologue_short_clip_bf16():
+    # the short-clip layer shape (20 heads, D = 112, 21 x 880 tokens)
+    inp = gin.make_inputs(B=1, H=20, T=21, N=880, D=112, io="bf16", seed=62, raw=True)
+    eo, _ = check_forward(inp, 880, "bf16", True, True, with_state=False)
+    assert eo < 5e-3
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("flags", list(FLAGS))
+def test_token_form_prologue(io, flags):
+    nq, gl = FLAGS[flags]
+    N = 4
+    inp = gin.make_inputs(B=1, H=3, T=40, N=N, D=64, io=io, seed=63, with_state=True,
+                          raw=True)
+    check_forward(inp, N, io, nq, gl, algorithm="token")
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_step_prologue(io):
+    # streaming frames with the prologue (token splits of the Gram/write pass)
+    B, H, T, N, D = 1, 2, 4, 300, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, seed=64, with_state=True,
+                          raw=True)
+    d = dev(inp)
+    state = d["state"].clone()
+    outs = []
+    for t in range(T):
+        sl = slice(t * N, (t + 1) * N)
+        outs.append(gb.step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                            d["v"][:, sl].contiguous(), d["gamma"][:, t:t + 1].contiguous(),
+                            d["beta"][:, sl].contiguous(), state, normalize_qk=True,
+                            gate_logits=True).clone())
+    torch.cuda.synchronize()
+    ro, rs = oracle_forward(inp, N, True, True, True)
+    eo = rel_l2(f64(torch.cat(outs, dim=1).cpu()), ro)
+    es = rel_l2(f64(state.cpu()), rs)
+    print("prologue step rel_l2: o %.3e state %.3e" % (eo, es))
+    assert eo <= TOL[io] and es <= TOL[io]
+
+
+def test_zero_rows_stay_zero():
+    # a query or key row of zeros has no direction: the library keeps it
+    # zero (its token writes nothing, its output row is zero); compare with
+    # the oracle on inputs normalised row by row where the norm is not zero
+    io, N = "fp32", 20
+    inp = gin.make_inputs(B=1, H=2, T=3, N=N, D=32, io=io, seed=65, raw=True)
+    inp["k"][0, 5, 1] = 0.0
+    inp["k"][0, 47, 0] = 0.0
+    inp["q"][0, 12, 0] = 0.0
+    d = dev(inp)
+    o, so = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, normalize_qk=True)
+    torch.cuda.synchronize()
+    qn, kn = f64(inp["q"]), f64(inp["k"])
+    for x in (qn, kn):
+        nrm = np.linalg.norm(x, axis=-1, keepdims=True)
+        np.divide(x, nrm, out=x, where=nrm > 0)
+    ro, rs = oracle.forward(qn, kn, f64(inp["v"]), f64(inp["gamma"]), f64(inp["beta"]), N)
+    assert np.all(f64(o.cpu())[0, 12, 0] == 0.0)
+    assert rel_l2(f64(o.cpu()), ro) <= TOL[io]
+    assert rel_l2(f64(so.cpu()), rs) <= TOL[io]
+
+
+def check_backward(inp, N, io, nq, gl, use_saved):
+    d = dev(inp)
+    saved = None
+    if use_saved:
+        _, _, saved = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                                 state_in=d["state"], return_saved=True, normalize_qk=nq,
+                                 gate_logits=gl)
+    gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                     state_in=d["state"], d_state_out=d["d_state"], saved=saved,
+                     normalize_qk=nq, gate_logits=gl)
+    torch.cuda.synchronize()
+    ref = oracle.backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["gamma"]),
+                          f64(inp["beta"]), N, f64(inp["d_o"]), state_in=f64(inp["state"]),
+                          d_state_out=f64(inp["d_state"]), normalize_qk=nq, gate_logits=gl)
+    errs = {n: rel_l2(f64(gr[n].cpu()), ref[n])
+            for n in ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]}
+    print("prologue backward rel_l2:", {k: "%.2e" % v for k, v in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL[io], (name, e)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("flags", list(FLAGS))
+@pytest.mark.parametrize("use_saved", [False, True])
+def test_backward_prologue(io, flags, use_saved):
+    nq, gl = FLAGS[flags]
+    inp = gin.make_inputs(B=2, H=3, T=5, N=100, D=112, io=io, seed=66, with_do=True,
+                          with_dstate=True, with_state=True, raw=True)
+    check_backward(inp, 100, io, nq, gl, use_saved)
