@@ -118,8 +118,8 @@ def cpu_baseline(inp, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--scan-chunk", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -189,6 +189,8 @@ def main():
         extra["windows"] = [bench_windows(gb, d, B, H, D, T, N, k) for k in (2, 8, 15)]
         print("[bench] token-wise GDN (token form)", file=sys.stderr, flush=True)
         extra["tokenwise"] = bench_tokenwise(gb, d, B, H, D, T * N)
+        print("[bench] block prologue", file=sys.stderr, flush=True)
+        extra["prologue"] = bench_prologue(gb, d, B, H, D, T, N)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -293,6 +295,50 @@ def bench_tokenwise(gb, d, B, H, D, L):
         ms = e0.elapsed_time(e1) / reps
         out[name] = {"tokens": B * T, "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1)}
         del plan
+    return out
+
+
+def bench_prologue(gb, d, B, H, D, T, N):
+    """The block's prologue at the 1-min shape: gdn_forward with the query /
+    key normalisation and gate logits fused (GDN_FLAG_*), the same forward
+    behind a separate normalisation pass (torch ops, for comparison only),
+    and forward + backward with the prologue."""
+    import torch
+    dev = d["q"].device
+    args = (d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    fused = gb.ForwardPlan(B, H, T, N, D, "bf16", dev, flags=3)
+    plain = gb.ForwardPlan(B, H, T, N, D, "bf16", dev)
+    sv = gb.ForwardPlan(B, H, T, N, D, "bf16", dev, flags=3, saved=True)
+    ws = torch.empty(gb.workspace_size(sv.prob, gb.GDN_OP_BACKWARD), dtype=torch.uint8,
+                     device=dev)
+
+    def separate():
+        q = torch.nn.functional.normalize(d["q"].float(), dim=-1).to(torch.bfloat16)
+        k = torch.nn.functional.normalize(d["k"].float(), dim=-1).to(torch.bfloat16)
+        plain(q, k, d["v"], torch.sigmoid(d["gamma"]), torch.sigmoid(d["beta"]))
+
+    def train():
+        sv(*args)
+        gb.backward(*args, N, d["d_o"], saved=sv.saved, workspace=ws, normalize_qk=True,
+                    gate_logits=True)
+
+    out = {"workload": "gdn_forward with normalised q, k and gate logits, 1-min shape"}
+    tokens = B * T * N
+    for name, fn, reps in (("fused_forward", lambda: fused(*args), 10),
+                           ("plain_forward", lambda: plain(*args), 10),
+                           ("separate_pass_forward", separate, 5),
+                           ("fused_forward_backward", train, 3)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1)}
+    del fused, plain, sv, ws
     return out
 
 

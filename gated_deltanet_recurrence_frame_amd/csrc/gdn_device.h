@@ -111,6 +111,39 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_mov<0x140>(v);   // row_mirror
   return v;
 }
+// Sum of squares of the 8 bf16 (or 4 fp32) values of a 16-byte piece, and
+// the piece scaled by r (bf16 rounded to nearest even).
+template <int IO>
+__device__ __forceinline__ float piece_sumsq(const u32x4& v) {
+  float ss = 0.f;
+  if constexpr (IO == IO_BF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xffff0000u);
+      ss = fmaf(hi, hi, fmaf(lo, lo, ss));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(__uint_as_float(v[e]), __uint_as_float(v[e]), ss);
+  }
+  return ss;
+}
+template <int IO>
+__device__ __forceinline__ u32x4 piece_scale(const u32x4& v, float r) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (IO == IO_BF16) {
+      const float lo = __uint_as_float(v[e] << 16) * r;
+      const float hi = __uint_as_float(v[e] & 0xffff0000u) * r;
+      o[e] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    } else {
+      o[e] = __float_as_uint(__uint_as_float(v[e]) * r);
+    }
+  }
+  return o;
+}
+
 // Reciprocal of the L2 norm from a sum of squares; 0 for a zero row.
 __device__ __forceinline__ float inv_norm(float ss) { return ss > 0.f ? rsqrtf(ss) : 0.f; }
 

@@ -32,13 +32,13 @@
 // are read with the gfx950 transposing LDS read.  The weight w multiplies
 // the X operand in fp32 before rounding to bf16.  Tail tokens of the last
 // chunk re-read the frame's last row and get weight 0, so they add exactly 0.
-// Normalised keys (NORM, forward only): K^ = s K / |K| per token row, with
-// the norms taken from the rows being staged, no pass over K of its own.
-// At commit every thread also stores the sum of squares of its 16-byte
-// key piece; a wave then adds, per token it weights, the pieces of its
-// head's row (one per lane of a DPP row, summed across it).  A_t gets
-// w / |k|^2 on the K rows, U_t gets w / |k| on the V rows, and the raw keys
-// stay the Y operand.
+// Normalised keys (NORM, forward only): K^ = s K / |K| per token row,
+// normalised on the way into LDS, no pass over K of its own.  The key
+// pieces are then dealt by whole head rows, one DPP row of 16 lanes per
+// row (two for fp32 rows of more than 16 pieces): each lane sums the
+// squares of its piece, the row's lanes add them up, and every lane
+// scales its piece by 1 / |k| before committing it; the products then run
+// on the normalised keys exactly as without NORM.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -65,7 +65,9 @@ struct GramCfg {
   static constexpr int PPT = NMAT * PPM;                    // pieces per thread
   static constexpr int NWT = CT * HPW;                      // weights per chunk
   static constexpr int PH = D * ES / 16;                    // 16-byte pieces per head row
-  static constexpr int NU = (PH + 15) / 16;                 // of them per lane of a DPP row
+  // NORM: key pieces by head rows, LPR lanes a row (pieces past PH idle)
+  static constexpr int LPR = PH <= 16 ? 16 : 32;
+  static constexpr int NK = CT * HPW * LPR;                 // lanes dealt key pieces
   // LDS row stride (elements).  A fragment read takes the same 16 bf16 (or
   // 16 fp32) columns of 4 consecutive token rows per group of lanes; rows
   // are padded so that those rows start on different banks of the 32
@@ -100,13 +102,12 @@ template <int IO, int NT, int NR, bool Y_IS_X0, int HPW, bool SPLIT, bool NORM>
 __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_kernel(GramArgs a) {
   typedef GramCfg<IO, NT, NR, Y_IS_X0, HPW> C;
   static_assert(!NORM || (NR == 2 && Y_IS_X0), "normalised keys: X_0 == Y == K, X_1 == V");
+  static_assert(!NORM || (C::NK <= C::NTH && C::PPM == 1), "one key piece per thread");
   typedef typename Io<IO>::elem E;
   constexpr int D = C::D, CT = C::CT, ES = C::ES, PR = C::PR, NTH = C::NTH;
   constexpr int LDR = C::LDR;
   __shared__ __attribute__((aligned(16))) E stage[2][C::STAGE_ELEMS];
   __shared__ float wstage[2][C::NWT];
-  // NORM: sums of squares of the key pieces, [token][piece of the row segment]
-  __shared__ float nstage[2][NORM ? CT * PR : 1];
 
   const int HG = a.H / HPW;                        // head groups
   const int total = a.B * a.Tc * HG * a.P;
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
 
   // Register ring: chunk c of an item: pieces q = tid + NTH j of each
   // staged matrix ([CT][row segment], rows LDR apart in LDS) and one weight
-  // ([token][head] of the group).  Loads are clamped, never skipped (past
+  // ([token][head] of the group).  (NORM: the keys' piece of thread tid is
+  // piece tid % LPR of head (tid / LPR) % HPW of token tid / (HPW LPR).)  Loads are clamped, never skipped (past
   // the item's last chunk, past the frame's last row, past the matrix's
   // last piece), so the loop stays straight-line and the compiler's wait
   // counts exact.  Addresses are a uniform 64-bit frame base plus 32-bit
@@ -164,9 +166,14 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
       for (int j = 0; j < C::PPM; ++j) {
         int q = tid + NTH * j;
         if (C::MPC % NTH != 0) q = q < C::MPC ? q : C::MPC - 1;
-        int tk = c0 + q / PR;
+        int row = q / PR, col = q % PR;
+        if (NORM && m == 0) {
+          row = min(tid / (HPW * C::LPR), CT - 1);
+          col = ((tid / C::LPR) % HPW) * C::PH + min(tid % C::LPR, C::PH - 1);
+        }
+        int tk = c0 + row;
         tk = tk < N ? tk : N - 1;
-        const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)((q % PR) * 16);
+        const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(col * 16);
         R.v[m * C::PPM + j] = *reinterpret_cast<const u32x4*>(base + off);
       }
     }
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
   };
   auto commit = [&](const Ring& R, int st, int nv) {   // nv: tokens of the chunk in the frame
 #pragma unroll
-    for (int m = 0; m < C::NMAT; ++m)
+    for (int m = NORM ? 1 : 0; m < C::NMAT; ++m)
 #pragma unroll
       for (int j = 0; j < C::PPM; ++j) {
         const int q = tid + NTH * j;
@@ -190,25 +197,17 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
           *reinterpret_cast<u32x4*>(&stage[st][(m * CT + q / PR) * LDR + (q % PR) * (16 / ES)]) =
               R.v[m * C::PPM + j];
       }
-    if constexpr (NORM) {   // matrix 0: the keys
-#pragma unroll
-      for (int j = 0; j < C::PPM; ++j) {
-        const int q = tid + NTH * j;
-        const u32x4 pc = R.v[j];
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (C::BF) {
-            const float lo = __uint_as_float(pc[e] << 16), hi = __uint_as_float(pc[e] & 0xffff0000u);
-            ss = fmaf(lo, lo, ss);
-            ss = fmaf(hi, hi, ss);
-          } else {
-            const float x = __uint_as_float(pc[e]);
-            ss = fmaf(x, x, ss);
-          }
-        }
-        if (C::MPC % NTH == 0 || q < C::MPC) nstage[st][q] = ss;
-      }
+    if constexpr (NORM) {   // the keys, by head rows
+      const int row = tid / (HPW * C::LPR), pc = tid % C::LPR;
+      const int col = ((tid / C::LPR) % HPW) * C::PH + pc;
+      const float live = (row < CT && pc < C::PH) ? 1.f : 0.f;   // from tid only
+      u32x4 v = R.v[0];
+      float ss = live * piece_sumsq<IO>(v);
+      ss = row_sum16(ss);
+      if constexpr (C::LPR == 32) ss += __shfl_xor(ss, 16);
+      v = piece_scale<IO>(v, inv_norm(ss));
+      if (row < CT && pc < C::PH)
+        *reinterpret_cast<u32x4*>(&stage[st][row * LDR + col * (16 / ES)]) = v;
     }
     // tokens past the frame's end get weight 0 (their rows are re-read copies)
     if (tid < C::NWT) wstage[st][tid] = tid / HPW < nv ? (has_w ? R.w : 1.0f) : 0.0f;
@@ -222,38 +221,15 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
       for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
   };
 
-  // NORM: this lane's share of |k|^2 for token tk of the chunk and this
-  // wave's head: pieces i, i + 16, .. of the head's row (lane i of its DPP row)
-  auto key_piece_sum = [&](int st, int tk) {
-    float ss = 0.f;
-    if constexpr (NORM) {
-#pragma unroll
-      for (int u = 0; u < C::NU; ++u) {
-        const int pc = li + 16 * u;
-        const float x = nstage[st][tk * PR + hp * C::PH + min(pc, C::PH - 1)];
-        ss += pc < C::PH ? x : 0.f;
-      }
-    }
-    return ss;
-  };
-
   auto compute = [&](int st) {
     // this wave's head: its D features at offset hp * D of each row segment
     const E* xs = &stage[st][hp * D];
     const E* ys = Y_IS_X0 ? xs : xs + (C::NMAT - 1) * CT * LDR;
     const float* ws = wstage[st];
     if constexpr (C::BF) {
-      float wv[8], wv1[8];   // weights of the X_0 and X_1 rows: token 8 g + e
+      float wv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wv[e] = wv1[e] = ws[(8 * g + e) * HPW + hp];
-      if constexpr (NORM) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float r = inv_norm(row_sum16(key_piece_sum(st, 8 * g + e)));
-          wv1[e] = wv[e] * r;
-          wv[e] = wv1[e] * r;
-        }
-      }
+      for (int e = 0; e < 8; ++e) wv[e] = ws[(8 * g + e) * HPW + hp];
       // the wave's weighted row fragments first, then one column fragment at
       // a time (few fragments live next to the accumulators)
       bf16x8 af[C::RT];
@@ -268,7 +244,7 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
                                   ft * 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          af[j][e] = static_cast<__bf16>(static_cast<float>(af[j][e]) * (m == 0 ? wv[e] : wv1[e]));
+          af[j][e] = static_cast<__bf16>(static_cast<float>(af[j][e]) * wv[e]);
       }
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
@@ -281,22 +257,16 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
 #pragma unroll 1
       for (int kb = 0; kb < CT / 4; ++kb) {
         const int k = kb * 4 + g;
-        float wv = ws[k * HPW + hp], wv1 = wv;
+        const float wv = ws[k * HPW + hp];
         float bfr[NT];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) bfr[ct] = reinterpret_cast<const float*>(ys)[k * LDR + ct * 16 + li];
-        if constexpr (NORM) {
-          const float r = inv_norm(row_sum16(key_piece_sum(st, k)));
-          wv1 = wv * r;
-          wv = wv1 * r;
-        }
 #pragma unroll
         for (int j = 0; j < C::RT; ++j) {
           const int m = j / C::RPM;   // see the bf16 path
           const int ft = min(wl + C::WPH * (j % C::RPM), NT - 1);
           const float af =
-              reinterpret_cast<const float*>(xs + m * CT * LDR)[k * LDR + ft * 16 + li] *
-              (m == 0 ? wv : wv1);
+              reinterpret_cast<const float*>(xs + m * CT * LDR)[k * LDR + ft * 16 + li] * wv;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) acc[j][ct] = mfma_f32(af, bfr[ct], acc[j][ct]);
         }

@@ -19,10 +19,13 @@
 // while stores are pending), and the barriers are LDS-only, so the PF - 1
 // chunks ahead stay in flight across them.  The loop over whole chunks is
 // straight-line; the frame's last, partial chunk is finished after it.
-// Normalised queries (NORM, forward only): o = S_t q / |q|.  A lane's
-// query fragments hold a quarter of its token's features, so the squares
-// it sums over them, added over the token's four lanes, give |q|^2; the
-// accumulators are scaled by 1 / |q| before rounding.
+// Normalised queries (NORM, forward only): o = S_t q / |q|, the
+// accumulators scaled by 1 / |q| before rounding.  bf16: the query
+// fragments of a 16-token tile are both operands of a second MFMA chain,
+// whose result Q Q^T holds |q_i|^2 on its diagonal (lane (i / 4, i),
+// register i % 4), read back by every lane of token i.  fp32: each lane
+// sums the squares of its quarter of the features, added over the
+// token's four lanes.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -148,8 +151,9 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
       for (int tt = 0; tt < CT / 16; ++tt) {
         f32x4 acc = zero4();
         const E* trow = ts + (tt * 16 + li) * RW + hp * D;
-        float ss = 0.f;   // NORM: squares of this lane's query features
+        float ss = 0.f;   // NORM: |q|^2 of this lane's token (fp32: its share)
         if constexpr (BF) {
+          f32x4 gram = zero4();   // NORM: Q Q^T of the tile's 16 tokens
 #pragma unroll
           for (int kb = 0; kb < KF; ++kb) {
             // past D the read runs into the next head or row (or the next
@@ -157,13 +161,12 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
             bf16x8 q = load_bf16x8(reinterpret_cast<const uint16_t*>(trow) + kb * 32 + 8 * g);
             if (KTAIL && kb == KF - 1 && kb * 32 + 8 * g >= D) q = zero_bf16x8();
             acc = mfma_bf16(sf[hp][kb], q, acc);
-            if constexpr (NORM) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float x = static_cast<float>(q[e]);
-                ss = fmaf(x, x, ss);
-              }
-            }
+            if constexpr (NORM) gram = mfma_bf16(q, q, gram);
+          }
+          if constexpr (NORM) {
+            const int r = li & 3;
+            const float dg = r == 0 ? gram[0] : r == 1 ? gram[1] : r == 2 ? gram[2] : gram[3];
+            ss = __shfl(dg, ((li >> 2) << 4) | li);   // lane (i / 4, i)
           }
         } else {
 #pragma unroll
@@ -174,8 +177,10 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
           }
         }
         if constexpr (NORM) {   // token tt * 16 + i sits in lanes i, i + 16, i + 32, i + 48
-          ss += __shfl_xor(ss, 16);
-          ss += __shfl_xor(ss, 32);
+          if constexpr (!BF) {
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+          }
           acc *= inv_norm(ss);
         }
         E* dst = ob + (tt * 16 + li) * RW + hp * D + ft * 16 + 4 * g;

@@ -9,9 +9,10 @@
 // chain rule here:
 //   x^ = x / |x|:      dx = (dx^ - x^ (x^ . dx^)) / |x|   (0 for a zero row)
 //   p = sigmoid(z):    dz = dp p (1 - p)
-// One thread per gate or per row of d io elements (16-byte pieces, two
-// passes: the sums, then the rewritten row, which the first pass left in
-// cache).
+// One thread per gate; a row of d io elements takes one 16-byte piece per
+// lane on 16 lanes (a DPP row; 32 lanes for fp32 rows of more than 16
+// pieces), so a wave reads whole rows contiguously and the row's sums
+// come from a cross-lane reduction.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -69,68 +70,67 @@ template <> struct Piece<IO_F32> {
   }
 };
 
-template <int IO>
-__global__ __launch_bounds__(kPrologueThreads) void rows_normalize_kernel(const void* x, void* y,
-                                                                         int64_t rows, int d) {
-  typedef Piece<IO> P;
-  const int64_t r = (int64_t)blockIdx.x * kPrologueThreads + threadIdx.x;
-  if (r >= rows) return;
-  const int np = d / P::n;
-  const u32x4* xr = reinterpret_cast<const u32x4*>(x) + r * np;
-  u32x4* yr = reinterpret_cast<u32x4*>(y) + r * np;
-  float ss = 0.f;
-  for (int p = 0; p < np; ++p) {
-    float f[P::n];
-    P::get(xr[p], f);
-#pragma unroll
-    for (int e = 0; e < P::n; ++e) ss = fmaf(f[e], f[e], ss);
-  }
-  const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-  for (int p = 0; p < np; ++p) {
-    float f[P::n];
-    P::get(xr[p], f);
-#pragma unroll
-    for (int e = 0; e < P::n; ++e) f[e] *= inv;
-    yr[p] = P::put(f);
-  }
+// Sum over the LPR lanes of a row (a DPP row, or two adjacent ones).
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  v = row_sum16(v);
+  if constexpr (LPR == 32) v += __shfl_xor(v, 16);
+  return v;
 }
 
-template <int IO>
+template <int IO, int LPR>
+__global__ __launch_bounds__(kPrologueThreads) void rows_normalize_kernel(const void* x, void* y,
+                                                                         int64_t rows, int ph) {
+  const int64_t r = (int64_t)blockIdx.x * (kPrologueThreads / LPR) + threadIdx.x / LPR;
+  const int pc = threadIdx.x % LPR;
+  const bool live = r < rows && pc < ph;
+  // every lane takes part in the row sums: no early return
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (live) v = reinterpret_cast<const u32x4*>(x)[r * ph + pc];
+  const float ss = row_sum<LPR>(piece_sumsq<IO>(v));
+  const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+  if (live) reinterpret_cast<u32x4*>(y)[r * ph + pc] = piece_scale<IO>(v, inv);
+}
+
+template <int IO, int LPR>
 __global__ __launch_bounds__(kPrologueThreads) void rows_normalize_bwd_kernel(const void* x,
                                                                              void* g,
-                                                                             int64_t rows, int d) {
+                                                                             int64_t rows, int ph) {
   typedef Piece<IO> P;
-  const int64_t r = (int64_t)blockIdx.x * kPrologueThreads + threadIdx.x;
-  if (r >= rows) return;
-  const int np = d / P::n;
-  const u32x4* xr = reinterpret_cast<const u32x4*>(x) + r * np;
-  u32x4* gr = reinterpret_cast<u32x4*>(g) + r * np;
-  float ss = 0.f, dot = 0.f;
-  for (int p = 0; p < np; ++p) {
-    float f[P::n], h[P::n];
-    P::get(xr[p], f);
-    P::get(gr[p], h);
-#pragma unroll
-    for (int e = 0; e < P::n; ++e) {
-      ss = fmaf(f[e], f[e], ss);
-      dot = fmaf(f[e], h[e], dot);
-    }
+  const int64_t r = (int64_t)blockIdx.x * (kPrologueThreads / LPR) + threadIdx.x / LPR;
+  const int pc = threadIdx.x % LPR;
+  const bool live = r < rows && pc < ph;
+  u32x4 xv = u32x4{0u, 0u, 0u, 0u}, gv = xv;
+  if (live) {
+    xv = reinterpret_cast<const u32x4*>(x)[r * ph + pc];
+    gv = reinterpret_cast<const u32x4*>(g)[r * ph + pc];
   }
+  float f[P::n], h[P::n];
+  P::get(xv, f);
+  P::get(gv, h);
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < P::n; ++e) {
+    ss = fmaf(f[e], f[e], ss);
+    dot = fmaf(f[e], h[e], dot);
+  }
+  ss = row_sum<LPR>(ss);
+  dot = row_sum<LPR>(dot);
   // dx = (g - x^ (x^ . g)) / |x| = g inv - x (x . g) inv^3
   const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
   const float c = dot * inv * inv;
-  for (int p = 0; p < np; ++p) {
-    float f[P::n], h[P::n];
-    P::get(xr[p], f);
-    P::get(gr[p], h);
 #pragma unroll
-    for (int e = 0; e < P::n; ++e) h[e] = (h[e] - f[e] * c) * inv;
-    gr[p] = P::put(h);
-  }
+  for (int e = 0; e < P::n; ++e) h[e] = (h[e] - f[e] * c) * inv;
+  if (live) reinterpret_cast<u32x4*>(g)[r * ph + pc] = P::put(h);
 }
 
 static dim3 grid_for(int64_t n) {
   return dim3((unsigned)((n + kPrologueThreads - 1) / kPrologueThreads));
+}
+// rows of ph pieces, LPR lanes a row
+static dim3 grid_rows(int64_t rows, int lpr) {
+  const int64_t per = kPrologueThreads / lpr;
+  return dim3((unsigned)((rows + per - 1) / per));
 }
 
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s) {
@@ -148,26 +148,36 @@ hipError_t launch_sigmoid_bwd(const float* x, float* g, int64_t n, hipStream_t s
 hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, int io,
                                  hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d % 16 != 0) return hipErrorInvalidValue;
+  const int ph = d * (io == IO_BF16 ? 2 : 4) / 16;
+  if (d % 16 != 0 || ph > (io == IO_BF16 ? 16 : 32)) return hipErrorInvalidValue;
+  const dim3 blk(kPrologueThreads);
   if (io == IO_BF16)
-    hipLaunchKernelGGL(rows_normalize_kernel<IO_BF16>, grid_for(rows), dim3(kPrologueThreads), 0,
-                       s, x, y, rows, d);
+    hipLaunchKernelGGL((rows_normalize_kernel<IO_BF16, 16>), grid_rows(rows, 16), blk, 0, s, x, y,
+                       rows, ph);
+  else if (ph <= 16)
+    hipLaunchKernelGGL((rows_normalize_kernel<IO_F32, 16>), grid_rows(rows, 16), blk, 0, s, x, y,
+                       rows, ph);
   else
-    hipLaunchKernelGGL(rows_normalize_kernel<IO_F32>, grid_for(rows), dim3(kPrologueThreads), 0,
-                       s, x, y, rows, d);
+    hipLaunchKernelGGL((rows_normalize_kernel<IO_F32, 32>), grid_rows(rows, 32), blk, 0, s, x, y,
+                       rows, ph);
   return hipGetLastError();
 }
 
 hipError_t launch_rows_normalize_bwd(const void* x, void* g, int64_t rows, int d, int io,
                                      hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d % 16 != 0) return hipErrorInvalidValue;
+  const int ph = d * (io == IO_BF16 ? 2 : 4) / 16;
+  if (d % 16 != 0 || ph > (io == IO_BF16 ? 16 : 32)) return hipErrorInvalidValue;
+  const dim3 blk(kPrologueThreads);
   if (io == IO_BF16)
-    hipLaunchKernelGGL(rows_normalize_bwd_kernel<IO_BF16>, grid_for(rows), dim3(kPrologueThreads),
-                       0, s, x, g, rows, d);
+    hipLaunchKernelGGL((rows_normalize_bwd_kernel<IO_BF16, 16>), grid_rows(rows, 16), blk, 0, s,
+                       x, g, rows, ph);
+  else if (ph <= 16)
+    hipLaunchKernelGGL((rows_normalize_bwd_kernel<IO_F32, 16>), grid_rows(rows, 16), blk, 0, s,
+                       x, g, rows, ph);
   else
-    hipLaunchKernelGGL(rows_normalize_bwd_kernel<IO_F32>, grid_for(rows), dim3(kPrologueThreads),
-                       0, s, x, g, rows, d);
+    hipLaunchKernelGGL((rows_normalize_bwd_kernel<IO_F32, 32>), grid_rows(rows, 32), blk, 0, s,
+                       x, g, rows, ph);
   return hipGetLastError();
 }
 
