@@ -356,7 +356,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   GramArgs ga{};
   ga.x0 = k; ga.x1 = v; ga.y = k; ga.w = beta;
   ga.out0 = A; ga.out1 = U;
-  ga.layout0 = LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
+  ga.layout0 = s.io == IO_BF16 ? LAYOUT_FRAG : LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
   ga.scale0 = s.s * s.s; ga.scale1 = s.s;
   ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
   ga.t0 = 0; ga.Tc = (int)s.T;
@@ -555,7 +555,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     void* U_ = ws + 2 * s.mat;
     GramArgs ga{};
     ga.x0 = k; ga.x1 = v; ga.y = k; ga.w = beta; ga.out0 = A_; ga.out1 = U_;
-    ga.layout0 = LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
+    ga.layout0 = s.io == IO_BF16 ? LAYOUT_FRAG : LAYOUT_ROWMAJOR; ga.layout1 = LAYOUT_TILES;
     ga.scale0 = s.s * s.s; ga.scale1 = s.s;
     ga.B = (int)s.B; ga.H = (int)s.H; ga.T = (int)s.T; ga.N = (int)s.N;
     ga.t0 = 0; ga.Tc = (int)s.T;

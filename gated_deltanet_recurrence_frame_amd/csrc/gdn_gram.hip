@@ -18,8 +18,9 @@
 // the scan consumes.
 //
 // Layout of the work: one workgroup per (b, t) frame and pair of adjacent
-// heads (16 waves, one per CU) when H is even, else per single head (8
-// waves, two per CU); 8 waves share a head's row tiles.  XCD-aware ordering
+// heads (one per CU) when H is even, else per single head (two per CU); a
+// head's row tiles are shared by up to 8 waves, one tile each when there
+// are 5 to 8 tiles (head dims 80 to 128).  XCD-aware ordering
 // so the heads of one frame run together on one XCD.  Tokens stream through
 // LDS in chunks of CT rows (natural [token][feature] layout, the head
 // group's row segments side by side, double-buffered); each thread loads
@@ -46,14 +47,17 @@
 
 namespace gdn {
 
-constexpr int GRAM_WPH = 8;   // waves per head: 8 x 64 threads share a head's row tiles
+// Waves per head: one per 16-row tile of the products from 5 tiles up (no
+// wave repeats another's tile), else 8 (the smaller heads' tiles repeated).
+// NORM deals a chunk's key rows 16 lanes a row and keeps 8.
+constexpr int gram_wph(int nt, bool norm) { return (nt >= 5 && !norm) ? nt : 8; }
 
-template <int IO, int NT, int NR, bool Y_IS_X0, int HPW>
+template <int IO, int NT, int NR, bool Y_IS_X0, int HPW, bool NORM>
 struct GramCfg {
   static constexpr bool BF = (IO == IO_BF16);
   static constexpr int D = 16 * NT;
   static constexpr int ES = Io<IO>::bytes;
-  static constexpr int WPH = GRAM_WPH;                      // waves per head
+  static constexpr int WPH = gram_wph(NT, NORM);            // waves per head
   static constexpr int NW = WPH * HPW;                      // waves
   static constexpr int NTH = 64 * NW;
   static constexpr int RW = HPW * D;                        // elements of a token's row segment
@@ -99,8 +103,9 @@ struct GramItem {
 // partials; a compile-time choice, so that no branch joins stores of the two
 // kinds (the compiler would lose its count of the stores in flight).
 template <int IO, int NT, int NR, bool Y_IS_X0, int HPW, bool SPLIT, bool NORM>
-__global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_kernel(GramArgs a) {
-  typedef GramCfg<IO, NT, NR, Y_IS_X0, HPW> C;
+__global__ __launch_bounds__(64 * gram_wph(NT, NORM) * HPW, HPW == 1 ? 2 : 1) void gram_kernel(
+    GramArgs a) {
+  typedef GramCfg<IO, NT, NR, Y_IS_X0, HPW, NORM> C;
   static_assert(!NORM || (NR == 2 && Y_IS_X0), "normalised keys: X_0 == Y == K, X_1 == V");
   static_assert(!NORM || (C::NK <= C::NTH && C::PPM == 1), "one key piece per thread");
   typedef typename Io<IO>::elem E;
@@ -329,12 +334,14 @@ __global__ __launch_bounds__(64 * GRAM_WPH * HPW, HPW == 1 ? 2 : 1) void gram_ke
         const int ft = min(wl + C::WPH * (j % C::RPM) * jm, NT - 1);
         const float sc = (m == 0 ? a.scale0 : a.scale1);
         E* out = static_cast<E*>(m == 0 ? a.out0 : a.out1) + obase;
-        const bool tiles = (m == 0 ? a.layout0 : a.layout1) == LAYOUT_TILES;
-        // tiles: tile [ft][ct], this lane's slot; row-major (transposed
-        // tile): row 16 ct + i, columns 16 ft + 4g .. + 3.  Both are
-        // base + ct * stride.
-        E* base = tiles ? out + (ft * NT * 64 + lane) * 4 : out + li * D + ft * 16 + 4 * g;
-        const int stride = (tiles ? 256 : 16 * D) * jm;
+        const int lay = m == 0 ? a.layout0 : a.layout1;
+        // tiles: tile [ft][ct], this lane's slot; row-major or fragments
+        // (transposed tile): row 16 ct + i, columns 16 ft + 4g .. + 3.  All
+        // are base + ct * stride.
+        E* base = lay == LAYOUT_TILES ? out + (ft * NT * 64 + lane) * 4
+                  : lay == LAYOUT_FRAG ? out + frag_index(li, ft * 16 + 4 * g, D)
+                                       : out + li * D + ft * 16 + 4 * g;
+        const int stride = (lay == LAYOUT_TILES ? 256 : 16 * D) * jm;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) pack(sc * acc[j][ct], base + ct * stride);
       }
@@ -430,9 +437,11 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs a) {
       *reinterpret_cast<f32x4*>(dst) = sum;
     }
   } else {
+    const bool frag = (m == 0 ? a.layout0 : a.layout1) == LAYOUT_FRAG;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      E* dst = out + (ft * 16 + 4 * g + r) * D + ct * 16 + li;
+      const int R = ft * 16 + 4 * g + r, Cc = ct * 16 + li;
+      E* dst = out + (frag ? frag_index(R, Cc, D) : (long)R * D + Cc);
       if constexpr (IO == IO_BF16)
         *dst = f32_to_bf16_bits(sum[r]);
       else
@@ -483,6 +492,13 @@ static int gram_slots(int hpw) {
   return cus * (hpw == 2 ? 1 : 2);
 }
 
+template <int IO, int NT, int NR, bool YX, int HPW, bool SPLIT, bool NORM>
+static void launch_one(const GramArgs& a, int grid, hipStream_t s) {
+  typedef GramCfg<IO, NT, NR, YX, HPW, NORM> C;
+  hipLaunchKernelGGL((gram_kernel<IO, NT, NR, YX, HPW, SPLIT, NORM>), dim3(grid),
+                     dim3(64 * C::WPH * HPW), 0, s, a);
+}
+
 template <int IO, int NT, int HPW>
 static void launch_gram_hpw(const GramArgs& a, int nr, hipStream_t s) {
   // persistent: at most one workgroup per slot, a multiple of 8 so that a
@@ -491,21 +507,20 @@ static void launch_gram_hpw(const GramArgs& a, int nr, hipStream_t s) {
   int grid = gram_slots(HPW);
   grid -= grid % 8;
   if (total < grid) grid = total;
-  const dim3 block(64 * GRAM_WPH * HPW);
   if (a.P > 1) {
     if (nr == 2 && a.norm)
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, true, true>), dim3(grid), block, 0, s, a);
+      launch_one<IO, NT, 2, true, HPW, true, true>(a, grid, s);
     else if (nr == 2)
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, true, false>), dim3(grid), block, 0, s, a);
+      launch_one<IO, NT, 2, true, HPW, true, false>(a, grid, s);
     else
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, true, false>), dim3(grid), block, 0, s, a);
+      launch_one<IO, NT, 1, false, HPW, true, false>(a, grid, s);
   } else {
     if (nr == 2 && a.norm)
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, false, true>), dim3(grid), block, 0, s, a);
+      launch_one<IO, NT, 2, true, HPW, false, true>(a, grid, s);
     else if (nr == 2)
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 2, true, HPW, false, false>), dim3(grid), block, 0, s, a);
+      launch_one<IO, NT, 2, true, HPW, false, false>(a, grid, s);
     else
-      hipLaunchKernelGGL((gram_kernel<IO, NT, 1, false, HPW, false, false>), dim3(grid), block, 0, s, a);
+      launch_one<IO, NT, 1, false, HPW, false, false>(a, grid, s);
   }
 }
 

@@ -8,13 +8,23 @@
 namespace gdn {
 
 // Per-frame D x D intermediates are stored in the "intermediate type": bf16
-// when the io dtype is bf16, fp32 when it is fp32.  Two layouts:
+// when the io dtype is bf16, fp32 when it is fp32.  Three layouts:
 //   row-major  [D][D];
 //   tiles      [D/16][D/16][64][4]: 16x16 tile (I, J), lane (g, i) holds
 //              the elements [16 I + 4 g + r][16 J + i], r = 0..3 (the MFMA
 //              accumulator layout, so a consumer in the same layout reads
-//              4 contiguous values per lane).
-enum MatLayout { LAYOUT_ROWMAJOR = 0, LAYOUT_TILES = 1 };
+//              4 contiguous values per lane);
+//   fragments  (bf16 only) the bf16 MFMA operand order of 16-row blocks:
+//              element [R][C] at frag_index(R, C, D), so that the 64 lanes
+//              of a wave reading rows 16 I .. + 15, columns 32 k .. + 31 as
+//              an operand (lane (g, i): row 16 I + i, columns 32 k + 8 g ..
+//              + 7) read one contiguous 1 KB piece (512 B for the last,
+//              16-column block when D % 32 == 16).  Same size as row-major.
+enum MatLayout { LAYOUT_ROWMAJOR = 0, LAYOUT_TILES = 1, LAYOUT_FRAG = 2 };
+__host__ __device__ inline long frag_index(int R, int C, int D) {
+  return (long)(R >> 4) * 16 * D + (C >> 5) * 512 + ((((C & 31) >> 3) << 4) + (R & 15)) * 8 +
+         (C & 7);
+}
 
 // Token contraction C_r = scale_r X_r^T diag(w) Y per (b, t, h) frame.
 struct GramArgs {
@@ -34,9 +44,9 @@ struct GramArgs {
   // launch_gram_reduce then sums them in a fixed order into out0 / out1.
   int P;
   float* part;
-  // Normalised keys (NR == 2, Y == X_0 == K, X_1 == V): every token's row is
-  // taken as k / |k|, so X_0's weight becomes w / |k|^2 and X_1's w / |k|,
-  // with |k| from the staged rows of Y (a zero row gets weight 0).
+  // Normalised keys (NR == 2, Y == X_0 == K, X_1 == V): every token's key
+  // row is taken as k / |k| (a zero row stays zero), normalised as it is
+  // staged.
   int norm;
 };
 hipError_t launch_gram(const GramArgs& a, int io, int nt, int nr, hipStream_t s);
@@ -64,7 +74,7 @@ hipError_t launch_gram_reduce(const GramArgs& a, int io, int nt, int nr, hipStre
 //     sequential walk does; only the last chunk writes zT.
 enum ScanMode { SCAN_FWD = 0, SCAN_REV = 1, SCAN_COMP_FWD = 2, SCAN_COMP_REV = 3 };
 struct ScanArgs {
-  const void* A;        // [B, H, T] x D x D row-major, intermediate type
+  const void* A;        // [B, H, T] x D x D, intermediate type: fragments (bf16), row-major (fp32)
   const void* U;        // [B, H, T] x D x D tiles, intermediate type
   const float* gamma;   // [B, T, H], or nullptr for 0
   const float* z0;

@@ -135,11 +135,14 @@ const char* gdn_status_string(int status);
 gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes);
 
 /* Bytes of the optional forward->backward buffer `saved` (written to
- * *bytes).  Layout: A_t = K^_t beta_t K^_t^T as [B, H, T, Dk, Dk], followed
- * by the states S_t after every frame as [B, H, T, Dv, Dk], row-major, in
- * the intermediate type: bf16 (round to nearest even) when io_dtype is
- * GDN_BF16, fp32 when it is GDN_FP32.  GDN_ERR_UNSUPPORTED for the token
- * form, which keeps neither. */
+ * *bytes).  Layout: A_t = K^_t beta_t K^_t^T as [B, H, T] x Dk x Dk,
+ * followed by the states S_t after every frame as [B, H, T, Dv, Dk]
+ * row-major, in the intermediate type: bf16 (round to nearest even) when
+ * io_dtype is GDN_BF16, fp32 when it is GDN_FP32.  fp32 A_t is row-major;
+ * bf16 A_t is in the MFMA operand order of the scan: element [r][c] of a
+ * frame's A_t at (r / 16) 16 Dk + (c / 32) 512 + (16 ((c % 32) / 8) +
+ * r % 16) 8 + c % 8.  GDN_ERR_UNSUPPORTED for the token form, which keeps
+ * neither. */
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
 
 /* Whole-sequence forward (module 2 recurrence over t = 1..T):
