@@ -31,9 +31,9 @@ CSRC = os.path.join(HERE, "csrc")
 
 # kernel (short name) -> (name fragment in the trace, source files it is built from)
 KERNELS = {
-    "gram": ("gram_kernel<0, 7, 2, true, 2, false>", ["gdn_gram.hip", "gdn_device.h", "gdn_internal.h"]),
+    "gram": ("gram_kernel<0, 7, 2, true, 2, false, false>", ["gdn_gram.hip", "gdn_device.h", "gdn_internal.h"]),
     "scan": ("scan_kernel<0, 7, 0>", ["gdn_scan.hip", "gdn_device.h", "gdn_internal.h"]),
-    "output": ("output_kernel<0, 7, false, 2>", ["gdn_output.hip", "gdn_device.h", "gdn_internal.h"]),
+    "output": ("output_kernel<0, 7, false, 2, false>", ["gdn_output.hip", "gdn_device.h", "gdn_internal.h"]),
 }
 
 
