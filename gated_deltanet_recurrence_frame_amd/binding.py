@@ -108,7 +108,7 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-ALGORITHMS = {"auto": 0, "frame": 1, "token": 2}
+ALGORITHMS = {"auto": 0, "frame": 1, "token": 2, "direct": 3}
 GDN_FLAG_NORMALIZE_QK, GDN_FLAG_GATE_LOGITS = 1, 2
 
 
@@ -229,12 +229,12 @@ def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, scan_chunk=0,
 
 
 def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None,
-         normalize_qk=False, gate_logits=False):
+         normalize_qk=False, gate_logits=False, algorithm="auto"):
     """One streaming frame: q, k, v [B, N, H, D], gamma [B, 1, H], beta
     [B, N, H]; `state` [B, H, D, D] fp32 is updated in place.  Returns o."""
     B, N, H, D, T, dev = _shapes(q, k, v, gamma, beta, q.shape[1])
     _need(state, "state", torch.float32, (B, H, D, D), dev)
-    prob = make_problem(B, H, 1, N, D, _io_of(q), key_scale, 0,
+    prob = make_problem(B, H, 1, N, D, _io_of(q), key_scale, 0, algorithm,
                         flags=flags_of(normalize_qk, gate_logits))
     o = out if out is not None else torch.empty_like(v)
     if workspace is None:

@@ -15,8 +15,10 @@ namespace {
 
 constexpr int kDefaultChunk = 1;   // sequential scan unless asked otherwise
 // GDN_ALGO_AUTO takes the token form for frames of at most this many tokens
-// (0: never; the frame form is the default everywhere)
+// (0: never), the direct form for bf16 launches of at most this many frames
+// (streaming steps, short windows), else the frame form
 constexpr int kTokenAutoMaxN = 0;
+constexpr int kDirectAutoMaxT = 2;
 
 struct Shape {
   int64_t B, H, T, N, D, L;
@@ -28,6 +30,8 @@ struct Shape {
                      // type (bf16 for bf16 io, fp32 for fp32 io)
   int64_t parts;     // composite chunks per sequence
   bool token;        // forward in token form (chunks of frames, no D x D per frame)
+  bool direct;       // forward in direct form (frames in turn, from the token rows)
+  int algo;          // the problem's gdn_algorithm
   bool norm;         // GDN_FLAG_NORMALIZE_QK
   bool gates;        // GDN_FLAG_GATE_LOGITS
 };
@@ -40,7 +44,7 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (p->scan_chunk < 0) return GDN_ERR_BAD_SHAPE;
   if (!isfinite(p->key_scale)) return GDN_ERR_BAD_SHAPE;
   if (p->Dk != p->Dv || p->Dk % 16 != 0 || p->Dk > 128) return GDN_ERR_UNSUPPORTED;
-  if (p->algorithm < GDN_ALGO_AUTO || p->algorithm > GDN_ALGO_TOKEN) return GDN_ERR_UNSUPPORTED;
+  if (p->algorithm < GDN_ALGO_AUTO || p->algorithm > GDN_ALGO_DIRECT) return GDN_ERR_UNSUPPORTED;
   if (p->flags & ~(GDN_FLAG_NORMALIZE_QK | GDN_FLAG_GATE_LOGITS)) return GDN_ERR_UNSUPPORTED;
   Shape s;
   s.B = p->B; s.H = p->H; s.T = p->T; s.N = p->N; s.D = p->Dk;
@@ -65,6 +69,11 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
   if (p->algorithm == GDN_ALGO_TOKEN && s.N > tok_max) return GDN_ERR_UNSUPPORTED;
   s.token = p->algorithm == GDN_ALGO_TOKEN ||
             (p->algorithm == GDN_ALGO_AUTO && s.N <= kTokenAutoMaxN);
+  if (p->algorithm == GDN_ALGO_DIRECT && s.io != IO_BF16) return GDN_ERR_UNSUPPORTED;
+  s.direct = p->algorithm == GDN_ALGO_DIRECT ||
+             (p->algorithm == GDN_ALGO_AUTO && !s.token && s.io == IO_BF16 &&
+              s.T <= kDirectAutoMaxT);
+  s.algo = p->algorithm;
   s.norm = (p->flags & GDN_FLAG_NORMALIZE_QK) != 0;
   s.gates = (p->flags & GDN_FLAG_GATE_LOGITS) != 0;
   *sh = s;
@@ -164,8 +173,11 @@ int64_t forward_base(const Shape& s) {
   return round256(s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
 }
 int64_t backward_base(const Shape& s) { return round256(6 * s.mat + scratch_bytes(s)); }
+// The direct form takes normalised copies of q and k too; it falls back to
+// the frame form (same workspace start) when a saved buffer is asked for.
+bool forward_copies(const Shape& s) { return s.token || s.direct; }
 int64_t forward_ws(const Shape& s) {
-  const int64_t pro = prologue_layout(s, s.token).end;
+  const int64_t pro = prologue_layout(s, forward_copies(s)).end;
   return pro ? forward_base(s) + pro : (s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
 }
 int64_t backward_ws(const Shape& s) {
@@ -337,17 +349,42 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
                        hipStream_t stream, void* const* events = nullptr) {
   char* ws = static_cast<char*>(workspace);
   // phases: the token form's prologue and passes all count as the output
-  // phase; the frame form's prologue as part of the Gram/write phase
+  // phase; the frame and direct forms' prologue as part of the Gram/write
+  // phase, the direct form's update as the scan phase
   gdn_status st = GDN_OK;
   for (int i = 0; i < (s.token ? 3 : 1) && st == GDN_OK; ++i) st = record(events, i, stream);
   if (st != GDN_OK) return st;
-  // the prologue's gates (and, for the token form, normalised rows)
+  // the prologue's gates (and, for the token and direct forms, normalised rows)
+  const bool direct = s.direct && !saved;
   Inputs in;
-  st = run_prologue(s, s.token, q, k, gamma, beta, ws + forward_base(s), &in, stream);
+  st = run_prologue(s, s.token || direct, q, k, gamma, beta, ws + forward_base(s), &in, stream);
   if (st != GDN_OK) return st;
   q = in.q; k = in.k; gamma = in.gamma; beta = in.beta;
   if (s.token)
     return run_token(s, q, k, v, gamma, beta, state_in, o, state_out, workspace, stream, events);
+  if (direct) {
+    // the state update in direct form (the scan phase), then the outputs
+    // from the emitted states
+    void* S = ws + s.mat;
+    DirectArgs da{};
+    da.k = k; da.v = v; da.gamma = gamma; da.beta = beta;
+    da.z0 = state_in; da.emit = S; da.zT = state_out; da.s = s.s;
+    da.B = (int)s.B; da.H = (int)s.H; da.T = (int)s.T; da.N = (int)s.N;
+    st = record(events, 1, stream);
+    if (st != GDN_OK) return st;
+    st = hip_status(launch_direct(da, (int)(s.D / 16), stream));
+    if (st != GDN_OK) return st;
+    st = record(events, 2, stream);
+    if (st != GDN_OK) return st;
+    OutArgs oa{};
+    oa.tok = q; oa.mat = S; oa.out = o;
+    oa.B = (int)s.B; oa.H = (int)s.H; oa.T = (int)s.T; oa.N = (int)s.N;
+    oa.t0 = 0; oa.Tc = (int)s.T;
+    oa.P = out_splits(s);
+    st = hip_status(launch_output(oa, s.io, (int)(s.D / 16), false, stream));
+    if (st != GDN_OK) return st;
+    return record(events, 3, stream);
+  }
   void* A = saved ? saved : ws;
   void* S = saved ? static_cast<char*>(saved) + s.mat : ws + s.mat;
   void* U = ws + 2 * s.mat;
@@ -430,7 +467,9 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes) {
   Shape s;
   gdn_status st = check_problem(p, &s);
   if (st != GDN_OK) return st;
-  if (s.token) return GDN_ERR_UNSUPPORTED;   // the token form keeps no A_t, S_t
+  // the token and direct forms keep no A_t, S_t (GDN_ALGO_AUTO's direct
+  // form gives way to the frame form when a saved buffer is passed)
+  if (s.token || s.algo == GDN_ALGO_DIRECT) return GDN_ERR_UNSUPPORTED;
   *bytes = (size_t)(2 * s.mat);
   return GDN_OK;
 }
@@ -449,7 +488,8 @@ static gdn_status forward_checked(const gdn_problem* p, const void* q, const voi
     if (x && !aligned16(x)) return GDN_ERR_MISALIGNED;
   if (!aligned4(gamma) || !aligned4(beta)) return GDN_ERR_MISALIGNED;
   if ((int64_t)workspace_bytes < forward_ws(s)) return GDN_ERR_WORKSPACE_TOO_SMALL;
-  if (s.token && saved) return GDN_ERR_UNSUPPORTED;   // no per-frame intermediates
+  if ((s.token || s.algo == GDN_ALGO_DIRECT) && saved)
+    return GDN_ERR_UNSUPPORTED;   // no per-frame intermediates
   const int64_t tok = s.B * s.L * s.H * s.D * s.es;
   const int64_t stb = s.B * s.H * s.D * s.D * 4;
   const Span ins[] = {{q, tok}, {k, tok}, {v, tok}, {gamma, s.B * s.T * s.H * 4},

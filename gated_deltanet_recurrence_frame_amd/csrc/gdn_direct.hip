@@ -1,0 +1,252 @@
+// Direct form of the frame-wise GDN state update for short launches
+// (streaming steps, short windows): the frames are walked one after the
+// other and every step works on the token rows themselves, with no
+// per-frame D x D products.
+//
+// The module-2 update of the summary page (方法步骤详情), S_t = S_{t-1}
+// (gamma_t I - K^_t beta_t K^_t^T) + V_t beta_t K^_t^T with K^ = s K, is,
+// token by token of the frame (all of them read S_{t-1}),
+//     S_t = gamma_t S_{t-1} + sum_n beta_n r_n k_n^T,
+//     r_n = s v_n - s^2 S_{t-1} k_n.
+// Rows of S evolve independently, so a workgroup owns 16 rows of one head's
+// state (one wave per 16-column tile, the tile in fp32 registers).  Per
+// frame it stages its rows of S_{t-1} in LDS (bf16) as MFMA operands, stores
+// them as the previous frame's state, and streams the frame's keys in
+// chunks of 128 tokens through LDS: per 16-token tile P = S_{t-1} K^T (keys
+// read as rows), R = s V^T - s^2 P scaled by beta (values of its 16 rows
+// read straight from memory), staged in LDS; then the update R K (keys read
+// with the transposing LDS read) accumulates in every wave's tile.  The
+// chunks of all frames form one sequence whose keys, values and gates ride
+// in a register ring PK chunks ahead, across frame boundaries.  The states
+// S_t go to the caller's buffer (bf16 row-major, as the scan emits them),
+// from which the output kernel forms O_t = S_t Q_t for all frames at once.
+// The same products as the frame form, with the state as one operand of
+// each: one launch, sequential over frames, parallel over heads and row
+// blocks.  It pays where the frame form's fixed costs (token splits of the
+// Gram/write pass, their reduction, the scan launch) dominate: a handful
+// of frames.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+template <int NT>
+__global__ __launch_bounds__(64 * NT) void direct_kernel(DirectArgs a) {
+  typedef uint16_t E;                            // bf16 bits
+  constexpr int D = 16 * NT;
+  constexpr int KB = (D + 31) / 32;              // MFMA k blocks over the features
+  constexpr int CK = 128;                        // tokens per chunk
+  constexpr int TT = CK / 16;                    // 16-token tiles per chunk
+  constexpr int NW = NT;                         // waves
+  constexpr int NTH = 64 * NW;
+  constexpr int KPR = D * 2 / 16;                // 16-byte pieces per key row
+  constexpr int KPT = CK * KPR / NTH;            // of a chunk per thread
+  constexpr int TPW = (TT + NW - 1) / NW;        // P tiles per wave
+  constexpr int VPC = CK * 2;                    // 16-byte value pieces of a chunk
+  constexpr int VPT = (VPC + NTH - 1) / NTH;     // of them per thread
+  constexpr int BPT = (CK + NTH - 1) / NTH;      // gates per thread
+  constexpr int ZLD = D + 8;                     // staged state row (elements)
+  constexpr int RLD = CK + 8;                    // staged R row (elements)
+  constexpr int PK = 3;                          // chunks in flight
+  static_assert(KPT * NTH == CK * KPR, "key pieces split evenly");
+  static_assert(16 * (D / 4) == NTH, "one 4-element piece of the staged rows per thread");
+  __shared__ __attribute__((aligned(16))) E Kst[2][CK * D];
+  __shared__ __attribute__((aligned(16))) E Rs[2][16 * RLD];
+  __shared__ __attribute__((aligned(16))) E Zs[16 * ZLD];
+  __shared__ __attribute__((aligned(16))) E Vs[2][CK * 16];       // values of the 16 rows
+  __shared__ float bs[2][CK];                                     // gates of the tokens
+  __shared__ float gs[2];                                         // the frame's decay
+
+  const int total = a.B * a.H * NT;
+  const int item = xcd_item(blockIdx.x, total);
+  const int rb = item % NT;
+  const int bh = item / NT;
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, li = lane & 15;
+  const int N = a.N, H = a.H, T = a.T;
+  const float s = a.s, s2 = a.s * a.s;
+  const long DD = (long)D * D;
+  const E* kp = static_cast<const E*>(a.k);
+  const E* vp = static_cast<const E*>(a.v);
+  E* Sout = static_cast<E*>(a.emit) + (long)bh * T * DD;
+
+  // this lane's state: S[16 rb + 4 g + r][16 w + i]
+  f32x4 z = zero4();
+  if (a.z0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = a.z0[bh * DD + (rb * 16 + 4 * g + r) * D + w * 16 + li];
+  }
+
+  const int nch = (N + CK - 1) / CK;
+  const int nall = T * nch;                      // chunks of all frames
+  // Ring slot: everything a chunk needs from memory, all of it committed to
+  // LDS at once (a value kept in registers past the slot's reload would
+  // have to be copied, and the copy would wait for every load in flight).
+  struct Pre {
+    u32x4 k[KPT];      // key pieces of the chunk
+    u32x4 v[VPT];      // 8 of the 16 rows' values of one token each
+    float bt[BPT];     // gates of tokens
+    float gm;          // the frame's decay
+  };
+  // element (token n of frame t, feature d): (((b T + t) N + n) H + h) D + d
+  auto rowbase = [&](int t, int n) { return (((long)b * T + t) * N + n) * H + h; };
+  // loads clamped, never skipped (past the last chunk, past a frame's rows)
+  auto prefetch = [&](Pre& P, int gc) {
+    gc = gc < nall ? gc : nall - 1;
+    const int t = gc / nch, c0 = (gc - t * nch) * CK;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int q = tid + NTH * j;
+      int n = c0 + q / KPR;
+      n = n < N ? n : N - 1;
+      P.k[j] = *reinterpret_cast<const u32x4*>(kp + rowbase(t, n) * D + (q % KPR) * 8);
+    }
+    // (pieces past the chunk's count re-read one inside it and are not committed)
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int vt = (tid + NTH * j) % VPC;
+      int n = c0 + vt / 2;
+      n = n < N ? n : N - 1;
+      P.v[j] = *reinterpret_cast<const u32x4*>(vp + rowbase(t, n) * D + rb * 16 + 8 * (vt % 2));
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      int n = c0 + (tid + NTH * j) % CK;
+      n = n < N ? n : N - 1;
+      P.bt[j] = a.beta[rowbase(t, n)];
+    }
+    P.gm = a.gamma[((long)b * T + t) * H + h];
+  };
+  auto stage_z = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Zs[(4 * g + r) * ZLD + w * 16 + li] = f32_to_bf16_bits(z[r]);
+  };
+  auto emit_rows = [&](int t) {   // the staged rows as S_t
+    constexpr int PRW = D / 4;
+    const int row = tid / PRW, pc = tid % PRW;
+    *reinterpret_cast<u32x2*>(Sout + t * DD + (rb * 16 + row) * D + pc * 4) =
+        *reinterpret_cast<const u32x2*>(&Zs[row * ZLD + pc * 4]);
+  };
+
+  bf16x8 sz[KB];
+  f32x4 dS = zero4();
+  // One chunk (global index gc, ring slot R): at a frame's first chunk
+  // stage S_{t-1}; store the staged rows as frame t - 1's state (at every
+  // chunk of the frame, the same bytes: a store under a branch would cost
+  // the compiler its count of the loads in flight; frame 0 stores S_{-1}
+  // into slot 0, which S_0 overwrites later); commit the keys, reload the
+  // slot PK chunks ahead, then P, R and the update; at the frame's last
+  // chunk S_t = gamma_t S_{t-1} + update.
+  auto step = [&](Pre& R, int gc) {
+    const int t = gc / nch, c = gc - t * nch;
+    const int st = gc & 1;
+    if (c == 0) {
+      stage_z();
+      lds_barrier();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k = kb * 32 + 8 * g;
+        sz[kb] = load_bf16x8(Zs + li * ZLD + (k < D ? k : 0));
+        if (k >= D) sz[kb] = zero_bf16x8();
+      }
+      dS = zero4();
+    }
+    emit_rows(t > 0 ? t - 1 : 0);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int q = tid + NTH * j;
+      *reinterpret_cast<u32x4*>(&Kst[st][(q / KPR) * D + (q % KPR) * 8]) = R.k[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      if (tid + NTH * j < VPC) *reinterpret_cast<u32x4*>(&Vs[st][(tid + NTH * j) * 8]) = R.v[j];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if (tid + NTH * j < CK) bs[st][tid + NTH * j] = R.bt[j];
+    if (tid == 0) gs[st] = R.gm;
+    prefetch(R, gc + PK);
+    lds_barrier();
+    // P = S K^T per 16-token tile, R = (s v - s^2 P) beta, staged as [row][token]
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = w + NW * u;
+      if (tt < TT) {
+        f32x4 p = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int k = kb * 32 + 8 * g;
+          bf16x8 kf = load_bf16x8(&Kst[st][(tt * 16 + li) * D + (k < D ? k : 0)]);
+          if (k >= D) kf = zero_bf16x8();
+          p = mfma_bf16(sz[kb], kf, p);
+        }
+        // tokens past the frame's end (re-read rows) write nothing
+        const int tk = tt * 16 + li;
+        const float bt = (c * CK + tk < N) ? bs[st][tk] : 0.f;
+        const u32x2 vv = *reinterpret_cast<const u32x2*>(&Vs[st][tk * 16 + 4 * g]);
+        const float v4[4] = {bf16_bits_to_f32((uint16_t)(vv[0] & 0xffff)),
+                             bf16_bits_to_f32((uint16_t)(vv[0] >> 16)),
+                             bf16_bits_to_f32((uint16_t)(vv[1] & 0xffff)),
+                             bf16_bits_to_f32((uint16_t)(vv[1] >> 16))};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Rs[st][(4 * g + r) * RLD + tt * 16 + li] = f32_to_bf16_bits((s * v4[r] - s2 * p[r]) * bt);
+      }
+    }
+    lds_barrier();
+    // update of this wave's tile: R (rows x tokens) times K (tokens x 16 features)
+#pragma unroll
+    for (int kk = 0; kk < CK / 32; ++kk) {
+      const bf16x8 rf = load_bf16x8(&Rs[st][li * RLD + kk * 32 + 8 * g]);
+      const bf16x8 kf = lds_col_frag_bf16(&Kst[st][0], D, kk * 32, w * 16);
+      dS = mfma_bf16(rf, kf, dS);
+    }
+    if (c == nch - 1) z = gs[st] * z + dS;
+  };
+
+  // whole trips of PK chunks straight-line (no branch around a memory
+  // operation), then the last, partial trip
+  Pre ring[PK];
+#pragma unroll
+  for (int r = 0; r < PK; ++r) prefetch(ring[r], r);
+  int gc0 = 0;
+  for (; gc0 + PK <= nall; gc0 += PK) {
+#pragma unroll
+    for (int r = 0; r < PK; ++r) step(ring[r], gc0 + r);
+  }
+#pragma unroll
+  for (int r = 0; r < PK; ++r)
+    if (gc0 + r < nall) step(ring[r], gc0 + r);
+  // the last frame's state
+  stage_z();
+  lds_barrier();
+  emit_rows(T - 1);
+  if (a.zT) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a.zT[bh * DD + (rb * 16 + 4 * g + r) * D + w * 16 + li] = z[r];
+  }
+}
+
+template <int NT>
+static hipError_t launch_direct_nt(const DirectArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((direct_kernel<NT>), dim3(a.B * a.H * NT), dim3(64 * NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_direct(const DirectArgs& a, int nt, hipStream_t s) {
+  if (a.T < 1 || a.N < 1) return hipErrorInvalidValue;
+  switch (nt) {
+    case 1: return launch_direct_nt<1>(a, s);
+    case 2: return launch_direct_nt<2>(a, s);
+    case 3: return launch_direct_nt<3>(a, s);
+    case 4: return launch_direct_nt<4>(a, s);
+    case 5: return launch_direct_nt<5>(a, s);
+    case 6: return launch_direct_nt<6>(a, s);
+    case 7: return launch_direct_nt<7>(a, s);
+    case 8: return launch_direct_nt<8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -145,6 +145,23 @@ hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, in
 hipError_t launch_rows_normalize_bwd(const void* x, void* g, int64_t rows, int d, int io,
                                      hipStream_t s);
 
+// Direct form of the state update (short launches): per (b, h, 16-row
+// block) a workgroup walks the T frames, S_t = gamma_t S_{t-1} + sum_n
+// beta_n (s v_n - s^2 S_{t-1} k_n) k_n^T, straight from the token rows, and
+// emits every S_t; the output kernel then forms O_t.  bf16 only.
+struct DirectArgs {
+  const void* k;
+  const void* v;
+  const float* gamma;   // [B, T, H]
+  const float* beta;    // [B, L, H]
+  const float* z0;      // [B, H, D, D] fp32 initial state or nullptr (zero)
+  void* emit;           // [B, H, T] x D x D bf16 row-major: S_t
+  float* zT;            // [B, H, D, D] fp32 final state or nullptr; may equal z0
+  float s;              // key scale
+  int B, H, T, N;
+};
+hipError_t launch_direct(const DirectArgs& a, int nt, hipStream_t s);
+
 // Token-space forward (frames with few tokens): one workgroup per (b, h),
 // chunks of F frames of N tokens, F N <= TokCfg<io>::CP.
 template <int IO> struct TokCfg {

@@ -65,8 +65,9 @@ typedef enum {
     GDN_ERR_MISALIGNED = 4,          /* a pointer misaligned (16 B; gates 4 B) */
     GDN_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < required            */
     GDN_ERR_UNSUPPORTED = 6,         /* D not a multiple of 16, > 128, Dk!=Dv;
-                                        unknown algorithm or flag; token form
-                                        outside its limits (gdn_algorithm)    */
+                                        unknown algorithm or flag; token or
+                                        direct form outside its limits
+                                        (gdn_algorithm)                       */
     GDN_ERR_HIP = 7,                 /* a kernel launch failed                */
     GDN_ERR_ALIASING = 8             /* an output overlaps an input           */
 } gdn_status;
@@ -88,10 +89,20 @@ typedef enum { GDN_OP_FORWARD = 0, GDN_OP_STEP = 1, GDN_OP_BACKWARD = 2 } gdn_op
  *                   head and batch in bf16).  For frames of few tokens
  *                   (token-wise GDN is N = 1).
  *                   Requires N <= 64 (bf16) / 32 (fp32) and saved == NULL.
- *   GDN_ALGO_AUTO   currently the frame form.
+ *   GDN_ALGO_DIRECT the direct form: the frames in turn in one launch,
+ *                   S_t = gamma_t S_{t-1} + sum_n beta_n (s v_n -
+ *                   s^2 S_{t-1} k_n) k_n^T straight from the token rows
+ *                   (no A_t, U_t), then O_t = S_t Q^_t for all frames.
+ *                   For launches of few frames (streaming steps, short
+ *                   windows).  bf16 only; requires saved == NULL.
+ *   GDN_ALGO_AUTO   the direct form for bf16 launches of at most 2 frames
+ *                   (the frame form when a saved buffer is passed), else
+ *                   the frame form.
  * gdn_backward always uses the frame form (recomputing A_t, S_t when no
  * saved buffer is given). */
-typedef enum { GDN_ALGO_AUTO = 0, GDN_ALGO_FRAME = 1, GDN_ALGO_TOKEN = 2 } gdn_algorithm;
+typedef enum {
+    GDN_ALGO_AUTO = 0, GDN_ALGO_FRAME = 1, GDN_ALGO_TOKEN = 2, GDN_ALGO_DIRECT = 3
+} gdn_algorithm;
 
 /* Optional prologue of the GDN block, fused into the entry points (bits of
  * gdn_problem.flags; any other bit is GDN_ERR_UNSUPPORTED).  The hats on
@@ -141,8 +152,8 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes);
  * io_dtype is GDN_BF16, fp32 when it is GDN_FP32.  fp32 A_t is row-major;
  * bf16 A_t is in the MFMA operand order of the scan: element [r][c] of a
  * frame's A_t at (r / 16) 16 Dk + (c / 32) 512 + (16 ((c % 32) / 8) +
- * r % 16) 8 + c % 8.  GDN_ERR_UNSUPPORTED for the token form, which keeps
- * neither. */
+ * r % 16) 8 + c % 8.  GDN_ERR_UNSUPPORTED for GDN_ALGO_TOKEN and
+ * GDN_ALGO_DIRECT, which keep neither. */
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
 
 /* Whole-sequence forward (module 2 recurrence over t = 1..T):
@@ -167,7 +178,9 @@ gdn_status gdn_forward(const gdn_problem* p,
  * (events[0..3], all non-NULL) on `stream`: before the per-frame Gram/write
  * kernel, between it and the inter-frame scan, between the scan and the
  * output kernel, and after the output kernel.  For measuring the three
- * phases; results are identical to gdn_forward. */
+ * phases; results are identical to gdn_forward.  The token form counts
+ * entirely as the output phase; the direct form's state update as the
+ * scan phase. */
 gdn_status gdn_forward_events(const gdn_problem* p,
                               const void* q, const void* k, const void* v,
                               const float* gamma, const float* beta,

@@ -149,11 +149,33 @@ def test_algorithm_field(lib):
         assert _ws(gb.make_problem(1, 2, 3, nmax + 1, 16, io, algorithm="frame"),
                    gb.GDN_OP_FORWARD)[0] == 0
     bad = gb.make_problem(1, 2, 4, 8, 32, "bf16")
-    bad.algorithm = 3
+    bad.algorithm = 4
     assert gb.STATUS[_ws(bad, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
-    # auto is currently the frame form
+    # auto may take the direct form, which falls back to the frame form when
+    # a saved buffer is passed: its workspace is the frame form's
     auto = gb.make_problem(1, 2, 4, 1, 32, "bf16")
-    assert _ws(auto, gb.GDN_OP_FORWARD)[1] > 0
+    assert _ws(auto, gb.GDN_OP_FORWARD) == _ws(gb.make_problem(1, 2, 4, 1, 32, "bf16",
+                                                                 algorithm="frame"),
+                                                 gb.GDN_OP_FORWARD)
+    assert gb.STATUS[lib.gdn_saved_size(ctypes.byref(auto), ctypes.byref(n))] == "GDN_OK"
+
+
+def test_direct_form_limits(lib):
+    vp = ctypes.c_void_p
+    n = ctypes.c_size_t(0)
+    # bf16 only
+    pf = gb.make_problem(1, 2, 4, 8, 32, "fp32", algorithm="direct")
+    assert gb.STATUS[_ws(pf, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
+    p = gb.make_problem(1, 2, 4, 8, 32, "bf16", algorithm="direct")
+    assert _ws(p, gb.GDN_OP_FORWARD)[0] == 0
+    # no saved buffer
+    assert gb.STATUS[lib.gdn_saved_size(ctypes.byref(p), ctypes.byref(n))] == "GDN_ERR_UNSUPPORTED"
+    good = [vp(0x100000 * (i + 1)) for i in range(10)]
+    code = lib.gdn_forward(ctypes.byref(p), *good, 1 << 30, None)
+    assert gb.STATUS[code] == "GDN_ERR_UNSUPPORTED"
+    # normalised rows: copies of q and k in the workspace
+    pn = gb.make_problem(1, 2, 4, 8, 32, "bf16", algorithm="direct", flags=1)
+    assert _ws(pn, gb.GDN_OP_FORWARD)[1] > _ws(p, gb.GDN_OP_FORWARD)[1]
 
 
 def test_prologue_flags(lib):

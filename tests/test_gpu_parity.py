@@ -36,7 +36,7 @@ def f64(t):
 
 
 def run_forward_pair(inp, N, io, key_scale=0.0, scan_chunk=0, with_state=False,
-                     algorithm="auto"):
+                     algorithm="frame"):
     d = {k: to_dev(v) for k, v in inp.items()}
     st = d.get("state") if with_state else None
     o, so = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, state_in=st,
@@ -68,11 +68,14 @@ def test_forward_tiny_fp32():
 
 @pytest.mark.parametrize("io", ["fp32", "bf16"])
 @pytest.mark.parametrize("D", [16, 32, 48, 64, 112, 128])
-def test_forward_head_dims_ragged(io, D):
+@pytest.mark.parametrize("algorithm", ["frame", "auto"])
+def test_forward_head_dims_ragged(io, D, algorithm):
     # several token chunks with a ragged tail (N = 100), two batches, odd H
-    inp = gin.make_inputs(B=2, H=3, T=5, N=100, D=D, io=io, gamma="uniform", seed=1,
+    # (auto: the direct form for bf16 at two frames)
+    T = 2 if algorithm == "auto" else 5
+    inp = gin.make_inputs(B=2, H=3, T=T, N=100, D=D, io=io, gamma="uniform", seed=1,
                           with_state=True)
-    check_forward(inp, 100, io, with_state=True)
+    check_forward(inp, 100, io, with_state=True, algorithm=algorithm)
 
 
 @pytest.mark.parametrize("io", ["fp32", "bf16"])
@@ -205,14 +208,14 @@ def test_step_chain_equals_forward(io):
                           with_state=True)
     d = {k: to_dev(v) for k, v in inp.items()}
     o_full, s_full = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
-                                state_in=d["state"])
+                                state_in=d["state"], algorithm="frame")
     state = d["state"].clone()
     outs = []
     for t in range(T):
         sl = slice(t * N, (t + 1) * N)
         outs.append(gb.step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
                             d["v"][:, sl].contiguous(), d["gamma"][:, t:t + 1].contiguous(),
-                            d["beta"][:, sl].contiguous(), state).clone())
+                            d["beta"][:, sl].contiguous(), state, algorithm="frame").clone())
     torch.cuda.synchronize()
     o_step = torch.cat(outs, dim=1)
     # the step path runs the same kernels frame by frame, the Gram/write sums
@@ -235,12 +238,12 @@ def test_chunk_causal_windows_equal_one_call(io):
                           with_state=True)
     d = {k: to_dev(v) for k, v in inp.items()}
     o_full, s_full = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
-                                state_in=d["state"])
+                                state_in=d["state"], algorithm="frame")
     state = d["state"].clone()
     outs = []
     for t0, t1 in [(0, 1), (1, 9), (9, 17)]:
         sl = slice(t0 * N, t1 * N)
-        plan = gb.ForwardPlan(B, H, t1 - t0, N, D, io, torch.device(DEV))
+        plan = gb.ForwardPlan(B, H, t1 - t0, N, D, io, torch.device(DEV), algorithm="frame")
         o, st = plan(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
                      d["v"][:, sl].contiguous(), d["gamma"][:, t0:t1].contiguous(),
                      d["beta"][:, sl].contiguous(), state_in=state, state_out=state)
