@@ -29,6 +29,10 @@
 // LDS one chunk at a time behind an LDS-only barrier, so the ring stays in
 // flight across it.  (Direct-to-LDS copies move the same bytes, but at
 // this number of waves per CU they ran about a tenth slower.)
+// The token rows are loaded non-temporally: they stream through once, and
+// the caches keep the A_t and U_t just written for the scan that reads them
+// next (the scan took 80 instead of 58 us at the one-minute shape when the
+// rows went through the caches).
 // Both MFMA operands need a feature's values over consecutive tokens; they
 // are read with the gfx950 transposing LDS read.  The weight w multiplies
 // the X operand in fp32 before rounding to bf16.  Tail tokens of the last
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(64 * gram_wph(NT, NORM) * HPW, HPW == 1 ? 2 : 1) vo
         int tk = c0 + row;
         tk = tk < N ? tk : N - 1;
         const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(col * 16);
-        R.v[m * C::PPM + j] = *reinterpret_cast<const u32x4*>(base + off);
+        R.v[m * C::PPM + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
       }
     }
     // the first NWT threads load the chunk's weights; the others load one

@@ -14,6 +14,9 @@
 // The outputs of a chunk are staged in LDS and stored one iteration later
 // as contiguous 16-byte pieces of token rows.
 //
+// Query rows are read and output rows written non-temporally: they stream
+// through once, and the caches keep the frame matrices (the scan's states,
+// read just after they were written) instead.
 // The ring is plain register loads that the compiler's wait counts track
 // exactly (no direct-to-LDS copies, whose waits the compiler cannot relax
 // while stores are pending), and the barriers are LDS-only, so the PF - 1
@@ -133,7 +136,8 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
       const int row = p / PR, pc = p % PR;
       int tk = c0 + row;
       if (tk >= N) tk = N - 1;
-      R.v[j] = *reinterpret_cast<const u32x4*>(tok + ((row0 + tk) * a.H + h0) * (long)D + pc * (16 / ES));
+      R.v[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(tok + ((row0 + tk) * a.H + h0) * (long)D + pc * (16 / ES)));
     }
   };
   auto commit = [&](const Ring& R, int c) {
@@ -201,8 +205,9 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
     for (int j = 0; j < PPT; ++j) {
       const int p = tid + NTH * j;
       const int row = p / PR, pc = p % PR;
-      *reinterpret_cast<u32x4*>(out + ((r0 + row) * a.H + h0) * (long)D + pc * (16 / ES)) =
-          *reinterpret_cast<const u32x4*>(src + p * (16 / ES));
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src + p * (16 / ES)),
+                                  reinterpret_cast<u32x4*>(out + ((r0 + row) * a.H + h0) * (long)D +
+                                                           pc * (16 / ES)));
     }
   };
   auto store_tail = [&](int c) {
