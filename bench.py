@@ -242,14 +242,12 @@ def bench_stream(gb, d, B, H, D, T, N, ev):
     import torch
     dev = d["q"].device
     state = torch.zeros((B, H, D, D), dtype=torch.float32, device=dev)
-    prob = gb.make_problem(B, H, 1, N, D, "bf16")
-    ws = torch.empty(gb.workspace_size(prob, gb.GDN_OP_STEP), dtype=torch.uint8, device=dev)
-    o = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    plan = gb.StepPlan(B, H, N, D, "bf16", dev)
     frames = [(d["q"][:, t * N:(t + 1) * N], d["k"][:, t * N:(t + 1) * N],
                d["v"][:, t * N:(t + 1) * N], d["gamma"][:, t:t + 1], d["beta"][:, t * N:(t + 1) * N])
               for t in range(T)]
     for f in frames[:3]:
-        gb.step(*f, state, out=o, workspace=ws)
+        plan(*f, state)
     state.zero_()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -257,7 +255,7 @@ def bench_stream(gb, d, B, H, D, T, N, ev):
     evs[0].record(stream)
     t0 = time.perf_counter()
     for t, f in enumerate(frames):
-        gb.step(*f, state, out=o, workspace=ws)
+        plan(*f, state)
         evs[t + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -228,6 +228,31 @@ def forward(q, k, v, gamma, beta, n, state_in=None, key_scale=0.0, scan_chunk=0,
     return o, st
 
 
+class StepPlan:
+    """Preallocated problem, output and workspace for repeated gdn_step calls
+    on one frame shape (streaming: one call per latent frame, the state
+    carried in place).  Call with q, k, v [B, N, H, D], gamma [B, 1, H],
+    beta [B, N, H] and the state [B, H, D, D] fp32; returns the plan's
+    output buffer [B, N, H, D] (overwritten by the next call)."""
+
+    def __init__(self, B, H, N, D, io, device, key_scale=0.0, algorithm="auto", flags=0):
+        self.prob = make_problem(B, H, 1, N, D, io, key_scale, 0, algorithm, flags)
+        dt = torch.bfloat16 if io == "bf16" else torch.float32
+        self.o = torch.empty((B, N, H, D), dtype=dt, device=device)
+        self.ws = torch.empty(max(16, workspace_size(self.prob, GDN_OP_STEP)), dtype=torch.uint8,
+                              device=device)
+        self.device = device
+        self.shape = (B, N, H, D)
+
+    def __call__(self, q, k, v, gamma, beta, state):
+        if tuple(q.shape) != self.shape or tuple(state.shape[:2]) != self.shape[:1] + self.shape[2:3]:
+            raise ValueError("tensor shapes do not match the plan")
+        _check(lib().gdn_step(ctypes.byref(self.prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
+                              _p(state), _p(self.o), _p(self.ws), self.ws.numel(),
+                              _stream(self.device)), "gdn_step")
+        return self.o
+
+
 def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None,
          normalize_qk=False, gate_logits=False, algorithm="auto"):
     """One streaming frame: q, k, v [B, N, H, D], gamma [B, 1, H], beta

@@ -50,12 +50,12 @@ __global__ __launch_bounds__(64 * NT) void direct_kernel(DirectArgs a) {
   constexpr int PK = 3;                          // chunks in flight
   static_assert(KPT * NTH == CK * KPR, "key pieces split evenly");
   static_assert(16 * (D / 4) == NTH, "one 4-element piece of the staged rows per thread");
-  __shared__ __attribute__((aligned(16))) E Kst[2][CK * D];
+  __shared__ __attribute__((aligned(16))) E Kst[3][CK * D];
   __shared__ __attribute__((aligned(16))) E Rs[2][16 * RLD];
   __shared__ __attribute__((aligned(16))) E Zs[16 * ZLD];
-  __shared__ __attribute__((aligned(16))) E Vs[2][CK * 16];       // values of the 16 rows
-  __shared__ float bs[2][CK];                                     // gates of the tokens
-  __shared__ float gs[2];                                         // the frame's decay
+  __shared__ __attribute__((aligned(16))) E Vs[3][CK * 16];       // values of the 16 rows
+  __shared__ float bs[3][CK];                                     // gates of the tokens
+  __shared__ float gs[3];                                         // the frame's decay
 
   const int total = a.B * a.H * NT;
   const int item = xcd_item(blockIdx.x, total);
@@ -130,45 +130,37 @@ __global__ __launch_bounds__(64 * NT) void direct_kernel(DirectArgs a) {
         *reinterpret_cast<const u32x2*>(&Zs[row * ZLD + pc * 4]);
   };
 
-  bf16x8 sz[KB];
+  bf16x8 sz[KB];   // this block's rows of S_{t-1}, left operand of P
   f32x4 dS = zero4();
-  // One chunk (global index gc, ring slot R): at a frame's first chunk
-  // stage S_{t-1}; store the staged rows as frame t - 1's state (at every
-  // chunk of the frame, the same bytes: a store under a branch would cost
-  // the compiler its count of the loads in flight; frame 0 stores S_{-1}
-  // into slot 0, which S_0 overwrites later); commit the keys, reload the
-  // slot PK chunks ahead, then P, R and the update; at the frame's last
-  // chunk S_t = gamma_t S_{t-1} + update.
-  auto step = [&](Pre& R, int gc) {
-    const int t = gc / nch, c = gc - t * nch;
-    const int st = gc & 1;
-    if (c == 0) {
-      stage_z();
-      lds_barrier();
+  auto load_sz = [&]() {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int k = kb * 32 + 8 * g;
-        sz[kb] = load_bf16x8(Zs + li * ZLD + (k < D ? k : 0));
-        if (k >= D) sz[kb] = zero_bf16x8();
-      }
-      dS = zero4();
+    for (int kb = 0; kb < KB; ++kb) {
+      const int k = kb * 32 + 8 * g;
+      sz[kb] = load_bf16x8(Zs + li * ZLD + (k < D ? k : 0));
+      if (k >= D) sz[kb] = zero_bf16x8();
     }
-    emit_rows(t > 0 ? t - 1 : 0);
+  };
+  // chunk gc's keys, values, gates and decay into LDS buffer gc % 3
+  auto commit = [&](const Pre& R, int gc) {
+    const int sk = gc % 3;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int q = tid + NTH * j;
-      *reinterpret_cast<u32x4*>(&Kst[st][(q / KPR) * D + (q % KPR) * 8]) = R.k[j];
+      *reinterpret_cast<u32x4*>(&Kst[sk][(q / KPR) * D + (q % KPR) * 8]) = R.k[j];
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
-      if (tid + NTH * j < VPC) *reinterpret_cast<u32x4*>(&Vs[st][(tid + NTH * j) * 8]) = R.v[j];
+      if (tid + NTH * j < VPC) *reinterpret_cast<u32x4*>(&Vs[sk][(tid + NTH * j) * 8]) = R.v[j];
 #pragma unroll
     for (int j = 0; j < BPT; ++j)
-      if (tid + NTH * j < CK) bs[st][tid + NTH * j] = R.bt[j];
-    if (tid == 0) gs[st] = R.gm;
-    prefetch(R, gc + PK);
-    lds_barrier();
-    // P = S K^T per 16-token tile, R = (s v - s^2 P) beta, staged as [row][token]
+      if (tid + NTH * j < CK) bs[sk][tid + NTH * j] = R.bt[j];
+    if (tid == 0) gs[sk] = R.gm;
+  };
+  // P = S K^T per 16-token tile of chunk gc, R = (s v - s^2 P) beta staged
+  // as [row][token] in R buffer gc % 2
+  auto compute_p = [&](int gc) {
+    const int sk = gc % 3, sr = gc & 1;
+    const int c = gc % nch;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tt = w + NW * u;
@@ -177,48 +169,88 @@ __global__ __launch_bounds__(64 * NT) void direct_kernel(DirectArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const int k = kb * 32 + 8 * g;
-          bf16x8 kf = load_bf16x8(&Kst[st][(tt * 16 + li) * D + (k < D ? k : 0)]);
+          bf16x8 kf = load_bf16x8(&Kst[sk][(tt * 16 + li) * D + (k < D ? k : 0)]);
           if (k >= D) kf = zero_bf16x8();
           p = mfma_bf16(sz[kb], kf, p);
         }
         // tokens past the frame's end (re-read rows) write nothing
         const int tk = tt * 16 + li;
-        const float bt = (c * CK + tk < N) ? bs[st][tk] : 0.f;
-        const u32x2 vv = *reinterpret_cast<const u32x2*>(&Vs[st][tk * 16 + 4 * g]);
+        const float bt = (c * CK + tk < N) ? bs[sk][tk] : 0.f;
+        const u32x2 vv = *reinterpret_cast<const u32x2*>(&Vs[sk][tk * 16 + 4 * g]);
         const float v4[4] = {bf16_bits_to_f32((uint16_t)(vv[0] & 0xffff)),
                              bf16_bits_to_f32((uint16_t)(vv[0] >> 16)),
                              bf16_bits_to_f32((uint16_t)(vv[1] & 0xffff)),
                              bf16_bits_to_f32((uint16_t)(vv[1] >> 16))};
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          Rs[st][(4 * g + r) * RLD + tt * 16 + li] = f32_to_bf16_bits((s * v4[r] - s2 * p[r]) * bt);
+          Rs[sr][(4 * g + r) * RLD + tk] = f32_to_bf16_bits((s * v4[r] - s2 * p[r]) * bt);
       }
     }
-    lds_barrier();
-    // update of this wave's tile: R (rows x tokens) times K (tokens x 16 features)
+  };
+  // the update of this wave's tile by chunk gc: R (rows x tokens) times K
+  // (tokens x 16 features)
+  auto compute_ds = [&](int gc) {
+    const int sk = gc % 3, sr = gc & 1;
 #pragma unroll
     for (int kk = 0; kk < CK / 32; ++kk) {
-      const bf16x8 rf = load_bf16x8(&Rs[st][li * RLD + kk * 32 + 8 * g]);
-      const bf16x8 kf = lds_col_frag_bf16(&Kst[st][0], D, kk * 32, w * 16);
+      const bf16x8 rf = load_bf16x8(&Rs[sr][li * RLD + kk * 32 + 8 * g]);
+      const bf16x8 kf = lds_col_frag_bf16(&Kst[sk][0], D, kk * 32, w * 16);
       dS = mfma_bf16(rf, kf, dS);
     }
-    if (c == nch - 1) z = gs[st] * z + dS;
   };
 
-  // whole trips of PK chunks straight-line (no branch around a memory
-  // operation), then the last, partial trip
+  // Software pipeline, one barrier per chunk: step i commits chunk i + 1
+  // (and reloads its ring slot PK chunks ahead), then computes P of chunk
+  // i + 1 next to the update by chunk i (K in three LDS buffers, R in two).
+  // At a frame's last chunk the state is updated, staged and P of the next
+  // frame's first chunk follows behind one more barrier.  The staged rows
+  // are stored as the previous frame's state at every step (the same bytes
+  // each time: a store under a branch would cost the compiler its count of
+  // the loads in flight; frame 0 stores S_{-1} into slot 0, which S_0
+  // overwrites later).
+  auto step = [&](Pre& R, int i) {
+    const int t = i / nch, c = i - t * nch;
+    commit(R, i + 1);
+    prefetch(R, i + 1 + PK);
+    emit_rows(t > 0 ? t - 1 : 0);
+    lds_barrier();
+    const bool last = c == nch - 1;
+    if (!last && i + 1 < nall) compute_p(i + 1);
+    compute_ds(i);
+    if (last) {
+      z = gs[i % 3] * z + dS;
+      dS = zero4();
+      if (i + 1 < nall) {
+        stage_z();
+        lds_barrier();
+        load_sz();
+        compute_p(i + 1);
+      }
+    }
+  };
+
   Pre ring[PK];
 #pragma unroll
   for (int r = 0; r < PK; ++r) prefetch(ring[r], r);
-  int gc0 = 0;
-  for (; gc0 + PK <= nall; gc0 += PK) {
+  stage_z();
+  lds_barrier();
+  load_sz();
+  commit(ring[0], 0);
+  prefetch(ring[0], PK);
+  lds_barrier();
+  compute_p(0);
+  // whole trips of PK steps straight-line (no branch around a memory
+  // operation), then the last, partial trip; step i uses ring slot i + 1
+  int i0 = 0;
+  for (; i0 + PK <= nall; i0 += PK) {
 #pragma unroll
-    for (int r = 0; r < PK; ++r) step(ring[r], gc0 + r);
+    for (int r = 0; r < PK; ++r) step(ring[(r + 1) % PK], i0 + r);
   }
 #pragma unroll
   for (int r = 0; r < PK; ++r)
-    if (gc0 + r < nall) step(ring[r], gc0 + r);
+    if (i0 + r < nall) step(ring[(r + 1) % PK], i0 + r);
   // the last frame's state
+  lds_barrier();
   stage_z();
   lds_barrier();
   emit_rows(T - 1);

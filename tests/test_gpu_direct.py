@@ -126,3 +126,21 @@ def test_direct_prologue(nq, gl):
     inp = gin.make_inputs(B=1, H=3, T=3, N=150, D=112, io="bf16", seed=86, with_state=True,
                           raw=True)
     check(inp, 150, normalize_qk=nq, gate_logits=gl)
+
+
+def test_step_plan_matches_step():
+    # the preallocated streaming plan calls the same entry point
+    B, H, T, N, D = 1, 4, 3, 200, 112
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io="bf16", seed=87, with_state=True)
+    d = dev(inp)
+    s1, s2 = d["state"].clone(), d["state"].clone()
+    plan = gb.StepPlan(B, H, N, D, "bf16", torch.device(DEV))
+    for t in range(T):
+        sl = slice(t * N, (t + 1) * N)
+        args = (d["q"][:, sl], d["k"][:, sl], d["v"][:, sl], d["gamma"][:, t:t + 1],
+                d["beta"][:, sl])
+        o1 = gb.step(*[x.contiguous() for x in args], s1)
+        o2 = plan(*args, s2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+    assert torch.equal(s1, s2)
