@@ -48,6 +48,10 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
   constexpr int RW = HPW * D;                    // elements of a token's row segment
   constexpr int CT = (BF ? 64 : 32) / HPW;       // tokens per chunk
   constexpr int PR = RW * ES / 16;               // 16-byte pieces per row segment
+  // LDS row stride: padded so that the 16 rows a fragment read (or an
+  // output tile's write) touches start on different banks (row stride
+  // = 4 mod 8 dwords: 116 dwords for bf16 head pairs of 112)
+  constexpr int LDR = RW + (BF ? 8 : 4);
   constexpr int NTH = 64 * NT;
   constexpr int PPT = CT * PR / NTH;             // pieces per thread per chunk (2)
   constexpr int PF = 3;                          // chunks in flight
@@ -56,8 +60,8 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
   constexpr int KF = BF ? (D + 31) / 32 : D / 4;
   constexpr bool KTAIL = BF && (D % 32) != 0;
   // (16 elements of padding: the zeroed tail of the last row's read stays in the array)
-  __shared__ __attribute__((aligned(16))) E stage[2][CT * RW + 16];
-  __shared__ __attribute__((aligned(16))) E obuf[2][CT * RW];
+  __shared__ __attribute__((aligned(16))) E stage[2][CT * LDR + 16];
+  __shared__ __attribute__((aligned(16))) E obuf[2][CT * LDR];
 
   const int HG = a.H / HPW;                        // head groups
   const int total = a.B * a.Tc * HG * a.P;
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
       // S_t as [KR][D] rows in the output staging (free until the first
       // chunk), rows past D zero
       constexpr int KR = KF * 32;
-      static_assert(KR * D <= 2 * CT * RW, "staged matrix must fit the output buffers");
+      static_assert(KR * D <= 2 * CT * LDR, "staged matrix must fit the output buffers");
       uint16_t* ms = reinterpret_cast<uint16_t*>(&obuf[0][0]);
       constexpr int PRW = D / 8;
       for (int p = tid; p < KR * PRW; p += NTH) {
@@ -143,8 +147,10 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
   auto commit = [&](const Ring& R, int c) {
     E* st = stage[c & 1];
 #pragma unroll
-    for (int j = 0; j < PPT; ++j)
-      *reinterpret_cast<u32x4*>(st + (tid + NTH * j) * (16 / ES)) = R.v[j];
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      *reinterpret_cast<u32x4*>(st + (p / PR) * LDR + (p % PR) * (16 / ES)) = R.v[j];
+    }
   };
   auto compute = [&](int c) {
     const E* ts = stage[c & 1];
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
 #pragma unroll
       for (int tt = 0; tt < CT / 16; ++tt) {
         f32x4 acc = zero4();
-        const E* trow = ts + (tt * 16 + li) * RW + hp * D;
+        const E* trow = ts + (tt * 16 + li) * LDR + hp * D;
         float ss = 0.f;   // NORM: |q|^2 of this lane's token (fp32: its share)
         if constexpr (BF) {
           f32x4 gram = zero4();   // NORM: Q Q^T of the tile's 16 tokens
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
           }
           acc *= inv_norm(ss);
         }
-        E* dst = ob + (tt * 16 + li) * RW + hp * D + ft * 16 + 4 * g;
+        E* dst = ob + (tt * 16 + li) * LDR + hp * D + ft * 16 + 4 * g;
         if constexpr (BF) {
           u32x2 pk;
           pk[0] = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
     for (int j = 0; j < PPT; ++j) {
       const int p = tid + NTH * j;
       const int row = p / PR, pc = p % PR;
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src + p * (16 / ES)),
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src + row * LDR + pc * (16 / ES)),
                                   reinterpret_cast<u32x4*>(out + ((r0 + row) * a.H + h0) * (long)D +
                                                            pc * (16 / ES)));
     }
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
       const int tk = (cbeg + c) * CT + row;
       if (tk < N)
         *reinterpret_cast<u32x4*>(out + ((row0 + tk) * a.H + h0) * (long)D + pc * (16 / ES)) =
-            *reinterpret_cast<const u32x4*>(src + p * (16 / ES));
+            *reinterpret_cast<const u32x4*>(src + row * LDR + pc * (16 / ES));
     }
   };
 
