@@ -11,7 +11,15 @@
           [--copy-bytes N] [--json OUT]
       HBM bytes per dispatch from `rocprofv3 --pmc FETCH_SIZE` and
       `--pmc WRITE_SIZE` runs (KiB per dispatch), each scaled by what the
-      same counter reads for the plain copy of known size.
+      same counter reads for the plain copy of known size;
+  python -m gated_deltanet_recurrence_frame_amd.rocprof_summary counters CSV [--xcds 8 --cus 256]
+      shader-unit utilisation per kernel from one `rocprofv3 --pmc` run with
+      SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT,
+      SQ_WAVE_CYCLES, SQ_WAIT_INST_ANY, SQ_INSTS_MFMA, SQ_INSTS_LDS and
+      GRBM_GUI_ACTIVE.  GRBM_GUI_ACTIVE reads the busy cycles summed over the
+      XCDs, so one XCD's cycles are GRBM_GUI_ACTIVE / xcds; MFMA busy is the
+      fraction of the SIMDs' cycles (cus x 4 per XCD cycle) with the MFMA unit
+      busy, LDS busy the fraction of the CUs' cycles with the LDS active.
 
 Nothing here is on the compute path.
 """
@@ -97,6 +105,28 @@ def traffic(fetch, write, copy_fetch, copy_write, copy_bytes):
     return out
 
 
+def counters(csv_path, xcds, cus):
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(_find(csv_path, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            for short, (frag, _) in KERNELS.items():
+                if frag in r["Kernel_Name"]:
+                    acc[short][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for short, d in acc.items():
+        m = {c: sum(v) / len(v) for c, v in d.items()}
+        cyc = m["GRBM_GUI_ACTIVE"] / xcds          # one XCD's busy cycles
+        out[short] = {
+            "mfma_busy": m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * 4),
+            "lds_busy": m["SQ_LDS_IDX_ACTIVE"] / (cyc * cus),
+            "lds_bank_conflict_share": m["SQ_LDS_BANK_CONFLICT"] / max(1.0, m["SQ_LDS_IDX_ACTIVE"]),
+            "wave_wait_share": m["SQ_WAIT_INST_ANY"] / max(1.0, m["SQ_WAVE_CYCLES"]),
+            "mfma_insts": m["SQ_INSTS_MFMA"], "lds_insts": m["SQ_INSTS_LDS"],
+            "xcd_cycles": cyc,
+        }
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -110,6 +140,10 @@ def main(argv=None):
         tr.add_argument("--" + k.replace("_", "-"), required=True)
     tr.add_argument("--copy-bytes", type=int, default=1 << 30)
     tr.add_argument("--json", default=None)
+    cn = sub.add_parser("counters")
+    cn.add_argument("csv")
+    cn.add_argument("--xcds", type=int, default=8)
+    cn.add_argument("--cus", type=int, default=256)
     a = ap.parse_args(argv)
 
     if a.cmd == "copy":
@@ -126,6 +160,14 @@ def main(argv=None):
         print("|---|---|---|---|---|")
         for r in rows:
             print("| `%s` | %d | %.1f | %.1f | %.1f |" % (r[0], r[1], r[2], r[3], r[4]))
+    elif a.cmd == "counters":
+        print("| kernel | MFMA busy | LDS busy | LDS bank-conflict share | wave cycles waiting | "
+              "MFMA insts | LDS insts |")
+        print("|---|---|---|---|---|---|---|")
+        for k, r in counters(a.csv, a.xcds, a.cus).items():
+            print("| %s | %.1f%% | %.1f%% | %.0f%% | %.0f%% | %.3g | %.3g |" % (
+                k, 100 * r["mfma_busy"], 100 * r["lds_busy"], 100 * r["lds_bank_conflict_share"],
+                100 * r["wave_wait_share"], r["mfma_insts"], r["lds_insts"]))
     else:
         out = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
         text = json.dumps(out, indent=1, sort_keys=True)
