@@ -13,7 +13,12 @@ using namespace gdn;
 
 namespace {
 
-constexpr int kDefaultChunk = 1;   // sequential scan unless asked otherwise
+// Default scan: with few sequences (B H) the sequential scan leaves most
+// CUs idle, and the composite prefix over chunks of frames shortens its
+// chain (forward at 121 x 880 tokens, D = 112: 1 head 103 -> 83 us with
+// chunks of 16, 8 heads 248 -> 230 us, 16 heads 428 -> 409 us with chunks
+// of 32; 20 heads 516 vs 518 us).
+int default_chunk(int64_t seqs) { return seqs <= 8 ? 16 : seqs <= 16 ? 32 : 1; }
 // GDN_ALGO_AUTO takes the token form for frames of at most this many tokens
 // (0: never), the direct form for bf16 launches of at most this many frames
 // (streaming steps, short windows), else the frame form
@@ -61,7 +66,7 @@ gdn_status check_problem(const gdn_problem* p, Shape* sh) {
       s.N * s.H * s.D * s.es >= (int64_t(1) << 31))
     return GDN_ERR_BAD_SHAPE;
   s.s = p->key_scale != 0.f ? p->key_scale : (float)(1.0 / sqrt((double)s.D * (double)s.N));
-  s.chunk = p->scan_chunk == 0 ? kDefaultChunk : p->scan_chunk;
+  s.chunk = p->scan_chunk == 0 ? default_chunk(s.B * s.H) : p->scan_chunk;
   if (s.chunk > s.T) s.chunk = (int)s.T;
   s.mat = s.B * s.H * s.T * s.D * s.D * s.es;
   s.parts = s.chunk <= 1 ? 1 : (s.T + s.chunk - 1) / s.chunk;   // 1: sequential

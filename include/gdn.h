@@ -125,7 +125,9 @@ typedef struct {
     int32_t io_dtype;     /* gdn_dtype of q, k, v, o, d_o, dq, dk, dv        */
     float key_scale;      /* 0 => 1/sqrt(Dk * N), the 1/sqrt(D S) of the
                              summary page (module 2; novelty point 1)        */
-    int32_t scan_chunk;   /* inter-frame scan: 0 => library default,
+    int32_t scan_chunk;   /* inter-frame scan: 0 => library default (chunks
+                             of 16 frames for at most 8 sequences B H, 32
+                             for at most 16, else sequential),
                              1 => sequential over frames,
                              c >= 2 => composite prefix over chunks of c
                              frames (novelty point 1); same result up to

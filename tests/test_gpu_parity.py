@@ -208,7 +208,7 @@ def test_step_chain_equals_forward(io):
                           with_state=True)
     d = {k: to_dev(v) for k, v in inp.items()}
     o_full, s_full = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
-                                state_in=d["state"], algorithm="frame")
+                                state_in=d["state"], algorithm="frame", scan_chunk=1)
     state = d["state"].clone()
     outs = []
     for t in range(T):
@@ -238,12 +238,13 @@ def test_chunk_causal_windows_equal_one_call(io):
                           with_state=True)
     d = {k: to_dev(v) for k, v in inp.items()}
     o_full, s_full = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
-                                state_in=d["state"], algorithm="frame")
+                                state_in=d["state"], algorithm="frame", scan_chunk=1)
     state = d["state"].clone()
     outs = []
     for t0, t1 in [(0, 1), (1, 9), (9, 17)]:
         sl = slice(t0 * N, t1 * N)
-        plan = gb.ForwardPlan(B, H, t1 - t0, N, D, io, torch.device(DEV), algorithm="frame")
+        plan = gb.ForwardPlan(B, H, t1 - t0, N, D, io, torch.device(DEV), algorithm="frame",
+                              scan_chunk=1)
         o, st = plan(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
                      d["v"][:, sl].contiguous(), d["gamma"][:, t0:t1].contiguous(),
                      d["beta"][:, sl].contiguous(), state_in=state, state_out=state)
@@ -555,3 +556,19 @@ def test_train_minute_config_sampled_heads():
         e = rel_l2(f64(g), ref[name])
         print("minute backward %s: %.3e" % (name, e))
         assert e <= TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_default_scan_is_chunked_for_few_sequences(io):
+    # scan_chunk = 0 takes composite chunks of 16 frames for at most 8
+    # sequences: bit-identical to asking for them, and on the oracle's result
+    B, H, T, N, D = 1, 2, 40, 60, 64
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, gamma="uniform", seed=24,
+                          with_state=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    args = (d["q"], d["k"], d["v"], d["gamma"], d["beta"], N)
+    o0, s0 = gb.forward(*args, state_in=d["state"], algorithm="frame")
+    o16, s16 = gb.forward(*args, state_in=d["state"], algorithm="frame", scan_chunk=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o16) and torch.equal(s0, s16)
+    check_forward(inp, N, io, with_state=True)
