@@ -173,6 +173,12 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(dom), "algorithmic_bytes": abytes,
             "avg_ms": round(phases[dom], 4)}
+    copy_gbs = copy_ceiling()
+    roof["copy_gbs"] = round(copy_gbs, 1)
+    roof["frac_of_copy"] = round(achieved / copy_gbs, 4)
+    if roof["traffic"]:
+        roof["traffic_gbs"] = round(roof["traffic"] / (phases[dom] * 1e-3) / 1e9, 1)
+        roof["traffic_frac_of_copy"] = round(roof["traffic_gbs"] / copy_gbs, 4)
     fbytes, fflops = algorithmic("forward", B, H, D, T, N)
     step_roof = {"bound": "hbm", "achieved": round(fbytes / (ms_step * 1e-3) / 1e9, 1),
                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -211,6 +217,28 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def copy_ceiling(nbytes=1 << 30, reps=10):
+    """Device-to-device copy bandwidth (read + write bytes / time) of a plain
+    torch copy of `nbytes`: the practical HBM ceiling the kernels are also
+    set against."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def bench_train(gb, d, B, H, D, T, N, steps):

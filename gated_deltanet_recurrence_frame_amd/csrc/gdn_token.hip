@@ -75,8 +75,20 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
   constexpr int FLD = Y::FLD, DLD = Y::DLD;
   constexpr int NW = 8, NTH = 512;
 
-  __shared__ float KKs[CP * FLD];      // K^ K^^T, then L in place
-  __shared__ float KQs[CP * FLD];      // K Q^T, then (I + L)^-1
+  constexpr int KLD = Y::KLD, EP = Y::EP;
+  constexpr int PRD = D * Y::ES / 16;                 // 16-byte pieces of a row inside D
+  constexpr int PRP = DP * Y::ES / 16;                // ... of a staged (zero-padded) row
+  constexpr int NPC = 2 * CP * PRP;                   // staged pieces of K and Q
+  constexpr int NPJ = (NPC + NTH - 1) / NTH;
+  constexpr int STG = 2 * CP * KLD * Y::ES;           // K, Q rows staged
+  constexpr int GRM = 2 * CP * FLD * 4;               // the two token x token matrices
+  // The chunk's K and Q rows, staged; once the Gram tiles are in registers
+  // the same bytes hold K^ K^^T (then L in place) and K Q^T (then (I + L)^-1).
+  __shared__ __attribute__((aligned(16))) char Rg[STG > GRM ? STG : GRM];
+  E* Ks = reinterpret_cast<E*>(Rg);
+  E* Qs = Ks + CP * KLD;
+  float* KKs = reinterpret_cast<float*>(Rg);
+  float* KQs = KKs + CP * FLD;
   __shared__ float Dt[(CP + 1) * DLD];  // Dt[x][c] = P(x, c - 1)
   __shared__ float Ys[NB][256];
   __shared__ float gs[CP], bs[CP];
@@ -115,17 +127,39 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // 1. the chunk's gates
+  // 1. the chunk's gates and its K and Q rows (zero past C and D), every
+  // load in flight at once: unconditional loads from clamped addresses, the
+  // values past the chunk or the row replaced by zeros afterwards
   if (tid < CP) {
     gs[tid] = tid < nf ? a.gamma[((long)b * T + t0 + tid) * a.H + h] : 0.f;
     bs[tid] = tid < C ? a.beta[((long)b * L + tok0 + tid) * a.H + h] : 0.f;
     fr[tid] = tid / N;
   }
+  {
+    u32x4 pcs[NPJ];
+#pragma unroll
+    for (int j = 0; j < NPJ; ++j) {
+      const int p = min(tid + NTH * j, NPC - 1);
+      const int m = p / (CP * PRP), r = (p / PRP) % CP, pc = p % PRP;
+      const long off = (((long)b * L + tok0 + min(r, C - 1)) * a.H + h) * D + min(pc, PRD - 1) * EP;
+      pcs[j] = *reinterpret_cast<const u32x4*>((m ? Q : K) + off);
+    }
+#pragma unroll
+    for (int j = 0; j < NPJ; ++j) {
+      const int p = tid + NTH * j;
+      if (p < NPC) {
+        const int m = p / (CP * PRP), r = (p / PRP) % CP, pc = p % PRP;
+        const bool in = r < C && pc < PRD;
+        *reinterpret_cast<u32x4*>((m ? Qs : Ks) + r * KLD + pc * EP) =
+            in ? pcs[j] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
   block_sync();
 
   // 2. decay table: thread x runs the product over the chunk's gates, all
-  // of them first read into registers; K^ K^^T on blocks i <= j and K Q^T,
-  // their fragments read straight from the token rows (zero past C and D)
+  // of them first read into registers; K^ K^^T on blocks i <= j and K Q^T
+  // from the staged rows, into registers, then over the staged rows
   for (int x = tid; x <= nf; x += NTH) {
     float gv[CP];
 #pragma unroll
@@ -139,37 +173,42 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
       if (in) Dt[x * DLD + c + 1] = p;
     }
   }
-  auto gfrag = [&](const E* M, int u, int kb) {   // row u of the chunk, k block kb
-    const int k = kb * KS + (BF ? 8 * g : g);
-    const bool ok = u < C && k < D;
-    const long off = (((long)b * L + tok0 + (ok ? u : 0)) * a.H + h) * D + (ok ? k : 0);
-    if constexpr (BF) return ok ? load_bf16x8(M + off) : zero_bf16x8();
-    else return ok ? M[off] : 0.f;
-  };
   {
     constexpr int NP = NB * (NB + 1) / 2;
-    // a fixed trip count, so the loads of consecutive tiles overlap
     constexpr int TRIPS = (NP + NB * NB + NW - 1) / NW;
-#pragma unroll 2
+    f32x4 acc[TRIPS];
+    int tile[TRIPS];
+#pragma unroll
     for (int it = 0; it < TRIPS; ++it) {
       const int q = w + NW * it;
-      if (q >= NP + NB * NB) break;
-      int i, j;
-      const bool kq = q >= NP;
-      if (kq) {
-        i = (q - NP) / NB; j = (q - NP) % NB;
-      } else {
-        int rem = q; i = 0;
-        while (rem >= NB - i) { rem -= NB - i; ++i; }
-        j = i + rem;
-      }
-      const E* Bm = kq ? Q : K;
-      f32x4 acc = zero4();
-      for (int kb = 0; kb < DP / KS; ++kb)
-        acc = mma(gfrag(K, 16 * i + li, kb), gfrag(Bm, 16 * j + li, kb), acc);
-      float* dst = kq ? KQs : KKs;
+      acc[it] = zero4();
+      tile[it] = -1;
+      if (q < NP + NB * NB) {
+        int i, j;
+        const bool kq = q >= NP;
+        if (kq) {
+          i = (q - NP) / NB; j = (q - NP) % NB;
+        } else {
+          int rem = q; i = 0;
+          while (rem >= NB - i) { rem -= NB - i; ++i; }
+          j = i + rem;
+        }
+        const E* Bm = kq ? Qs : Ks;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * FLD + 16 * j + li] = acc[r];
+        for (int kb = 0; kb < DP / KS; ++kb)
+          acc[it] = mma(fragA(Ks, KLD, 16 * i, kb * KS), fragA(Bm, KLD, 16 * j, kb * KS), acc[it]);
+        tile[it] = (kq ? 1 << 16 : 0) | (i << 8) | j;
+      }
+    }
+    block_sync();   // every wave's reads of the staged rows are done
+#pragma unroll
+    for (int it = 0; it < TRIPS; ++it) {
+      if (tile[it] >= 0) {
+        const int i = (tile[it] >> 8) & 255, j = tile[it] & 255;
+        float* dst = (tile[it] >> 16) ? KQs : KKs;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * i + 4 * g + r) * FLD + 16 * j + li] = acc[it][r];
+      }
     }
   }
   block_sync();
@@ -199,18 +238,19 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
   block_sync();
 
   // 4. (I + L)^-1 into KQs: diagonal blocks by substitution (lane c holds
-  // column c), then block back-substitution by distance
+  // column c; column-oriented, so that the updates of one step are
+  // independent and the dependent chain is 15 steps long, not 120), then
+  // block back-substitution by distance
   for (int I = w; I < NB; I += NW) {
     if (g == 0) {
       const float* Lb = &KKs[16 * I * FLD + 16 * I];
       float x[16];
 #pragma unroll
-      for (int i = 15; i >= 0; --i) {
-        float acc = (i == li) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == li) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = i + 1; j < 16; ++j) acc -= Lb[i * FLD + j] * x[j];
-        x[i] = acc;
-      }
+      for (int j = 15; j > 0; --j)
+#pragma unroll
+        for (int i = 0; i < j; ++i) x[i] -= Lb[i * FLD + j] * x[j];
 #pragma unroll
       for (int i = 0; i < 16; ++i) KQs[(16 * I + i) * FLD + 16 * I + li] = x[i];
     }
