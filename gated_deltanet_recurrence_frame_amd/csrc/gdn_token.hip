@@ -286,8 +286,10 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
 
 // ---------------------------------------------------------------------------
 // The state pass: one workgroup per (b, h), wave w owns state rows
-// 16 w .. 16 w + 15 (in fp32 registers), chunks in order.
-template <int IO, int NT>
+// 16 w .. 16 w + 15 (in fp32 registers), chunks in order.  OUTS: the pass
+// emits outputs (TOK_PLAIN, TOK_REPLAY); the composite pass does not, and
+// neither loads Q and Om nor forms E_0 Q^T and W Om.
+template <int IO, int NT, bool OUTS>
 __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
   typedef TokLayout<IO, NT> Y;
   typedef typename Y::E E;
@@ -372,11 +374,12 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
       P.pc[j] = u32x4{0u, 0u, 0u, 0u};
       if (p < NKQ) {
         const int m = p / (CP * PR), q = p % (CP * PR), u = q / PR;
-        if (u < Cn)
+        if (u < Cn && (OUTS || m == 0))
           P.pc[j] = *reinterpret_cast<const u32x4*>(
               (m ? Q : K) + (((long)b * L + tok0 + u) * a.H + h) * D + (q % PR) * EP);
       } else if (p < NPC) {
-        P.pc[j] = *reinterpret_cast<const u32x4*>(rec + (long)(p - NKQ) * 16);
+        if (OUTS || p - NKQ < CP * CPR || p >= NKQ + NOP)   // no Om without outputs
+          P.pc[j] = *reinterpret_cast<const u32x4*>(rec + (long)(p - NKQ) * 16);
       }
     }
 #pragma unroll
@@ -459,7 +462,7 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
 #pragma unroll
         for (int kb = 0; kb < DP / KS; ++kb) {
           sk = mma(af[kb], fragA(Ks, KLD, 16 * j, kb * KS), sk);
-          sq = mma(af[kb], fragA(Qs, KLD, 16 * j, kb * KS), sq);
+          if constexpr (OUTS) sq = mma(af[kb], fragA(Qs, KLD, 16 * j, kb * KS), sq);
         }
         SK[j] = sk;
         SQ[j] = sq;
@@ -508,12 +511,12 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
       const float tail = vec[2 * CP + t];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        Zw[(4 * g + r) * ZLD + t] = toE(Wr[j][r]);
+        if constexpr (OUTS) Zw[(4 * g + r) * ZLD + t] = toE(Wr[j][r]);
         Zw[(4 * g + r) * ZLD + CP + t] = toE(Wr[j][r] * tail);
       }
     }
     fence();
-    {
+    if constexpr (OUTS) {
       decltype(fragA(Zw, ZLD, 0, 0)) wf[CP / KS];
 #pragma unroll
       for (int kb = 0; kb < CP / KS; ++kb) wf[kb] = fragA(Zw, ZLD, 0, kb * KS);
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
 #pragma unroll
         for (int kb = 0; kb < CP / KS; ++kb) acc = mma(wf[kb], fragA(OmT, TLD, 16 * j, kb * KS), acc);
         const int t = 16 * j + li;
-        if (!phi && a.mode != TOK_COMPOSITE && t < C) {
+        if (t < C) {
           const float upto = vec[CP + t];
           f32x4 ov;
 #pragma unroll
@@ -590,7 +593,10 @@ static hipError_t launch_token_io(const TokArgs& a, int nt, bool prep, hipStream
 #define GDN_TOK_CASE(n)                                                               \
   case n:                                                                             \
     if (prep) hipLaunchKernelGGL((token_prep_kernel<IO, n>), pgrid, pblock, 0, s, a); \
-    hipLaunchKernelGGL((token_scan_kernel<IO, n>), sgrid, sblock, 0, s, a);           \
+    if (a.mode == TOK_COMPOSITE)                                                       \
+      hipLaunchKernelGGL((token_scan_kernel<IO, n, false>), sgrid, sblock, 0, s, a);  \
+    else                                                                               \
+      hipLaunchKernelGGL((token_scan_kernel<IO, n, true>), sgrid, sblock, 0, s, a);   \
     break;
     GDN_TOK_CASE(1) GDN_TOK_CASE(2) GDN_TOK_CASE(3) GDN_TOK_CASE(4)
     GDN_TOK_CASE(5) GDN_TOK_CASE(6) GDN_TOK_CASE(7) GDN_TOK_CASE(8)
