@@ -139,8 +139,8 @@ int64_t token_chunks(const Shape& s) {
 }
 // Segments walked in parallel: about 256 (b, h, segment) items (two walks
 // each in the composite pass), at least 8 chunks per segment.  (Token-wise
-// GDN at 106,480 tokens and 20 heads: 4.17 ms with 128 items, 3.52 with
-// 256, 3.55 with 512.)
+// GDN at 106,480 tokens and 20 heads, before the prep kernel staged its
+// rows: 4.17 ms with 128 items, 3.52 with 256, 3.55 with 512.)
 int64_t token_segments(const Shape& s) {
   int64_t n = 256 / (s.B * s.H);
   const int64_t most = token_chunks(s) / 8;
