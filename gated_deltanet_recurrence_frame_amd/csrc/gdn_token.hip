@@ -54,7 +54,6 @@ struct TokLayout {
   static constexpr int KLD = DP + PAD;                // K, Q rows in LDS
   static constexpr int FLD = CP + 1;                  // fp32 token x token matrices
   static constexpr int TLD = CP + PAD;                // MFMA copies of them
-  static constexpr int DLD = CP + 1;                  // decay table
   static constexpr int ES = Io<IO>::bytes;
   static constexpr int PR = D * ES / 16;              // 16-byte pieces of a token row
   static constexpr int EP = 16 / ES;                  // elements per piece
@@ -72,7 +71,7 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
   typedef typename Y::E E;
   constexpr bool BF = Y::BF;
   constexpr int D = Y::D, CP = Y::CP, NB = Y::NB, KS = Y::KS, DP = Y::DP;
-  constexpr int FLD = Y::FLD, DLD = Y::DLD;
+  constexpr int FLD = Y::FLD;
   constexpr int NW = 8, NTH = 512;
 
   constexpr int KLD = Y::KLD, EP = Y::EP;
@@ -89,7 +88,9 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
   E* Qs = Ks + CP * KLD;
   float* KKs = reinterpret_cast<float*>(Rg);
   float* KQs = KKs + CP * FLD;
-  __shared__ float Dt[(CP + 1) * DLD];  // Dt[x][c] = P(x, c - 1)
+  // Dt(x, c) = P(x, c - 1) for x <= c <= CP, rows packed (the upper
+  // triangle only: three workgroups per CU fit in LDS)
+  __shared__ float Dt[(CP + 1) * (CP + 2) / 2];
   __shared__ float Ys[NB][256];
   __shared__ float gs[CP], bs[CP];
   __shared__ int fr[CP];
@@ -126,6 +127,8 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
     __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));
     asm volatile("" ::: "memory");
   };
+  // index of Dt(x, c); c < x (a value the caller discards) reads Dt(x, x)
+  auto dti = [](int x, int c) { return x * (CP + 1) - x * (x - 1) / 2 + (c > x ? c - x : 0); };
 
   // 1. the chunk's gates and its K and Q rows (zero past C and D), every
   // load in flight at once: unconditional loads from clamped addresses, the
@@ -165,12 +168,12 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
 #pragma unroll
     for (int c = 0; c < CP; ++c) gv[c] = gs[c];
     float p = 1.f;
-    Dt[x * DLD + x] = 1.f;
+    Dt[dti(x, x)] = 1.f;
 #pragma unroll
     for (int c = 0; c < CP; ++c) {
       const bool in = c >= x && c < nf;
       p = in ? p * gv[c] : p;
-      if (in) Dt[x * DLD + c + 1] = p;
+      if (in) Dt[dti(x, c + 1)] = p;
     }
   }
   {
@@ -223,17 +226,17 @@ __global__ __launch_bounds__(512) void token_prep_kernel(TokArgs a) {
     const bool valid = u < C && t < C;
     const int fu = fr[u], ft = fr[t];
     const float kk = KKs[u * FLD + t], kq = KQs[u * FLD + t];
-    KKs[u * FLD + t] = (valid && fu < ft) ? s2 * kk * Dt[(fu + 1) * DLD + ft] * bs[t] : 0.f;
-    OmT[t * CP + u] = toE((valid && fu <= ft) ? s * kq * Dt[(fu + 1) * DLD + ft + 1] : 0.f);
+    KKs[u * FLD + t] = (valid && fu < ft) ? s2 * kk * Dt[dti(fu + 1, ft)] * bs[t] : 0.f;
+    OmT[t * CP + u] = toE((valid && fu <= ft) ? s * kq * Dt[dti(fu + 1, ft + 1)] : 0.f);
   }
   if (tid < CP) {
     const int t = tid, f = fr[t];
     const bool valid = t < C;
-    vec[t] = valid ? Dt[f] : 0.f;                            // P(0, f(t) - 1)
-    vec[CP + t] = valid ? Dt[f + 1] : 0.f;                   // P(0, f(t))
-    vec[2 * CP + t] = valid ? Dt[(f + 1) * DLD + nf] : 0.f;  // P(f(t) + 1, F - 1)
+    vec[t] = valid ? Dt[dti(0, f)] : 0.f;                    // P(0, f(t) - 1)
+    vec[CP + t] = valid ? Dt[dti(0, f + 1)] : 0.f;           // P(0, f(t))
+    vec[2 * CP + t] = valid ? Dt[dti(f + 1, nf)] : 0.f;      // P(f(t) + 1, F - 1)
     vec[3 * CP + t] = bs[t];                                 // beta_t
-    vec[4 * CP + t] = t == 0 ? Dt[nf] : 0.f;                 // P(0, F - 1)
+    vec[4 * CP + t] = t == 0 ? Dt[dti(0, nf)] : 0.f;         // P(0, F - 1)
   }
   block_sync();
 
