@@ -3,13 +3,19 @@
 
 One step = one gdn_forward over one GDN layer at the one-minute 720p shape
 (B = 1, 20 heads, D = 112, 121 latent frames x 880 tokens = 106,480 tokens,
-bf16 Q/K/V/O, fp32 gates and state), inputs resident in HBM.  Prints one JSON
-line: tokens/s, the roofline of the dominant kernel (phase times from HIP
-events recorded by the library between its kernels, on the stream they run
-on), and the float64 CPU oracle timed on a bounded sample of the same
-workload.  Extras: forward + backward at the same shape, 121 streaming
-gdn_step calls, chunk-causal streaming by windows of latent frames, and
-token-wise GDN (one token per frame) in the token form.
+bf16 Q/K/V/O, fp32 gates and state), inputs resident in HBM.
+
+Before the W warm-up steps the forward runs untimed for --ramp-seconds so
+that the GPU's clocks have settled; the K timed steps are plain gdn_forward
+calls between two device synchronisations.  A separate, untimed pass with
+the library's phase events (gdn_forward_events, HIP events on the stream the
+kernels run on) gives each kernel's average duration, from which the
+roofline of the dominant kernel is computed.  Prints one JSON line:
+tokens/s, that roofline, and the float64 CPU oracle timed on a bounded
+sample of the same workloads.  Extras: forward + backward at the same shape,
+121 streaming gdn_step calls, chunk-causal streaming by windows of latent
+frames, token-wise GDN (one token per frame) in the token form, and the
+fused block prologue.
 """
 
 import argparse
@@ -84,37 +90,86 @@ def load_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s):
-    """The float64 oracle, untouched, on whole heads of the same workload
-    until the time budget is spent; scaled to layer tokens/s."""
-    import numpy as np  # noqa: F401
-    import oracle
-    from gated_deltanet_recurrence_frame_amd import inputs as gin
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = sum(p.get("num_threads", 1) for p in threadpool_info()
-                    if p.get("user_api") == "blas") or 1
+        return sum(p.get("num_threads", 1) for p in threadpool_info()
+                   if p.get("user_api") == "blas") or 1
     except Exception:
-        cores = 1
+        return 1
+
+
+def _oracle_heads(inp, fn, budget_s, T):
+    """Call fn(per-head float64 tensors) on whole heads in turn (again from
+    the first head while the budget lasts); returns one-layer tokens/s
+    (heads scaled to the layer) and the sample's description."""
+    from gated_deltanet_recurrence_frame_amd import inputs as gin
     H, N = SHAPE["H"], SHAPE["N"]
     done, t_total = 0, 0.0
-    # heads in turn (all 121 frames each), again from the first head while
-    # the budget lasts
     while t_total < budget_s:
-        h = done % H
-        sl = slice(h, h + 1)
-        q, k, v = (gin.as_f64(inp[x][:, :, sl]) for x in ("q", "k", "v"))
-        g, b = gin.as_f64(inp["gamma"][:, :, sl]), gin.as_f64(inp["beta"][:, :, sl])
+        sl = slice(done % H, done % H + 1)
+        x = {n: gin.as_f64(inp[n][:, :T * N, sl]) for n in ("q", "k", "v", "beta", "d_o")
+             if n in inp}
+        x["gamma"] = gin.as_f64(inp["gamma"][:, :T, sl])
         t0 = time.perf_counter()
-        oracle.forward(q, k, v, g, b, N)
+        fn(x)
         t_total += time.perf_counter() - t0
         done += 1
-    tokens = SHAPE["B"] * SHAPE["T"] * N
-    return {"value": tokens * (done / H) / t_total, "unit": "tokens/s", "cores": int(cores),
+    tokens = SHAPE["B"] * T * N
+    return tokens * (done / H) / t_total, done, t_total
+
+
+def cpu_baseline(inp, budget_s):
+    """The float64 oracle, untouched, on whole heads of the workloads until
+    each leg's share of the time budget is spent, scaled to one layer's
+    tokens/s.  The headline value is the one-minute forward on all the BLAS
+    threads the host gives; beside it the same forward on one thread, the
+    short clip, the 121 streaming steps and forward + backward."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    N = SHAPE["N"]
+    T = SHAPE["T"]
+    fwd = lambda x: oracle.forward(x["q"], x["k"], x["v"], x["gamma"], x["beta"], N)
+
+    def stream(x):
+        S = None                        # frame 0 from a zero state
+        for t in range(T):
+            sl = slice(t * N, (t + 1) * N)
+            _, S = oracle.step(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl],
+                               x["gamma"][:, t:t + 1], x["beta"][:, sl], S)
+
+    def train(x):
+        fwd(x)
+        oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["beta"], N, x["d_o"])
+
+    threads = _blas_threads()
+    legs = {}
+    share = {"forward_minute": 0.4, "forward_minute_1thread": 0.15, "forward_short": 0.1,
+             "stream_minute": 0.15, "train_minute": 0.2}
+    for name, fn, frames, one in (("forward_minute", fwd, T, False),
+                                  ("forward_minute_1thread", fwd, T, True),
+                                  ("forward_short", fwd, 21, False),
+                                  ("stream_minute", stream, T, False),
+                                  ("train_minute", train, T, False)):
+        if name == "train_minute" and "d_o" not in inp:
+            continue
+        if one:
+            with threadpool_limits(limits=1):
+                v, done, secs = _oracle_heads(inp, fn, budget_s * share[name], frames)
+        else:
+            v, done, secs = _oracle_heads(inp, fn, budget_s * share[name], frames)
+        legs[name] = {"tokens_per_s": round(v, 1), "head_passes": done,
+                      "seconds": round(secs, 2), "threads": 1 if one else threads}
+    main = legs["forward_minute"]
+    return {"value": main["tokens_per_s"], "unit": "tokens/s", "cores": threads,
+            "nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
             "kind": "oracle",
-            "sample": "float64 oracle forward on %d head passes over the %d heads (each all 121 "
-                      "frames x 880 tokens), %.1f s, scaled by heads to one-layer tokens/s"
-                      % (done, H, t_total)}
+            "sample": "float64 oracle (numpy, %d BLAS threads) forward on %d whole heads of the "
+                      "1-min shape (121 x 880 tokens each, the 20 heads in turn), %.1f s, scaled "
+                      "by heads to one-layer tokens/s; legs: the same on one thread, the short "
+                      "clip (21 frames), 121 oracle steps, forward + backward"
+                      % (threads, main["head_passes"], main["seconds"]),
+            "legs": legs}
 
 
 def main():
@@ -123,7 +178,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--scan-chunk", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ramp-seconds", type=float, default=1.0,
+                    help="untimed forwards before the warm-up steps (GPU clocks settle)")
+    ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     args = ap.parse_args()
@@ -145,26 +202,39 @@ def main():
     torch.cuda.synchronize()
 
     plan = gb.ForwardPlan(B, H, T, N, D, "bf16", dev, scan_chunk=args.scan_chunk)
-    ev = HipEvents(4 * args.steps)
-    print("[bench] warmup", file=sys.stderr, flush=True)
+    fwd = lambda: plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    print("[bench] clock ramp (%.1f s) and %d warm-up steps" % (args.ramp_seconds, args.warmup),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.ramp_seconds:
+        for _ in range(20):
+            fwd()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
-        plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+        fwd()
     torch.cuda.synchronize()
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"], events=ev.ev[4 * i:4 * i + 4])
+    for _ in range(args.steps):
+        fwd()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    tokens = B * T * N
+    value = tokens / (ms_step * 1e-3)
+
+    # phases: a separate, untimed pass with the library's events
+    nph = max(10, min(args.steps, 50))
+    ev = HipEvents(4 * nph)
+    for i in range(nph):
+        plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"], events=ev.ev[4 * i:4 * i + 4])
+    torch.cuda.synchronize()
     phases = {"gram": 0.0, "scan": 0.0, "output": 0.0}
-    for i in range(args.steps):
+    for i in range(nph):
         phases["gram"] += ev.elapsed(4 * i, 4 * i + 1)
         phases["scan"] += ev.elapsed(4 * i + 1, 4 * i + 2)
         phases["output"] += ev.elapsed(4 * i + 2, 4 * i + 3)
-    phases = {k: v / args.steps for k, v in phases.items()}
-    tokens = B * T * N
-    value = tokens / (ms_step * 1e-3)
+    phases = {k: v / nph for k, v in phases.items()}
 
     dom = max(("gram", "output"), key=lambda k: phases[k])
     abytes, aflops = algorithmic(dom, B, H, D, T, N)
@@ -172,7 +242,8 @@ def main():
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(dom), "algorithmic_bytes": abytes,
-            "avg_ms": round(phases[dom], 4)}
+            "avg_ms": round(phases[dom], 4), "timing": "phase events, separate pass of %d "
+                                                      "forwards" % nph}
     copy_gbs = copy_ceiling()
     roof["copy_gbs"] = round(copy_gbs, 1)
     roof["frac_of_copy"] = round(achieved / copy_gbs, 4)
@@ -192,7 +263,7 @@ def main():
         print("[bench] forward+backward", file=sys.stderr, flush=True)
         extra["train"] = bench_train(gb, d, B, H, D, T, N, max(3, args.steps // 4))
         print("[bench] streaming steps", file=sys.stderr, flush=True)
-        extra["stream"] = bench_stream(gb, d, B, H, D, T, N, ev)
+        extra["stream"] = bench_stream(gb, d, B, H, D, T, N)
         print("[bench] streaming windows", file=sys.stderr, flush=True)
         extra["windows"] = [bench_windows(gb, d, B, H, D, T, N, k) for k in (2, 8, 15)]
         print("[bench] token-wise GDN (token form)", file=sys.stderr, flush=True)
@@ -262,13 +333,17 @@ def bench_train(gb, d, B, H, D, T, N, steps):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     tokens = B * T * N
-    nbytes = tokens * H * (7 * D * 2 + 8)       # Q,K,V,dO read; dQ,dK,dV write; beta, dbeta
+    # algorithmic bytes of forward + backward: the forward's Q, K, V read, O
+    # written (bf16), beta read (fp32); the backward's Q, K, V, dO read,
+    # dQ, dK, dV written (bf16), beta read, dbeta written (fp32)
+    nbytes = tokens * H * ((4 * D * 2 + 4) + (7 * D * 2 + 8))
     return {"workload": "gdn_forward + gdn_backward (saved A_t, S_t), 1-min shape",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "algorithmic_bytes": nbytes,
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "steps": steps}
 
 
-def bench_stream(gb, d, B, H, D, T, N, ev):
+def bench_stream(gb, d, B, H, D, T, N):
     import torch
     dev = d["q"].device
     state = torch.zeros((B, H, D, D), dtype=torch.float32, device=dev)

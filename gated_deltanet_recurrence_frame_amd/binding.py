@@ -1,10 +1,17 @@
 """Thin ctypes binding over libgdn's C ABI (include/gdn.h).
 
-Argument marshalling only: tensors are checked for device, dtype, shape and
-contiguity, outputs and workspace are allocated with torch on the tensors'
-device, and the C entry point is called on torch's current stream.  Every
-step of the computation runs in the HIP kernels of libgdn.so; if the library
-is missing the first call raises.
+Argument marshalling only: every tensor argument is checked for device,
+dtype, shape and contiguity before the C entry point is called, outputs and
+workspace are allocated with torch on the tensors' device, and the entry
+point runs on torch's current stream.  Every step of the computation runs in
+the HIP kernels of libgdn.so; if the library is missing the first call
+raises.
+
+``POISON``: when true, every output, state and workspace buffer the binding
+allocates is filled with all-ones bytes (NaN in bf16 and fp32) before the
+library sees it, so that an element a kernel fails to write shows up as NaN
+instead of a stale value from the caching allocator.  The parity tests turn
+it on.
 """
 
 import ctypes
@@ -45,6 +52,15 @@ class GdnError(RuntimeError):
 
 _lib = None
 _VP = ctypes.c_void_p
+POISON = False
+
+
+def _empty(shape, dtype, device):
+    """torch.empty, filled with NaN bytes when POISON is set."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if POISON and t.numel():
+        t.view(torch.uint8).fill_(255)
+    return t
 
 
 def lib():
@@ -184,13 +200,27 @@ class ForwardPlan:
                  algorithm="auto", flags=0):
         self.prob = make_problem(B, H, T, N, D, io, key_scale, scan_chunk, algorithm, flags)
         dt = torch.bfloat16 if io == "bf16" else torch.float32
-        self.o = torch.empty((B, T * N, H, D), dtype=dt, device=device)
-        self.state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=device)
-        self.ws = torch.empty(max(16, workspace_size(self.prob, GDN_OP_FORWARD)),
-                              dtype=torch.uint8, device=device)
-        self.saved = (torch.empty(saved_size(self.prob), dtype=torch.uint8, device=device)
-                      if saved else None)
+        device = torch.device(device)
+        self.o = _empty((B, T * N, H, D), dt, device)
+        self.state_out = _empty((B, H, D, D), torch.float32, device)
+        self.ws = _empty(max(16, workspace_size(self.prob, GDN_OP_FORWARD)), torch.uint8, device)
+        self.saved = _empty(saved_size(self.prob), torch.uint8, device) if saved else None
         self.device = device
+        self.dtype = dt
+        self.dims = (B, H, T, N, D)
+
+    def check(self, q, k, v, gamma, beta, state_in=None, state_out=None):
+        """Raise unless every tensor matches the plan's device, dtype, shape
+        and layout (nothing is launched on a mismatch)."""
+        B, H, T, N, D = self.dims
+        dev, dt = self.device, self.dtype
+        for t, name in ((q, "q"), (k, "k"), (v, "v")):
+            _need(t, name, dt, (B, T * N, H, D), dev)
+        _need(gamma, "gamma", torch.float32, (B, T, H), dev)
+        _need(beta, "beta", torch.float32, (B, T * N, H), dev)
+        for t, name in ((state_in, "state_in"), (state_out, "state_out")):
+            if t is not None:
+                _need(t, name, torch.float32, (B, H, D, D), dev)
 
     def __call__(self, q, k, v, gamma, beta, state_in=None, events=None, state_out=None):
         """events: None, or 4 raw hipEvent_t handles (ints) recorded around
@@ -198,10 +228,8 @@ class ForwardPlan:
         state_out: None (the plan's own buffer), or a [B, H, D, D] fp32
         tensor, which may be state_in itself (the state carried in place
         from one call to the next)."""
+        self.check(q, k, v, gamma, beta, state_in, state_out)
         so = self.state_out if state_out is None else state_out
-        if state_out is not None:
-            _need(state_out, "state_out", torch.float32, tuple(self.state_out.shape),
-                  self.device)
         args = (ctypes.byref(self.prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
                 _p(state_in), _p(self.o), _p(so), _p(self.saved), _p(self.ws),
                 self.ws.numel(), _stream(self.device))
@@ -238,15 +266,26 @@ class StepPlan:
     def __init__(self, B, H, N, D, io, device, key_scale=0.0, algorithm="auto", flags=0):
         self.prob = make_problem(B, H, 1, N, D, io, key_scale, 0, algorithm, flags)
         dt = torch.bfloat16 if io == "bf16" else torch.float32
-        self.o = torch.empty((B, N, H, D), dtype=dt, device=device)
-        self.ws = torch.empty(max(16, workspace_size(self.prob, GDN_OP_STEP)), dtype=torch.uint8,
-                              device=device)
+        device = torch.device(device)
+        self.o = _empty((B, N, H, D), dt, device)
+        self.ws = _empty(max(16, workspace_size(self.prob, GDN_OP_STEP)), torch.uint8, device)
         self.device = device
+        self.dtype = dt
         self.shape = (B, N, H, D)
 
+    def check(self, q, k, v, gamma, beta, state):
+        """Raise unless every tensor matches the plan (nothing is launched on
+        a mismatch)."""
+        B, N, H, D = self.shape
+        dev, dt = self.device, self.dtype
+        for t, name in ((q, "q"), (k, "k"), (v, "v")):
+            _need(t, name, dt, (B, N, H, D), dev)
+        _need(gamma, "gamma", torch.float32, (B, 1, H), dev)
+        _need(beta, "beta", torch.float32, (B, N, H), dev)
+        _need(state, "state", torch.float32, (B, H, D, D), dev)
+
     def __call__(self, q, k, v, gamma, beta, state):
-        if tuple(q.shape) != self.shape or tuple(state.shape[:2]) != self.shape[:1] + self.shape[2:3]:
-            raise ValueError("tensor shapes do not match the plan")
+        self.check(q, k, v, gamma, beta, state)
         _check(lib().gdn_step(ctypes.byref(self.prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
                               _p(state), _p(self.o), _p(self.ws), self.ws.numel(),
                               _stream(self.device)), "gdn_step")
@@ -261,10 +300,13 @@ def step(q, k, v, gamma, beta, state, key_scale=0.0, out=None, workspace=None,
     _need(state, "state", torch.float32, (B, H, D, D), dev)
     prob = make_problem(B, H, 1, N, D, _io_of(q), key_scale, 0, algorithm,
                         flags=flags_of(normalize_qk, gate_logits))
-    o = out if out is not None else torch.empty_like(v)
+    if out is not None:
+        _need(out, "out", q.dtype, tuple(v.shape), dev)
+    o = out if out is not None else _empty(tuple(v.shape), q.dtype, dev)
     if workspace is None:
-        workspace = torch.empty(max(16, workspace_size(prob, GDN_OP_STEP)), dtype=torch.uint8,
-                                device=dev)
+        workspace = _empty(max(16, workspace_size(prob, GDN_OP_STEP)), torch.uint8, dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
     _check(lib().gdn_step(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
                           _p(state), _p(o), _p(workspace), workspace.numel(), _stream(dev)),
            "gdn_step")
@@ -284,15 +326,16 @@ def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None, save
         _need(d_state_out, "d_state_out", torch.float32, (B, H, D, D), dev)
     prob = make_problem(B, H, T, n, D, _io_of(q), key_scale, scan_chunk,
                         flags=flags_of(normalize_qk, gate_logits))
-    if saved is not None and saved.numel() != saved_size(prob):
-        raise ValueError("saved buffer has the wrong size")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dgamma = torch.empty_like(gamma)
-    dbeta = torch.empty_like(beta)
-    dstate = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    if saved is not None:
+        _need(saved, "saved", torch.uint8, (saved_size(prob),), dev)
+    dq, dk, dv = (_empty(tuple(t.shape), t.dtype, dev) for t in (q, k, v))
+    dgamma = _empty(tuple(gamma.shape), torch.float32, dev)
+    dbeta = _empty(tuple(beta.shape), torch.float32, dev)
+    dstate = _empty((B, H, D, D), torch.float32, dev)
     if workspace is None:
-        workspace = torch.empty(max(16, workspace_size(prob, GDN_OP_BACKWARD)),
-                                dtype=torch.uint8, device=dev)
+        workspace = _empty(max(16, workspace_size(prob, GDN_OP_BACKWARD)), torch.uint8, dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
     _check(lib().gdn_backward(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(gamma), _p(beta),
                               _p(state_in), _p(d_o), _p(d_state_out), _p(saved), _p(dq),
                               _p(dk), _p(dv), _p(dgamma), _p(dbeta), _p(dstate),

@@ -297,8 +297,10 @@ def backward(q, k, v, gamma, beta, n, d_o, state_in=None, d_state_out=None,
                 dv[b, sl, h, :] = ((G @ Kh) * bt).T
                 dKh = (G.T @ Vt) * bt + ((dA + dA.T) @ Kh) * bt
                 dk[b, sl, h, :] = (s * dKh).T
-                dbeta[b, sl, h] = (np.einsum("in,ij,jn->n", Vt, G, Kh)
-                                   + np.einsum("in,ij,jn->n", Kh, dA, Kh))
+                # dbeta_tn = v_tn^T G_t k^_tn + k^_tn^T dA_t k^_tn, one column
+                # (token) at a time: the column sums of V * (G K^) and K^ * (dA K^)
+                dbeta[b, sl, h] = (np.sum(Vt * (G @ Kh), axis=0)
+                                   + np.sum(Kh * (dA @ Kh), axis=0))
                 carry = G @ M.T
             dstate_in[b, h] = carry
     return {"dq": dq, "dk": dk, "dv": dv, "dgamma": dgamma, "dbeta": dbeta,

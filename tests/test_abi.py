@@ -205,3 +205,70 @@ def test_prologue_flags(lib):
         bad.flags = bit
         assert gb.STATUS[_ws(bad, gb.GDN_OP_FORWARD)[0]] == "GDN_ERR_UNSUPPORTED"
     assert gb.flags_of(True, False) == 1 and gb.flags_of(False, True) == 2
+
+
+def _cpu_inputs(B, H, T, N, D, dt):
+    import torch
+    L = T * N
+    return dict(q=torch.zeros((B, L, H, D), dtype=dt), k=torch.zeros((B, L, H, D), dtype=dt),
+                v=torch.zeros((B, L, H, D), dtype=dt),
+                gamma=torch.zeros((B, T, H), dtype=torch.float32),
+                beta=torch.zeros((B, L, H), dtype=torch.float32))
+
+
+def _mismatches(x, state_name):
+    """(argument overrides, expected exception) pairs, each one tensor wrong."""
+    import torch
+    q = x["q"]
+    B, L, H, D = q.shape
+    st = torch.zeros((B, H, D, D), dtype=torch.float32)
+    return [
+        ({"q": q.to(torch.float16)}, TypeError),                      # dtype
+        ({"k": x["k"][:, :-1]}, ValueError),                          # short rows
+        ({"v": x["v"].transpose(1, 2).contiguous().transpose(1, 2)}, ValueError),  # layout
+        ({"gamma": x["gamma"].double()}, TypeError),
+        ({"beta": x["beta"][..., :-1]}, ValueError),
+        ({state_name: st.to(torch.bfloat16)}, TypeError),             # bf16 state
+        ({state_name: st[:, :, :-1]}, ValueError),                    # wrong-sized state
+        ({state_name: st.transpose(2, 3)}, ValueError),               # non-contiguous state
+    ]
+
+
+def test_forward_plan_checks_every_tensor(lib):
+    # a mismatch in any tensor raises before the library is called
+    import torch
+    B, H, T, N, D = 1, 2, 3, 5, 16
+    plan = gb.ForwardPlan(B, H, T, N, D, "bf16", "cpu")
+    x = _cpu_inputs(B, H, T, N, D, torch.bfloat16)
+    x["state_in"] = None
+    for over, exc in _mismatches(x, "state_in"):
+        args = dict(x, **over)
+        with pytest.raises(exc):
+            plan(**args)
+    with pytest.raises(ValueError):
+        plan(**dict(x, state_out=torch.zeros((B, H, D, D + 1))))
+
+
+def test_step_plan_checks_every_tensor(lib):
+    import torch
+    B, H, N, D = 1, 2, 5, 16
+    plan = gb.StepPlan(B, H, N, D, "bf16", "cpu")
+    x = _cpu_inputs(B, H, 1, N, D, torch.bfloat16)
+    x["state"] = torch.zeros((B, H, D, D), dtype=torch.float32)
+    for over, exc in _mismatches(x, "state"):
+        with pytest.raises(exc):
+            plan(**dict(x, **over))
+    with pytest.raises(ValueError):      # gamma of two frames
+        plan(**dict(x, gamma=torch.zeros((B, 2, H))))
+
+
+def test_poisoned_buffers_are_nan(lib):
+    import torch
+    old = gb.POISON
+    gb.POISON = True
+    try:
+        plan = gb.ForwardPlan(1, 2, 3, 5, 16, "bf16", "cpu", saved=True)
+        assert torch.isnan(plan.o.float()).all() and torch.isnan(plan.state_out).all()
+        assert bool((plan.ws == 255).all()) and bool((plan.saved == 255).all())
+    finally:
+        gb.POISON = old

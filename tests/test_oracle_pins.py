@@ -606,3 +606,114 @@ def test_p14_finite_differences_catch_a_dropped_projection():
     fd = (_loss_pro(plus, d_o, d_st, N, s, True, False) -
           _loss_pro(minus, d_o, d_st, N, s, True, False)) / (2 * h)
     assert abs(fd - np.sum(wrong_dk * dirn)) > 1e-4 * max(1.0, abs(fd))
+
+
+# --------------------------------------------------------------------------
+# P15: the per-frame Gram A_t = K^_t beta_t K^_t^T and write
+# U_t = V_t beta_t K^_t^T (summary page, 方法步骤详情 module 2), as returned by
+# ``oracle.frame_terms``, against
+#   (a) token-by-token sums of rank-one outer products (brute force),
+#   (b) a closed form: keys that are scaled, permuted basis vectors make A_t a
+#       diagonal with known entries s^2 beta_j c_j^2 at the permuted places and
+#       put s beta_j c_j v_j in column pi(j) of U_t,
+#   (c) the A_t, U_t the recurrence itself keeps (forward(keep=True)),
+# and a mutation check: plausible mistakes (beta dropped, beta twice, the key
+# scale applied once, U_t transposed, the frames shifted by one, the head
+# index swapped) each fail (a) or (b).
+# --------------------------------------------------------------------------
+def _frame_terms_brute(k, v, beta, n, s):
+    B, L, H, D = k.shape
+    T = L // n
+    A = np.zeros((B, H, T, D, D))
+    U = np.zeros((B, H, T, v.shape[-1], D))
+    for b, h, t in itertools.product(range(B), range(H), range(T)):
+        for j in range(n):
+            l = t * n + j
+            kh = s * k[b, l, h]
+            A[b, h, t] += beta[b, l, h] * np.outer(kh, kh)
+            U[b, h, t] += beta[b, l, h] * np.outer(v[b, l, h], kh)
+    return A, U
+
+
+def _basis_problem(D, seed):
+    # one frame of N = D tokens per head; token j's key is c_j e_{pi(j)}
+    rng = np.random.default_rng(seed)
+    B, H = 1, 2
+    k = np.zeros((B, D, H, D))
+    perm = np.stack([rng.permutation(D) for _ in range(H)])
+    c = rng.uniform(0.5, 2.0, (H, D))
+    for h in range(H):
+        for j in range(D):
+            k[0, j, h, perm[h, j]] = c[h, j]
+    v = rng.standard_normal((B, D, H, D))
+    beta = rng.uniform(0.1, 1.0, (B, D, H))
+    return k, v, beta, perm, c
+
+
+def _frame_terms_errors(fn):
+    """Largest deviation of a frame_terms implementation from the pins (a), (b)."""
+    errs = []
+    q, k, v, g, beta, _ = _rand_problem(2, 3, 4, 3, 5, seed=40)
+    for key_scale in (0.0, 0.41):
+        s = key_scale or 1.0 / np.sqrt(5 * 3)
+        A, U = fn(k, v, beta, 3, key_scale=key_scale)
+        Ab, Ub = _frame_terms_brute(k, v, beta, 3, s)
+        errs += [np.max(np.abs(A - Ab)), np.max(np.abs(U - Ub))]
+    D = 6
+    k, v, beta, perm, c = _basis_problem(D, seed=41)
+    s = 0.7
+    A, U = fn(k, v, beta, D, key_scale=s)
+    for h in range(2):
+        Ac = np.zeros((D, D))
+        Uc = np.zeros((D, D))
+        for j in range(D):
+            p = perm[h, j]
+            Ac[p, p] = s * s * beta[0, j, h] * c[h, j] ** 2
+            Uc[:, p] = s * beta[0, j, h] * c[h, j] * v[0, j, h]
+        errs += [np.max(np.abs(A[0, h, 0] - Ac)), np.max(np.abs(U[0, h, 0] - Uc))]
+    return max(errs)
+
+
+def test_p15_frame_terms_pins():
+    assert _frame_terms_errors(oracle.frame_terms) < 1e-12
+    # (c) the same A_t, U_t as the recurrence keeps
+    q, k, v, g, beta, s0 = _rand_problem(1, 2, 5, 4, 6, seed=42)
+    A, U = oracle.frame_terms(k, v, beta, 4)
+    _, _, kept = oracle.forward(q, k, v, g, beta, 4, state_in=s0, keep=True)
+    assert np.max(np.abs(A - kept["A"])) < 1e-14
+    assert np.max(np.abs(U - kept["U"])) < 1e-14
+
+
+def _frame_terms_mutant(kind):
+    def fn(k, v, beta, n, key_scale=0.0):
+        B, L, H, Dk = k.shape
+        T = L // n
+        s = key_scale or 1.0 / np.sqrt(Dk * n)
+        A = np.zeros((B, H, T, Dk, Dk))
+        U = np.zeros((B, H, T, v.shape[-1], Dk))
+        for b, h, t in itertools.product(range(B), range(H), range(T)):
+            tt = max(t - 1, 0) if kind == "frame_shift" else t
+            hh = (h + 1) % H if kind == "head_swap" else h
+            sl = slice(tt * n, (tt + 1) * n)
+            Kh = s * k[b, sl, hh].T
+            Vt = v[b, sl, hh].T
+            bt = beta[b, sl, hh]
+            if kind == "beta_dropped":
+                A[b, h, t] = Kh @ Kh.T
+            elif kind == "beta_twice":
+                A[b, h, t] = (Kh * bt * bt) @ Kh.T
+            elif kind == "scale_once":
+                A[b, h, t] = (Kh * bt) @ Kh.T / s
+            else:
+                A[b, h, t] = (Kh * bt) @ Kh.T
+            Ut = (Vt * bt) @ Kh.T
+            U[b, h, t] = Ut.T if kind == "write_transposed" else Ut
+        return A, U
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["beta_dropped", "beta_twice", "scale_once",
+                                  "write_transposed", "frame_shift", "head_swap"])
+def test_p15_pins_catch_planted_mistakes(kind):
+    assert _frame_terms_errors(_frame_terms_mutant("none")) < 1e-12
+    assert _frame_terms_errors(_frame_terms_mutant(kind)) > 1e-6
