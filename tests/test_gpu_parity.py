@@ -558,13 +558,16 @@ def _minute_inputs():
     return _MINUTE
 
 
+_MINUTE_REF = {}
+
+
 def _minute_oracle_forward():
     """oracle.forward over all 20 heads of the one-minute inputs (cached)."""
-    if "ref_fwd" not in _MINUTE:
+    if not _MINUTE_REF:
         inp = _minute_inputs()
-        _MINUTE["ref_fwd"] = oracle.forward(*(f64(inp[k]) for k in ("q", "k", "v", "gamma",
+        _MINUTE_REF["fwd"] = oracle.forward(*(f64(inp[k]) for k in ("q", "k", "v", "gamma",
                                                                       "beta")), 880)
-    return _MINUTE["ref_fwd"]
+    return _MINUTE_REF["fwd"]
 
 
 def test_forward_minute_config_all_heads():
