@@ -29,10 +29,11 @@ GDN_OP_FORWARD, GDN_OP_STEP, GDN_OP_BACKWARD = 0, 1, 2
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
           3: "GDN_ERR_BAD_DTYPE", 4: "GDN_ERR_MISALIGNED",
           5: "GDN_ERR_WORKSPACE_TOO_SMALL", 6: "GDN_ERR_UNSUPPORTED",
-          7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIASING"}
+          7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIASING", 9: "GDN_ERR_SCRATCH_TOO_SMALL"}
 
 
-ABI_VERSION = 3   # GDN_ABI_VERSION of include/gdn.h that GdnProblem mirrors
+ABI_VERSION = 4   # GDN_ABI_VERSION of include/gdn.h that GdnProblem mirrors
+NOALLOC_SCRATCH_BYTES = 192 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 
 
 class GdnProblem(ctypes.Structure):
@@ -85,6 +86,8 @@ def lib():
     L.gdn_forward_events.restype = ctypes.c_int
     L.gdn_forward_events.argtypes = [P] + [_VP] * 10 + [ctypes.c_size_t, _VP,
                                                          ctypes.POINTER(_VP)]
+    L.gdn_forward_noalloc.restype = ctypes.c_int
+    L.gdn_forward_noalloc.argtypes = [P] + [_VP] * 10
     L.gdn_step.restype = ctypes.c_int
     L.gdn_step.argtypes = [P] + [_VP] * 8 + [ctypes.c_size_t, _VP]
     L.gdn_backward.restype = ctypes.c_int

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -430,6 +432,29 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   return record(events, 3, stream);
 }
 
+// Static scratch of gdn_forward_noalloc: the forward's workspace for callers
+// that cannot allocate.  One copy per GPU, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address of each GPU's copy is taken once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch (nullptr on failure).
+void* device_scratch(int dev) {
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -449,6 +474,9 @@ const char* gdn_status_string(int status) {
              "or the token form's limits (N <= 64 bf16 / 32 fp32, no saved buffer)";
     case GDN_ERR_HIP: return "HIP kernel launch failed";
     case GDN_ERR_ALIASING: return "an output overlaps an input";
+    case GDN_ERR_SCRATCH_TOO_SMALL:
+      return "the problem needs more workspace than the static scratch of gdn_forward_noalloc "
+             "holds (GDN_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -531,6 +559,25 @@ gdn_status gdn_forward_events(const gdn_problem* p, const void* q, const void* k
     if (!events[i]) return GDN_ERR_NULL_POINTER;
   return forward_checked(p, q, k, v, gamma, beta, state_in, o, state_out, saved, workspace,
                          workspace_bytes, stream, events);
+}
+
+gdn_status gdn_forward_noalloc(const gdn_problem* p, const void* q, const void* k,
+                               const void* v, const float* gamma, const float* beta,
+                               const float* state_in, void* o, float* state_out, void* saved,
+                               void* stream) {
+  Shape s;
+  gdn_status st = check_problem(p, &s);
+  if (st != GDN_OK) return st;
+  const int64_t need = forward_ws(s);
+  if (need > (int64_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH_TOO_SMALL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+  void* ws = device_scratch(dev);
+  if (!ws) return GDN_ERR_HIP;
+  // nothing in the forward's workspace needs to start at zero: every
+  // intermediate is written before it is read within the call
+  return forward_checked(p, q, k, v, gamma, beta, state_in, o, state_out, saved, ws,
+                         (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 gdn_status gdn_step(const gdn_problem* p, const void* q, const void* k, const void* v,

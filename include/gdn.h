@@ -39,7 +39,8 @@
  *   - Tensor and workspace pointers must be 16-byte aligned; the gate
  *     pointers (gamma, beta, dgamma, dbeta) 4-byte aligned.  Outputs must
  *     not overlap inputs, except where an entry point says so.
- *   - Reentrant: no mutable global state.
+ *   - Reentrant: no mutable global state, except the static scratch that
+ *     gdn_forward_noalloc shares between its calls on one GPU.
  *   - Supported shapes: Dk == Dv == D with D a multiple of 16 and <= 128;
  *     B, H, T, N >= 1; B*H*T must fit in int32 and B*L*H be at most 2^40;
  *     one frame's token rows (N*H*D io elements) under 2 GiB, and N and
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -69,7 +70,9 @@ typedef enum {
                                         direct form outside its limits
                                         (gdn_algorithm)                       */
     GDN_ERR_HIP = 7,                 /* a kernel launch failed                */
-    GDN_ERR_ALIASING = 8             /* an output overlaps an input           */
+    GDN_ERR_ALIASING = 8,            /* an output overlaps an input           */
+    GDN_ERR_SCRATCH_TOO_SMALL = 9    /* gdn_forward_noalloc: the problem needs
+                                        more than GDN_NOALLOC_SCRATCH_BYTES  */
 } gdn_status;
 
 typedef enum { GDN_BF16 = 0, GDN_FP32 = 1 } gdn_dtype;
@@ -190,6 +193,34 @@ gdn_status gdn_forward_events(const gdn_problem* p,
                               void* o, float* state_out, void* saved,
                               void* workspace, size_t workspace_bytes, void* stream,
                               void* const* events);
+
+/* Bytes of the static scratch of gdn_forward_noalloc (192 MiB): enough for
+ * the forward's workspace at 20 heads x 112, 121 frames x 880 tokens in
+ * bf16, prologue flags included. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+/* gdn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * errors as gdn_forward, except that the workspace is the library's own
+ * static scratch on the current device (hipGetDevice; `stream` must belong
+ * to that device): one GDN_NOALLOC_SCRATCH_BYTES array per GPU, created with
+ * the library's device code and held until the process ends.  Its device
+ * address is looked up once per device, on the first call there.
+ *   - A problem whose gdn_workspace_size(p, GDN_OP_FORWARD) exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_SCRATCH_TOO_SMALL before any
+ *     GPU work.
+ *   - Nothing is allocated or freed (no hipMalloc, hipFree or allocating
+ *     library routine); nothing in the scratch needs to start at zero.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one GPU (other streams, other threads) race and corrupt each
+ *     other's results.  Serialise them, e.g. on one stream.
+ *   - GDN_ERR_HIP if the scratch's device address cannot be obtained. */
+gdn_status gdn_forward_noalloc(const gdn_problem* p,
+                               const void* q, const void* k, const void* v,
+                               const float* gamma, const float* beta,
+                               const float* state_in,
+                               void* o, float* state_out, void* saved, void* stream);
 
 /* Streaming step: advance the carried state by one latent frame
  * (p->T must be 1), as the chunk-by-chunk autoregressive variant does

@@ -22,8 +22,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = gb.header_functions()
     assert set(names) == {"gdn_abi_version", "gdn_status_string", "gdn_workspace_size",
-                          "gdn_saved_size", "gdn_forward", "gdn_forward_events", "gdn_step",
-                          "gdn_backward"}
+                          "gdn_saved_size", "gdn_forward", "gdn_forward_events",
+                          "gdn_forward_noalloc", "gdn_step", "gdn_backward"}
     for n in names:
         assert hasattr(lib, n), n
     # and the shared object's dynamic symbol table really carries them
@@ -33,8 +33,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3 == gb.ABI_VERSION
-    for code in range(9):
+    assert lib.gdn_abi_version() == 4 == gb.ABI_VERSION
+    for code in range(10):
         s = lib.gdn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.gdn_status_string(99).decode() == "unknown status"
@@ -272,3 +272,19 @@ def test_poisoned_buffers_are_nan(lib):
         assert bool((plan.ws == 255).all()) and bool((plan.saved == 255).all())
     finally:
         gb.POISON = old
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    # the static scratch holds the one-minute shape's forward workspace, with
+    # the prologue; one more frame of fp32 io does not fit, and the call
+    # returns before any GPU work
+    ok = gb.make_problem(1, 20, 121, 880, 112, "bf16", flags=3)
+    assert _ws(ok, gb.GDN_OP_FORWARD)[1] <= gb.NOALLOC_SCRATCH_BYTES
+    big = gb.make_problem(1, 20, 121, 880, 112, "fp32")
+    assert _ws(big, gb.GDN_OP_FORWARD)[1] > gb.NOALLOC_SCRATCH_BYTES
+    z = ctypes.c_void_p(16)
+    code = lib.gdn_forward_noalloc(ctypes.byref(big), z, z, z, z, z, None, z, None, None, None)
+    assert gb.STATUS[code] == "GDN_ERR_SCRATCH_TOO_SMALL"
+    bad = gb.make_problem(1, 20, 121, 880, 100, "bf16")
+    code = lib.gdn_forward_noalloc(ctypes.byref(bad), z, z, z, z, z, None, z, None, None, None)
+    assert gb.STATUS[code] == "GDN_ERR_UNSUPPORTED"
