@@ -668,7 +668,16 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   void* G = ws + 4 * s.mat;
   void* W = ws + 5 * s.mat;
 
-  // X_t = dO_t Q^_t^T, the frame's own contribution to dLoss/dS_t.
+  // X_t = dO_t Q^_t^T, the frame's own contribution to dLoss/dS_t, and
+  // dQ^_t = S_t^T dO_t: one pass over dO where it suits (bf16, enough
+  // frames), else a Gram-mode pass for X_t here and the transposed output
+  // pass for dQ below.
+  XdqArgs xa{};
+  xa.d_o = d_o; xa.q = q; xa.S = S; xa.X = ws + 3 * s.mat; xa.dq = dq;
+  xa.B = (int)s.B; xa.H = (int)s.H; xa.T = (int)s.T; xa.N = (int)s.N;
+  hipError_t xe = launch_xdq(xa, s.io, nt, stream_);
+  if (xe != hipSuccess && xe != hipErrorNotSupported) return GDN_ERR_HIP;
+  const bool fused_dq = xe == hipSuccess;
   GramArgs gx{};
   gx.x0 = d_o; gx.x1 = nullptr; gx.y = q; gx.w = nullptr; gx.out0 = X; gx.out1 = nullptr;
   gx.layout0 = LAYOUT_TILES; gx.layout1 = LAYOUT_TILES;
@@ -677,10 +686,12 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   gx.t0 = 0; gx.Tc = (int)s.T;
   gx.P = gram_splits(s);
   gx.part = reinterpret_cast<float*>(ws + 6 * s.mat);
-  st = hip_status(launch_gram(gx, s.io, nt, 1, stream_));
-  if (st != GDN_OK) return st;
-  if (gx.P > 1 && (st = hip_status(launch_gram_reduce(gx, s.io, nt, 1, stream_))) != GDN_OK)
-    return st;
+  if (!fused_dq) {
+    st = hip_status(launch_gram(gx, s.io, nt, 1, stream_));
+    if (st != GDN_OK) return st;
+    if (gx.P > 1 && (st = hip_status(launch_gram_reduce(gx, s.io, nt, 1, stream_))) != GDN_OK)
+      return st;
+  }
 
   // Reverse scan: G_t = X_t + G_{t+1} M_{t+1}^T, dS_0 = G_1 M_1^T.
   st = run_scan(s, A, X, gamma, d_state_out, G, d_state_in, true, ws + 6 * s.mat, stream_);
@@ -692,14 +703,16 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   st = hip_status(launch_dm(da, s.io, nt, stream_));
   if (st != GDN_OK) return st;
 
-  // dQ^_t = S_t^T dO_t: the output kernel on the transposed states.
-  OutArgs qa{};
-  qa.tok = d_o; qa.mat = S; qa.out = dq;
-  qa.B = (int)s.B; qa.H = (int)s.H; qa.T = (int)s.T; qa.N = (int)s.N;
-  qa.t0 = 0; qa.Tc = (int)s.T;
-  qa.P = out_splits(s);
-  st = hip_status(launch_output(qa, s.io, nt, true, stream_));
-  if (st != GDN_OK) return st;
+  if (!fused_dq) {
+    // dQ^_t = S_t^T dO_t: the output kernel on the transposed states.
+    OutArgs qa{};
+    qa.tok = d_o; qa.mat = S; qa.out = dq;
+    qa.B = (int)s.B; qa.H = (int)s.H; qa.T = (int)s.T; qa.N = (int)s.N;
+    qa.t0 = 0; qa.Tc = (int)s.T;
+    qa.P = out_splits(s);
+    st = hip_status(launch_output(qa, s.io, nt, true, stream_));
+    if (st != GDN_OK) return st;
+  }
 
   BwdTokArgs ba{};
   ba.k = k; ba.v = v; ba.beta = beta; ba.G = G; ba.W = W;

@@ -18,12 +18,7 @@
 // fp32: 16x16x4 fp32 MFMA), writes W_t and dgamma_t (a fixed-order block
 // sum).
 // dQ = S_t^T dO is the output kernel run on S_t^T (gdn_output.hip).
-// bwd_kv_kernel: one workgroup per frame, one wave per 16-feature tile.
-// Each wave keeps its rows of G_t, G_t^T and W_t as MFMA operands in
-// registers; K, V and beta are copied straight into a 3-stage LDS ring in
-// 32-token chunks, dK and dV rows are staged in LDS and stored one chunk
-// later as contiguous 16-byte pieces.  dbeta sums the per-feature-tile
-// partial dot products in a fixed order (deterministic, no atomics).
+// bwd_kv_kernel: dK, dV and dbeta by token chunks (described below).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -182,61 +177,98 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
   }
 }
 
-template <int IO, int NT>
-__global__ __launch_bounds__(64 * NT) void bwd_kv_kernel(BwdTokArgs a) {
+// bwd_kv_kernel: one workgroup per (b, t) frame and group of HPW adjacent
+// heads (pairs when H is even: a token's two head rows are one contiguous
+// 448-byte piece at D = 112, where single-head rows half-fill their first
+// or last 64-byte sector), one wave per (head, 16-feature tile).  Each wave
+// keeps its rows of G_t, G_t^T and W_t as MFMA operands in registers.
+// Token rows of K and V stream in chunks of CT tokens: each thread loads
+// its 16-byte pieces of a chunk into a register ring PF chunks deep,
+// commits them to a double-buffered LDS stage behind an LDS-only barrier
+// (the ring stays in flight across it), and every wave reads its head's
+// rows of the chunk as the other MFMA operand.  dK and dV are staged in
+// LDS and stored one chunk later as contiguous 16-byte pieces of token
+// rows; dbeta sums the per-feature-tile partial dot products in a fixed
+// order (deterministic, no atomics).
+// Registers bound the shape: at 14 waves per CU a wave has 128 VGPRs, of
+// which its three matrices take 48; chunks of 16 tokens (pairs) two deep
+// fit without spills (at D = 112 the whole backward went from 1.17 to
+// 0.99 ms against the single-head kernel with a ring of direct-to-LDS
+// copies; 32-token chunks or a third chunk in flight spilled and ran
+// slower).
+template <int IO, int NT, int HPW>
+__global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) {
   typedef typename Io<IO>::elem E;
   constexpr bool BF = (IO == IO_BF16);
   constexpr int D = 16 * NT;
   constexpr int ES = Io<IO>::bytes;
-  constexpr int CT = 32;                          // tokens per chunk
-  constexpr int MAT_BYTES = CT * D * ES;          // one chunk of K (or V) rows
-  constexpr int WL = MAT_BYTES / 1024;            // 1 KB copies per matrix (NT or 2 NT)
-  constexpr int OPS = WL / NT;                    // per wave per matrix
-  constexpr int STAGE_BYTES = 2 * MAT_BYTES + 256;   // K, V, beta
-  constexpr int STAGES = BF ? 3 : 2;              // fp32 rows are twice as large
-  constexpr int NTH = 64 * NT;
+  constexpr int RW = HPW * D;                    // elements of a token's row segment
+  constexpr int CT = BF ? 32 / HPW : 16;         // tokens per chunk (whole 16-token tiles)
+  constexpr int PR = RW * ES / 16;               // 16-byte pieces per row segment
+  constexpr int LDR = RW + (BF ? 8 : 4);         // padded LDS row (elements)
+  constexpr int NTH = 64 * NT * HPW;
+  constexpr int PPT = 2 * CT * PR / NTH;         // K and V pieces per thread per chunk
+  constexpr int PF = 2;                          // chunks in flight
   constexpr int KB = BF ? (D + 31) / 32 : D / 4;
-  static_assert(WL % NT == 0, "copies must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES][STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) E obuf[2][2][CT * D];   // dK, dV staging
-  __shared__ float red[2][NT][CT];                               // dbeta partials
+  constexpr int NB = CT * HPW;                   // gates per chunk
+  static_assert(PPT * NTH == 2 * CT * PR, "pieces must split evenly over the threads");
+  static_assert(CT % 16 == 0, "chunks of whole 16-token tiles");
+  static_assert(NB <= NTH, "one gate per thread at most");
+  // stage: K rows then V rows of a chunk (16 elements of padding: the zeroed
+  // tail of a last 32-column block stays inside the array)
+  constexpr int STAGE = 2 * CT * LDR + 16;
+  constexpr int OBUF = 2 * CT * LDR;             // dK rows, dV rows
+  // the stages and the output staging, one array: the prologue stages the
+  // heads' G_t across all of it
+  __shared__ __attribute__((aligned(16))) E lds[2 * STAGE + 2 * OBUF];
+  auto stage = [&](int i) { return lds + i * STAGE; };
+  auto obuf = [&](int i) { return lds + 2 * STAGE + i * OBUF; };
+  __shared__ float bstage[2][NB];
+  __shared__ float red[2][HPW][NT][CT];                               // dbeta partials
 
-  const int total = a.B * a.T * a.H;
+  const int HG = a.H / HPW;
+  const int total = a.B * a.T * HG;
   const int item = xcd_item(blockIdx.x, total);
-  const int h = item % a.H;
-  const int t = (item / a.H) % a.T;
-  const int b = item / (a.H * a.T);
+  const int h0 = (item % HG) * HPW;
+  const int t = (item / HG) % a.T;
+  const int b = item / (HG * a.T);
   const int N = a.N;
   const long row0 = (long)b * a.T * N + (long)t * N;
   const long DD = (long)D * D;
-  const long moff = (((long)b * a.H + h) * a.T + t) * DD;
   const int tid = threadIdx.x;
-  const int lane = lane_id(), ft = wave_id();
+  const int lane = lane_id(), wave = wave_id();
+  const int hp = wave / NT, ft = wave % NT;      // this wave's head (in the group), tile
   const int g = lane >> 4, li = lane & 15;
   const float s = a.s;
+  const int h = h0 + hp;
+  const long moff = (((long)b * a.H + h) * a.T + t) * DD;
 
   // Left operands of this wave's feature tile: rows of G_t, of G_t^T
-  // (columns of G_t, staged in LDS and read with the transposing read) and
-  // of W_t (symmetric).
+  // (columns of G_t: bf16 from G_t staged in LDS with the transposing read)
+  // and of W_t (symmetric).
   const E* Gt = static_cast<const E*>(a.G) + moff;
   const E* Wt = static_cast<const E*>(a.W) + moff;
   const int fr = ft * 16 + li;
   typedef typename std::conditional<BF, bf16x8, float>::type Frag;
   Frag mG[KB], mGT[KB], mW[KB];
   if constexpr (BF) {
-    uint16_t* ms = reinterpret_cast<uint16_t*>(&obuf[0][0][0]);   // [KB*32][D], 4 KB * NT * 2
-    static_assert(KB * 32 * D * 2 <= 2 * 2 * CT * D * 2, "staging fits");
+    // every head's G_t as [KB*32][D] rows (rows past D zero) in the stage
+    constexpr int KR = KB * 32;
+    static_assert(HPW * KR * D <= 2 * STAGE + 2 * OBUF, "staged matrices must fit the LDS");
+    uint16_t* ms = reinterpret_cast<uint16_t*>(lds);
     constexpr int PRW = D / 8;
-    for (int p = tid; p < KB * 32 * PRW; p += NTH) {
-      const int row = p / PRW, pc = p % PRW;
-      *reinterpret_cast<u32x4*>(ms + row * D + pc * 8) =
-          row < D ? *reinterpret_cast<const u32x4*>(Gt + row * D + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int p = tid; p < HPW * KR * PRW; p += NTH) {
+      const int m = p / (KR * PRW), r = p % (KR * PRW);
+      const int row = r / PRW, pc = r % PRW;
+      const E* Gm = static_cast<const E*>(a.G) + (((long)b * a.H + h0 + m) * a.T + t) * DD;
+      *reinterpret_cast<u32x4*>(ms + (m * KR + row) * D + pc * 8) =
+          row < D ? *reinterpret_cast<const u32x4*>(Gm + row * D + pc * 8) : u32x4{0u, 0u, 0u, 0u};
     }
     block_sync();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int k = kb * 32 + 8 * g;
-      mGT[kb] = lds_col_frag_bf16(ms, D, kb * 32, ft * 16);
+      mGT[kb] = lds_col_frag_bf16(ms + hp * KR * D, D, kb * 32, ft * 16);
       mG[kb] = (k < D) ? load_bf16x8(Gt + fr * D + k) : zero_bf16x8();
       mW[kb] = (k < D) ? load_bf16x8(Wt + fr * D + k) : zero_bf16x8();
     }
@@ -251,50 +283,51 @@ __global__ __launch_bounds__(64 * NT) void bwd_kv_kernel(BwdTokArgs a) {
     }
   }
 
-  // Copies of a chunk: K pieces (op i < WL), V pieces (WL <= i < 2 WL), 1 KB
-  // each, lane l's 16 bytes at + 16 l; wave 0 also copies the chunk's beta.
-  const char* ksrc = static_cast<const char*>(a.k);
-  const char* vsrc = static_cast<const char*>(a.v);
-  auto issue = [&](int c) {
-    const int c0 = c * CT;
-    char* st = ring[c % STAGES];
+  const int nchunks = (N + CT - 1) / CT;
+  // Addresses: a uniform 64-bit base of the frame's rows of the head group
+  // plus 32-bit per-lane offsets from 24-bit multiplies (the host keeps a
+  // frame's rows under 2 GiB and N, H D es under 2^24).
+  const long fbase = (row0 * a.H + h0) * (long)(D * ES);
+  const char* kframe = static_cast<const char*>(a.k) + fbase;
+  const char* vframe = static_cast<const char*>(a.v) + fbase;
+  char* dkframe = static_cast<char*>(a.dk) + fbase;
+  char* dvframe = static_cast<char*>(a.dv) + fbase;
+  const float* bframe = a.beta + row0 * a.H + h0;
+  float* dbframe = a.dbeta + row0 * a.H + h0;
+  const unsigned rowb = (unsigned)(a.H * D * ES);   // bytes between tokens
+  struct Ring {
+    u32x4 v[PPT];
+    float bt;
+  };
+  // Chunk c: piece p = tid + NTH j of [K rows | V rows] (row p / PR of
+  // matrix (p / (CT PR))), rows past the frame re-read its last row.
+  auto issue = [&](Ring& R, int c) {
+    const int c0 = (c < nchunks ? c : nchunks - 1) * CT;
 #pragma unroll
-    for (int j = 0; j < 2 * OPS; ++j) {
-      const int i = ft + NT * j;
-      const int m = i / WL, w = i % WL;
-      const int o = w * 1024 + lane * 16;
-      const int row = o / (D * ES), col = o % (D * ES);
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      const int m = p / (CT * PR), r = p % (CT * PR);
+      const int row = r / PR, pc = r % PR;
       int tk = c0 + row;
       if (tk >= N) tk = N - 1;
-      dma16((m ? vsrc : ksrc) + (((row0 + tk) * a.H + h) * (long)D) * ES + col,
-            st + m * MAT_BYTES + w * 1024);
+      const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(pc * 16);
+      R.v[j] = *reinterpret_cast<const u32x4*>((m ? vframe : kframe) + off);
     }
-    if (ft == 0) {
-      int tk = c0 + lane;
-      if (tk >= N) tk = N - 1;          // lanes past the chunk or the frame: unused
-      dma4(a.beta + (row0 + tk) * a.H + h, st + 2 * MAT_BYTES);
-    }
+    const int bi = tid < NB ? tid : 0;
+    int tk = c0 + bi / HPW;
+    if (tk >= N) tk = N - 1;
+    R.bt = bframe[__umul24((unsigned)tk, (unsigned)a.H) + (unsigned)(bi % HPW)];
   };
-  auto store_chunk = [&](int c) {
-    constexpr int PRW = D * ES / 16;
-    for (int p = tid; p < 2 * CT * PRW; p += NTH) {
-      const int m = p / (CT * PRW), r = p % (CT * PRW);
-      const int row = r / PRW, pc = r % PRW;
-      const int tk = c * CT + row;
-      if (tk < N)
-        *reinterpret_cast<u32x4*>(static_cast<E*>(m ? a.dv : a.dk) +
-                                  ((row0 + tk) * a.H + h) * (long)D + pc * (16 / ES)) =
-            *reinterpret_cast<const u32x4*>(&obuf[c & 1][m][row * D + pc * (16 / ES)]);
-    }
-    if (tid < CT) {
-      const int tk = c * CT + tid;
-      if (tk < N) {
-        float sum = 0.f;
+  auto commit = [&](const Ring& R, int c) {
+    E* st = stage(c & 1);
 #pragma unroll
-        for (int f = 0; f < NT; ++f) sum += red[c & 1][f][tid];
-        a.dbeta[(row0 + tk) * a.H + h] = sum;
-      }
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      const int m = p / (CT * PR), r = p % (CT * PR);
+      *reinterpret_cast<u32x4*>(st + (m * CT + r / PR) * LDR + (r % PR) * (16 / ES)) = R.v[j];
     }
+    // tokens past the frame's end get gate 0 (their rows are re-read copies)
+    if (tid < NB) bstage[c & 1][tid] = c * CT + tid / HPW < N ? R.bt : 0.f;
   };
   auto load4 = [&](const E* row) -> f32x4 {   // 4 values at this lane's features
     f32x4 r;
@@ -319,25 +352,14 @@ __global__ __launch_bounds__(64 * NT) void bwd_kv_kernel(BwdTokArgs a) {
       *reinterpret_cast<f32x4*>(dst) = v;
     }
   };
-
-  const int nchunks = (N + CT - 1) / CT;
-#pragma unroll
-  for (int c = 0; c < STAGES - 1; ++c)
-    if (c < nchunks) issue(c);
-  for (int c = 0; c < nchunks; ++c) {
-    // with 3 stages chunk c+1's copies (2 OPS per wave, at least) are
-    // younger than chunk c's; with 2 stages nothing younger is in flight
-    if (STAGES == 3 && c + 1 < nchunks)
-      wait_vm_barrier<2 * OPS>();
-    else
-      wait_vm_barrier<0>();
-    if (c + STAGES - 1 < nchunks) issue(c + STAGES - 1);
-    if (c > 0) store_chunk(c - 1);
-    const char* st = ring[c % STAGES];
-    const E* ks = reinterpret_cast<const E*>(st);
-    const E* vs = reinterpret_cast<const E*>(st + MAT_BYTES);
-    const float* bs = reinterpret_cast<const float*>(st + 2 * MAT_BYTES);
-#pragma unroll
+  auto compute = [&](int c) {
+    const E* ks = stage(c & 1) + hp * D;
+    const E* vs = stage(c & 1) + CT * LDR + hp * D;
+    const float* bs = bstage[c & 1];
+    E* ob = obuf(c & 1);
+    // one 16-token tile at a time (hoisting every tile's fragments would
+    // not fit the registers of 14 waves per CU)
+#pragma unroll 1
     for (int tt = 0; tt < CT / 16; ++tt) {
       const int trow = tt * 16 + li;
       f32x4 ay = zero4(), az = zero4(), aw = zero4();
@@ -345,26 +367,29 @@ __global__ __launch_bounds__(64 * NT) void bwd_kv_kernel(BwdTokArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
         if constexpr (BF) {
           const int k = kb * 32 + 8 * g;
+          // past D the read runs into the next head or the padding: zero it
           const bool ok = k < D;
-          const bf16x8 kf = ok ? load_bf16x8(reinterpret_cast<const uint16_t*>(ks + trow * D) + k)
+          const bf16x8 kf = ok ? load_bf16x8(reinterpret_cast<const uint16_t*>(ks + trow * LDR) + k)
                                : zero_bf16x8();
-          const bf16x8 vf = ok ? load_bf16x8(reinterpret_cast<const uint16_t*>(vs + trow * D) + k)
+          const bf16x8 vf = ok ? load_bf16x8(reinterpret_cast<const uint16_t*>(vs + trow * LDR) + k)
                                : zero_bf16x8();
           ay = mfma_bf16(mG[kb], kf, ay);
           az = mfma_bf16(mGT[kb], vf, az);
           aw = mfma_bf16(mW[kb], kf, aw);
+          // one block's fragments live at a time (registers)
+          __builtin_amdgcn_sched_barrier(0);
         } else {
           const int k = kb * 4 + g;
-          const float kf = reinterpret_cast<const float*>(ks)[trow * D + k];
-          const float vf = reinterpret_cast<const float*>(vs)[trow * D + k];
+          const float kf = ks[trow * LDR + k];
+          const float vf = vs[trow * LDR + k];
           ay = mfma_f32(mG[kb], kf, ay);
           az = mfma_f32(mGT[kb], vf, az);
           aw = mfma_f32(mW[kb], kf, aw);
         }
       }
-      const float bt = (c * CT + trow < N) ? bs[trow] : 0.f;
-      const f32x4 kv = load4(ks + trow * D);
-      const f32x4 vv = load4(vs + trow * D);
+      const float bt = bs[trow * HPW + hp];
+      const f32x4 kv = load4(ks + trow * LDR);
+      const f32x4 vv = load4(vs + trow * LDR);
       f32x4 dvv, dkv;
       float part = 0.f;
 #pragma unroll
@@ -377,13 +402,67 @@ __global__ __launch_bounds__(64 * NT) void bwd_kv_kernel(BwdTokArgs a) {
       }
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
-      if (g == 0) red[c & 1][ft][trow] = part;
-      put4(&obuf[c & 1][0][trow * D + ft * 16 + 4 * g], dkv);
-      put4(&obuf[c & 1][1][trow * D + ft * 16 + 4 * g], dvv);
+      if (g == 0) red[c & 1][hp][ft][trow] = part;
+      put4(ob + trow * LDR + hp * D + ft * 16 + 4 * g, dkv);
+      put4(ob + CT * LDR + trow * LDR + hp * D + ft * 16 + 4 * g, dvv);
+    }
+  };
+  // dK, dV pieces and dbeta of chunk c (staged by compute(c))
+  auto store = [&](int c, bool full) {
+    const E* src = obuf(c & 1);
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int p = tid + NTH * j;
+      const int m = p / (CT * PR), r = p % (CT * PR);
+      const int row = r / PR, pc = r % PR;
+      const int tk = c * CT + row;
+      const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(pc * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (m * CT + row) * LDR + pc * (16 / ES));
+      if (full || tk < N) *reinterpret_cast<u32x4*>((m ? dvframe : dkframe) + off) = v;
+    }
+    if (tid < NB) {
+      const int tk = c * CT + tid / HPW, m = tid % HPW;
+      float sum = 0.f;
+#pragma unroll
+      for (int f = 0; f < NT; ++f) sum += red[c & 1][m][f][tid / HPW];
+      if (full || tk < N) dbframe[__umul24((unsigned)tk, (unsigned)a.H) + (unsigned)m] = sum;
+    }
+  };
+
+  // chunks before the frame's last are whole; the last may be partial
+  const int nfull = (nchunks * CT <= N) ? nchunks : nchunks - 1;
+  Ring ring[PF];
+#pragma unroll
+  for (int r = 0; r < PF; ++r) issue(ring[r], r);
+  commit(ring[0], 0);
+  lds_barrier();
+  issue(ring[0], PF);
+  compute(0);
+  int c0 = 1;
+  for (; c0 + PF <= nfull; c0 += PF) {
+#pragma unroll
+    for (int r = 0; r < PF; ++r) {
+      const int c = c0 + r;
+      Ring& R = ring[(1 + r) % PF];
+      commit(R, c);
+      lds_barrier();
+      issue(R, c + PF);        // clamped past the end
+      store(c - 1, true);
+      compute(c);
     }
   }
-  block_sync();
-  store_chunk(nchunks - 1);
+#pragma unroll
+  for (int r = 0; r < PF; ++r) {
+    const int c = c0 + r;
+    if (c < nchunks) {
+      commit(ring[(1 + r) % PF], c);
+      lds_barrier();
+      store(c - 1, true);      // not the last chunk
+      compute(c);
+    }
+  }
+  lds_barrier();
+  store(nchunks - 1, nfull == nchunks);
 }
 
 template <int IO, int NT>
@@ -413,7 +492,12 @@ hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s) {
 
 template <int IO, int NT>
 static hipError_t launch_bwd_tok_nt(const BwdTokArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kv_kernel<IO, NT>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0, s, a);
+  // adjacent head pairs when H is even
+  if (a.H % 2 == 0)
+    hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 2>), dim3(a.B * a.T * (a.H / 2)), dim3(128 * NT), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 1>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,22 @@ struct OutArgs {
 };
 hipError_t launch_output(const OutArgs& a, int io, int nt, bool trans, hipStream_t s);
 
+// Backward, per (frame, head group), bf16: the two passes over dO in one,
+//   X_t = dO_t Q^_t^T   (D x D per head, MFMA tile layout, bf16)
+//   dQ^_t = S_t^T dO_t  (token rows, io dtype).
+struct XdqArgs {
+  const void* d_o;      // [B, L, H, D]
+  const void* q;        // [B, L, H, D]
+  const void* S;        // [B, H, T] x D x D row-major bf16: S_t
+  void* X;              // [B, H, T] x D x D tiles bf16
+  void* dq;             // [B, L, H, D]
+  int B, H, T, N;
+};
+// hipErrorNotSupported when the launch does not suit the fused pass (fp32,
+// or fewer than 256 (frame, head group) items): the caller then runs the
+// Gram-mode X pass and the transposed output pass instead.
+hipError_t launch_xdq(const XdqArgs& a, int io, int nt, hipStream_t s);
+
 // Backward, per frame: W_t = dM_t + dM_t^T with dM_t = S_{t-1}^T G_t, and
 // dgamma_t = tr(dM_t).
 struct DmArgs {
