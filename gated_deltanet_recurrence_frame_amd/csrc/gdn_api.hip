@@ -131,6 +131,18 @@ int64_t scratch_bytes(const Shape& s) {
   return a > b ? a : b;
 }
 
+}  // namespace
+
+// Bytes of one chunk's operator record of the token form (two CP x CP
+// token matrices in the io type, five fp32 vectors of CP).
+int64_t gdn::token_record_bytes(int io) {
+  const int cp = io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
+  const int es = io == IO_BF16 ? 2 : 4;
+  return (int64_t)2 * cp * cp * es + 5 * cp * 4;
+}
+
+namespace {
+
 // Token form: per-chunk operators of F = CP / N frames for every (b, h).
 int64_t token_frames(const Shape& s) {
   return (s.io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP) / s.N;

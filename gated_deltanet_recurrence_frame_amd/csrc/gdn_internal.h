@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_device.h"   // IoKind
+
 namespace gdn {
 
 // Per-frame D x D intermediates are stored in the "intermediate type": bf16

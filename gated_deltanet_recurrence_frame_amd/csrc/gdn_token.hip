@@ -582,12 +582,6 @@ __global__ __launch_bounds__(64 * NT) void token_scan_kernel(TokArgs a) {
   }
 }
 
-int64_t token_record_bytes(int io) {
-  const int cp = io == IO_BF16 ? TokCfg<IO_BF16>::CP : TokCfg<IO_F32>::CP;
-  const int es = io == IO_BF16 ? 2 : 4;
-  return (int64_t)2 * cp * cp * es + 5 * cp * 4;
-}
-
 template <int IO>
 static hipError_t launch_token_io(const TokArgs& a, int nt, bool prep, hipStream_t s) {
   const dim3 pgrid(a.B * a.H * a.nck), pblock(512);
