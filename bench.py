@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--extras", default="train,stream,windows,tokenwise,prologue",
+                    help="comma-separated extra legs to run")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -197,7 +199,7 @@ def main():
     B, H, D, T, N = (SHAPE[k] for k in ("B", "H", "D", "T", "N"))
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io="bf16", gamma="uniform", seed=0,
-                          with_do=not args.no_extras)
+                          with_do=True)
     d = {k: v.to(dev) for k, v in inp.items()}
     torch.cuda.synchronize()
 
@@ -259,15 +261,20 @@ def main():
                  "mfma_frac": round(fflops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
     extra = {}
-    if not args.no_extras:
+    legs = set() if args.no_extras else set(x for x in args.extras.split(",") if x)
+    if "train" in legs:
         print("[bench] forward+backward", file=sys.stderr, flush=True)
         extra["train"] = bench_train(gb, d, B, H, D, T, N, max(3, args.steps // 4))
+    if "stream" in legs:
         print("[bench] streaming steps", file=sys.stderr, flush=True)
         extra["stream"] = bench_stream(gb, d, B, H, D, T, N)
+    if "windows" in legs:
         print("[bench] streaming windows", file=sys.stderr, flush=True)
         extra["windows"] = [bench_windows(gb, d, B, H, D, T, N, k) for k in (2, 8, 15)]
+    if "tokenwise" in legs:
         print("[bench] token-wise GDN (token form)", file=sys.stderr, flush=True)
         extra["tokenwise"] = bench_tokenwise(gb, d, B, H, D, T * N)
+    if "prologue" in legs:
         print("[bench] block prologue", file=sys.stderr, flush=True)
         extra["prologue"] = bench_prologue(gb, d, B, H, D, T, N)
 

@@ -709,11 +709,15 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   st = run_scan(s, A, X, gamma, d_state_out, G, d_state_in, true, ws + 6 * s.mat, stream_);
   if (st != GDN_OK) return st;
 
-  DmArgs da{};
-  da.S = S; da.s0 = state_in; da.G = G; da.W = W; da.dgamma = dgamma;
-  da.B = (int)s.B; da.H = (int)s.H; da.T = (int)s.T;
-  st = hip_status(launch_dm(da, s.io, nt, stream_));
-  if (st != GDN_OK) return st;
+  // W_t = dM_t + dM_t^T and dgamma_t: a pass of their own for fp32; the
+  // bf16 dK/dV pass forms them from S and G itself
+  if (s.io != IO_BF16) {
+    DmArgs da{};
+    da.S = S; da.s0 = state_in; da.G = G; da.W = W; da.dgamma = dgamma;
+    da.B = (int)s.B; da.H = (int)s.H; da.T = (int)s.T;
+    st = hip_status(launch_dm(da, s.io, nt, stream_));
+    if (st != GDN_OK) return st;
+  }
 
   if (!fused_dq) {
     // dQ^_t = S_t^T dO_t: the output kernel on the transposed states.
@@ -730,6 +734,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   ba.k = k; ba.v = v; ba.beta = beta; ba.G = G; ba.W = W;
   ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
   ba.B = (int)s.B; ba.H = (int)s.H; ba.T = (int)s.T; ba.N = (int)s.N;
+  ba.S = S; ba.s0 = state_in; ba.dgamma = dgamma;
   st = hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
   if (st != GDN_OK) return st;
 

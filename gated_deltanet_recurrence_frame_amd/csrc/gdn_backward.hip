@@ -13,10 +13,9 @@
 //
 // Per-frame matrices are in the intermediate type (bf16 for bf16 io, fp32
 // for fp32 io).
-// dm_kernel: one workgroup per frame forms dM_t on MFMA from S_{t-1} and G_t
-// staged in LDS (bf16: both operands read with the transposing LDS read;
-// fp32: 16x16x4 fp32 MFMA), writes W_t and dgamma_t (a fixed-order block
-// sum).
+// dm_kernel (fp32 io): one workgroup per frame forms dM_t on MFMA from
+// S_{t-1} and G_t staged in LDS, writes W_t and dgamma_t (a fixed-order
+// block sum).  With bf16 io the dK/dV pass forms them itself (below).
 // dQ = S_t^T dO is the output kernel run on S_t^T (gdn_output.hip).
 // bwd_kv_kernel: dK, dV and dbeta by token chunks (described below).
 #include <type_traits>
@@ -218,9 +217,16 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   // tail of a last 32-column block stays inside the array)
   constexpr int STAGE = 2 * CT * LDR + 16;
   constexpr int OBUF = 2 * CT * LDR;             // dK rows, dV rows
-  // the stages and the output staging, one array: the prologue stages the
-  // heads' G_t across all of it
-  __shared__ __attribute__((aligned(16))) E lds[2 * STAGE + 2 * OBUF];
+  constexpr int KR = KB * (BF ? 32 : 4);         // staged rows of a D x D matrix (zero past D)
+  constexpr int WLD = D + 8;                     // a wave's staged W rows
+  // bf16 prologue: the heads' G_t and S_{t-1} as [KR][D] rows, then every
+  // wave's 16 rows of W_t
+  constexpr int PRO = BF ? 2 * HPW * KR * D : HPW * KR * D;
+  static_assert(!BF || NT * HPW * 16 * WLD <= PRO, "W rows fit the prologue region");
+  constexpr int MAIN = 2 * STAGE + 2 * OBUF;
+  // the stages and the output staging, one array, shared with the prologue
+  __shared__ __attribute__((aligned(16))) E lds[MAIN > PRO ? MAIN : PRO];
+  __shared__ float gred[BF ? HPW : 1][NT * HPW];   // dgamma partials per wave
   auto stage = [&](int i) { return lds + i * STAGE; };
   auto obuf = [&](int i) { return lds + 2 * STAGE + i * OBUF; };
   __shared__ float bstage[2][NB];
@@ -247,33 +253,102 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   // (columns of G_t: bf16 from G_t staged in LDS with the transposing read)
   // and of W_t (symmetric).
   const E* Gt = static_cast<const E*>(a.G) + moff;
-  const E* Wt = static_cast<const E*>(a.W) + moff;
   const int fr = ft * 16 + li;
   typedef typename std::conditional<BF, bf16x8, float>::type Frag;
   Frag mG[KB], mGT[KB], mW[KB];
   if constexpr (BF) {
-    // every head's G_t as [KB*32][D] rows (rows past D zero) in the stage
-    constexpr int KR = KB * 32;
-    static_assert(HPW * KR * D <= 2 * STAGE + 2 * OBUF, "staged matrices must fit the LDS");
-    uint16_t* ms = reinterpret_cast<uint16_t*>(lds);
+    // The group's G_t and S_{t-1} (S_0 rounded like the saved states, or
+    // zero) as [KR][D] rows, rows past D zero, summing dgamma_t = <S_{t-1},
+    // G_t> on the way; then every wave forms its 16 rows of
+    //   W_t = S_{t-1}^T G_t + G_t^T S_{t-1}  (= dM_t + dM_t^T)
+    // on MFMA (columns of both staged matrices by the transposing read; the
+    // second product's left operand is the G_t^T fragments the wave keeps),
+    // stages them in LDS and reads them back as operand rows.
+    uint16_t* Gs = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* Ss = Gs + HPW * KR * D;
     constexpr int PRW = D / 8;
+    float dot[HPW];
+#pragma unroll
+    for (int m = 0; m < HPW; ++m) dot[m] = 0.f;
     for (int p = tid; p < HPW * KR * PRW; p += NTH) {
       const int m = p / (KR * PRW), r = p % (KR * PRW);
       const int row = r / PRW, pc = r % PRW;
-      const E* Gm = static_cast<const E*>(a.G) + (((long)b * a.H + h0 + m) * a.T + t) * DD;
-      *reinterpret_cast<u32x4*>(ms + (m * KR + row) * D + pc * 8) =
-          row < D ? *reinterpret_cast<const u32x4*>(Gm + row * D + pc * 8) : u32x4{0u, 0u, 0u, 0u};
+      const long bhm = (long)b * a.H + h0 + m;
+      u32x4 gv = {0u, 0u, 0u, 0u}, sv = {0u, 0u, 0u, 0u};
+      if (row < D) {
+        gv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.G) + (bhm * a.T + t) * DD +
+                                             row * D + pc * 8);
+        if (t > 0) {
+          sv = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.S) +
+                                               (bhm * a.T + t - 1) * DD + row * D + pc * 8);
+        } else if (a.s0) {
+          const float* s0 = a.s0 + bhm * DD + row * D + pc * 8;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(s0);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(s0 + 4);
+          float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          sv = __builtin_bit_cast(u32x4, f32x8_to_bf16x8(x));
+        }
+      }
+      const bf16x8 gb = __builtin_bit_cast(bf16x8, gv), sb = __builtin_bit_cast(bf16x8, sv);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d += static_cast<float>(sb[e]) * static_cast<float>(gb[e]);
+#pragma unroll
+      for (int mm = 0; mm < HPW; ++mm) dot[mm] += mm == m ? d : 0.f;
+      *reinterpret_cast<u32x4*>(Gs + (m * KR + row) * D + pc * 8) = gv;
+      *reinterpret_cast<u32x4*>(Ss + (m * KR + row) * D + pc * 8) = sv;
+    }
+    // dgamma partials: a fixed-order sum within each wave, then over the waves
+#pragma unroll
+    for (int m = 0; m < HPW; ++m) {
+      float v = dot[m];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) gred[m][wave] = v;
     }
     block_sync();
+    const uint16_t* Gh = Gs + hp * KR * D;
+    const uint16_t* Sh = Ss + hp * KR * D;
+    f32x4 wacc[NT];
+    {
+      bf16x8 sT[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k = kb * 32 + 8 * g;
+        mGT[kb] = lds_col_frag_bf16(Gh, D, kb * 32, ft * 16);
+        sT[kb] = lds_col_frag_bf16(Sh, D, kb * 32, ft * 16);
+        mG[kb] = (k < D) ? load_bf16x8(Gh + fr * D + k) : zero_bf16x8();
+      }
+#pragma unroll
+      for (int lt = 0; lt < NT; ++lt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          acc = mfma_bf16(sT[kb], lds_col_frag_bf16(Gh, D, kb * 32, lt * 16), acc);
+          acc = mfma_bf16(mGT[kb], lds_col_frag_bf16(Sh, D, kb * 32, lt * 16), acc);
+        }
+        wacc[lt] = acc;
+      }
+    }
+    if (tid < HPW) {
+      float sum = 0.f;
+      for (int w = 0; w < NT * HPW; ++w) sum += gred[tid][w];
+      a.dgamma[((long)b * a.T + t) * a.H + h0 + tid] = sum;
+    }
+    block_sync();   // every wave is done with the staged G_t, S_{t-1}
+    uint16_t* Wr = reinterpret_cast<uint16_t*>(lds) + wave * 16 * WLD;
+#pragma unroll
+    for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Wr[(4 * g + r) * WLD + lt * 16 + li] = f32_to_bf16_bits(wacc[lt][r]);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int k = kb * 32 + 8 * g;
-      mGT[kb] = lds_col_frag_bf16(ms + hp * KR * D, D, kb * 32, ft * 16);
-      mG[kb] = (k < D) ? load_bf16x8(Gt + fr * D + k) : zero_bf16x8();
-      mW[kb] = (k < D) ? load_bf16x8(Wt + fr * D + k) : zero_bf16x8();
+      mW[kb] = (k < D) ? load_bf16x8(Wr + li * WLD + k) : zero_bf16x8();
     }
-    block_sync();
+    block_sync();   // the LDS is the chunk loop's from here on
   } else {
+    const E* Wt = static_cast<const E*>(a.W) + moff;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int k = kb * 4 + g;
@@ -492,8 +567,9 @@ hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s) {
 
 template <int IO, int NT>
 static hipError_t launch_bwd_tok_nt(const BwdTokArgs& a, hipStream_t s) {
-  // adjacent head pairs when H is even
-  if (a.H % 2 == 0)
+  // adjacent head pairs when H is even (bf16: fp32's three D x D operand
+  // matrices would not fit the registers of 14 waves per CU)
+  if (IO == IO_BF16 && a.H % 2 == 0)
     hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 2>), dim3(a.B * a.T * (a.H / 2)), dim3(128 * NT), 0,
                        s, a);
   else

@@ -134,18 +134,23 @@ struct DmArgs {
 };
 hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s);
 
-// Backward, per frame, token pass: dK, dV, dbeta.
+// Backward, per frame, token pass: dK, dV, dbeta.  bf16: the pass also
+// forms W_t = dM_t + dM_t^T (dM_t = S_{t-1}^T G_t) and dgamma_t = tr(dM_t)
+// itself from S and G (no dm pass; W unused); fp32 reads W from dm_kernel.
 struct BwdTokArgs {
   const void* k;
   const void* v;
   const float* beta;    // [B, L, H]
   const void* G;        // row-major, intermediate type
-  const void* W;        // row-major, intermediate type
+  const void* W;        // row-major, intermediate type (fp32 io)
   void* dk;
   void* dv;
   float* dbeta;         // [B, L, H]
   float s;              // key scale
   int B, H, T, N;
+  const void* S;        // bf16: states after each frame, row-major
+  const float* s0;      // bf16: [B, H, D, D] fp32 initial state or nullptr (zero)
+  float* dgamma;        // bf16: [B, T, H]
 };
 hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
 

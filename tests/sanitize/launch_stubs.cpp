@@ -134,6 +134,9 @@ hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t) {
   need(a.dk, tok, "bwd dk");
   need(a.dv, tok, "bwd dv");
   need(a.dbeta, (int64_t)a.B * a.T * a.N * a.H * 4, "bwd dbeta");
+  need(a.S, mats, "bwd S");
+  need(a.s0, (int64_t)a.B * a.H * D * D * 4, "bwd s0");
+  need(a.dgamma, (int64_t)a.B * a.T * a.H * 4, "bwd dgamma");
   return hipSuccess;
 }
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t) {
