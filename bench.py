@@ -372,10 +372,23 @@ def bench_stream(gb, d, B, H, D, T, N):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     lat = sorted(evs[t].elapsed_time(evs[t + 1]) for t in range(T))
+    # the same chain with no event between the calls: GPU time per frame
+    state.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for f in frames:
+        plan(*f, state)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    chain = e0.elapsed_time(e1)
     return {"workload": "frame 0 then 120 gdn_step calls (state carried), 880 tokens each",
             "calls": T, "per_frame_ms_median": round(lat[T // 2], 4),
             "per_frame_ms_p90": round(lat[int(T * 0.9)], 4),
-            "tokens_per_s": round(B * T * N / wall, 1)}
+            "per_frame_ms_back_to_back": round(chain / T, 4),
+            "tokens_per_s": round(B * T * N / wall, 1),
+            "timing": "per-frame figures from an event after every call; back_to_back from "
+                      "two events around the whole chain"}
 
 
 def bench_tokenwise(gb, d, B, H, D, L):
