@@ -417,6 +417,11 @@ def bench_tokenwise(gb, d, B, H, D, L):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         out[name] = {"tokens": B * T, "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1)}
+        # algorithmic HBM bytes: q, k, v, o (bf16) and the two gates (fp32, one
+        # of each per token and head, the frames being single tokens)
+        nbytes = B * T * H * (4 * D * 2 + 4 + 4)
+        out[name]["algorithmic_bytes"] = nbytes
+        out[name]["hbm_frac"] = round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)
         del plan
     return out
 
