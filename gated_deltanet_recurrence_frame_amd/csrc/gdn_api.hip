@@ -123,12 +123,23 @@ int64_t partial_bytes(const Shape& s, int nr) {
 int64_t composite_bytes(const Shape& s) {
   return s.parts > 1 ? 3 * s.B * s.H * s.parts * s.D * s.D * 4 : 0;
 }
-// The token-split partials (used by the Gram launches) and the composites
-// (used by the scans) are never live at the same time on the stream, so
-// they share one region after the D x D buffers.
+// One-frame launches in direct form split the frame's tokens into parts
+// (when it has more than one part's worth) and keep every part's update of
+// the state in fp32.
+int64_t direct_parts(const Shape& s) {
+  if (!s.direct || s.T != 1) return 0;
+  const int64_t p = (s.N + kDirectPartTokens - 1) / kDirectPartTokens;
+  return p >= 2 ? p : 0;
+}
+int64_t direct_part_bytes(const Shape& s) { return direct_parts(s) * s.B * s.H * s.D * s.D * 4; }
+// The token-split partials (used by the Gram launches), the composites
+// (used by the scans) and the direct form's parts are never live at the
+// same time on the stream, so they share one region after the D x D
+// buffers.
 int64_t scratch_bytes(const Shape& s) {
-  const int64_t a = partial_bytes(s, 2), b = composite_bytes(s);
-  return a > b ? a : b;
+  const int64_t a = partial_bytes(s, 2), b = composite_bytes(s), c = direct_part_bytes(s);
+  const int64_t m = a > b ? a : b;
+  return m > c ? m : c;
 }
 
 }  // namespace
@@ -393,7 +404,14 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
     da.B = (int)s.B; da.H = (int)s.H; da.T = (int)s.T; da.N = (int)s.N;
     st = record(events, 1, stream);
     if (st != GDN_OK) return st;
-    st = hip_status(launch_direct(da, (int)(s.D / 16), stream));
+    if (direct_parts(s) >= 2) {
+      // one frame of many tokens: its tokens in parts, then their sum
+      da.part = reinterpret_cast<float*>(ws + 3 * s.mat);
+      da.P = (int)direct_parts(s);
+      st = hip_status(launch_direct_split(da, (int)(s.D / 16), stream));
+    } else {
+      st = hip_status(launch_direct(da, (int)(s.D / 16), stream));
+    }
     if (st != GDN_OK) return st;
     st = record(events, 2, stream);
     if (st != GDN_OK) return st;

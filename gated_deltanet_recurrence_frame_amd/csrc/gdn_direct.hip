@@ -260,6 +260,220 @@ __global__ __launch_bounds__(64 * NT) void direct_kernel(DirectArgs a) {
   }
 }
 
+// One frame with its tokens split over parts (streaming steps of many
+// tokens).  The update of a frame is a sum over its tokens, all of which
+// read S_0, so parts of kDirectPartTokens tokens are formed independently:
+// one workgroup per (head, row block, part) takes the products of
+// direct_kernel for its part (P = S_0 K^T, R = (s V^T - s^2 P) beta, dS_p =
+// R K) and stores dS_p in fp32; direct_combine_kernel then sums the parts in
+// a fixed order with the decay, S_1 = gamma S_0 + sum_p dS_p.  The
+// per-workgroup chain of one chunk after another becomes one chunk plus the
+// sum, and the launch fills the CUs (B H (D / 16) P workgroups).
+template <int NT>
+__global__ __launch_bounds__(64 * NT, 4) void direct_part_kernel(DirectArgs a) {
+  typedef uint16_t E;                            // bf16 bits
+  constexpr int D = 16 * NT;
+  constexpr int KB = (D + 31) / 32;              // MFMA k blocks over the features
+  constexpr int CK = kDirectPartTokens;          // tokens of a part
+  constexpr int TT = CK / 16;                    // 16-token tiles
+  constexpr int NW = NT;                         // waves
+  constexpr int NTH = 64 * NW;
+  constexpr int KPR = D * 2 / 16;                // 16-byte pieces per key row
+  constexpr int KPC = CK * KPR;                  // key pieces of a part
+  constexpr int KPT = (KPC + NTH - 1) / NTH;     // of them per thread
+  constexpr int VPC = CK * 2;                    // 16-byte value pieces (16 features a token)
+  constexpr int VPT = (VPC + NTH - 1) / NTH;
+  constexpr int BPT = (CK + NTH - 1) / NTH;      // gates per thread
+  constexpr int TPW = (TT + NW - 1) / NW;        // P tiles per wave
+  constexpr int ZLD = D + 8;                     // staged state row (elements)
+  constexpr int RLD = CK + 8;                    // staged R row (elements)
+  static_assert(CK % 32 == 0, "whole 32-token MFMA blocks");
+  static_assert(ZLD <= RLD, "the staged state rows fit the R buffer");
+  // (the staged rows of S_0 share R's buffer: they are read into registers
+  // before R is written, which keeps four workgroups per CU)
+  __shared__ __attribute__((aligned(16))) E Ks[CK * D];
+  __shared__ __attribute__((aligned(16))) E Rs[16 * RLD];
+  E* const Zs = Rs;
+  __shared__ __attribute__((aligned(16))) E Vs[CK * 16];          // values of the 16 rows
+  __shared__ float bs[CK];                                        // gates of the tokens
+
+  const int P = a.P;
+  const int total = a.B * a.H * NT * P;
+  const int item = xcd_item(blockIdx.x, total);  // a head's parts and row blocks share an XCD
+  const int pt = item % P;
+  const int rb = (item / P) % NT;
+  const int bh = item / (P * NT);
+  const int b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), w = wave_id();
+  const int g = lane >> 4, li = lane & 15;
+  const int N = a.N, H = a.H;
+  const float s = a.s, s2 = a.s * a.s;
+  const long DD = (long)D * D;
+  const E* kp = static_cast<const E*>(a.k);
+  const E* vp = static_cast<const E*>(a.v);
+  const int n0 = pt * CK;
+  // element (token n of frame 0, feature d): ((b T N + n) H + h) D + d
+  auto rowbase = [&](int n) { return (((long)b * a.T) * N + n) * H + h; };
+
+  // Every load in flight at once (clamped, never skipped: pieces past the
+  // part's count re-read one inside it and are not committed; tokens past
+  // the frame re-read its last row and get gate 0).
+  u32x4 kr[KPT], vr[VPT];
+  float br[BPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int q = min(tid + NTH * j, KPC - 1);
+    const int n = min(n0 + q / KPR, N - 1);
+    kr[j] = *reinterpret_cast<const u32x4*>(kp + rowbase(n) * D + (q % KPR) * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int vt = min(tid + NTH * j, VPC - 1);
+    const int n = min(n0 + vt / 2, N - 1);
+    vr[j] = *reinterpret_cast<const u32x4*>(vp + rowbase(n) * D + rb * 16 + 8 * (vt % 2));
+  }
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int c = min(tid + NTH * j, CK - 1);
+    br[j] = a.beta[rowbase(min(n0 + c, N - 1))];
+  }
+  // this lane's state: S_0[16 rb + 4 g + r][16 w + i]
+  f32x4 z = zero4();
+  if (a.z0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = a.z0[bh * DD + (rb * 16 + 4 * g + r) * D + w * 16 + li];
+  }
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Zs[(4 * g + r) * ZLD + w * 16 + li] = f32_to_bf16_bits(z[r]);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int q = tid + NTH * j;
+    if (q < KPC) *reinterpret_cast<u32x4*>(&Ks[(q / KPR) * D + (q % KPR) * 8]) = kr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int vt = tid + NTH * j;
+    if (vt < VPC) *reinterpret_cast<u32x4*>(&Vs[vt * 8]) = vr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int c = tid + NTH * j;
+    if (c < CK) bs[c] = n0 + c < N ? br[j] : 0.f;
+  }
+  block_sync();
+
+  // P = S_0[rows] K^T per 16-token tile, R = (s v - s^2 P) beta as [row][token]
+  bf16x8 sz[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int k = kb * 32 + 8 * g;
+    sz[kb] = k < D ? load_bf16x8(Zs + li * ZLD + k) : zero_bf16x8();
+  }
+  block_sync();   // every wave holds its rows of S_0 before R is written over them
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tt = w + NW * u;
+    if (tt < TT) {
+      f32x4 pr = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k = kb * 32 + 8 * g;
+        const bf16x8 kf = k < D ? load_bf16x8(&Ks[(tt * 16 + li) * D + k]) : zero_bf16x8();
+        pr = mfma_bf16(sz[kb], kf, pr);
+      }
+      const int tk = tt * 16 + li;
+      const float bt = bs[tk];
+      const u32x2 vv = *reinterpret_cast<const u32x2*>(&Vs[tk * 16 + 4 * g]);
+      const float v4[4] = {bf16_bits_to_f32((uint16_t)(vv[0] & 0xffff)),
+                           bf16_bits_to_f32((uint16_t)(vv[0] >> 16)),
+                           bf16_bits_to_f32((uint16_t)(vv[1] & 0xffff)),
+                           bf16_bits_to_f32((uint16_t)(vv[1] >> 16))};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Rs[(4 * g + r) * RLD + tk] = f32_to_bf16_bits((s * v4[r] - s2 * pr[r]) * bt);
+    }
+  }
+  block_sync();
+
+  // dS_p = R K on this wave's 16 features (keys by the transposing read)
+  f32x4 dS = zero4();
+#pragma unroll
+  for (int kk = 0; kk < CK / 32; ++kk) {
+    const bf16x8 rf = load_bf16x8(&Rs[li * RLD + kk * 32 + 8 * g]);
+    const bf16x8 kf = lds_col_frag_bf16(Ks, D, kk * 32, w * 16);
+    dS = mfma_bf16(rf, kf, dS);
+  }
+  *reinterpret_cast<f32x4*>(a.part + ((((long)bh * NT + rb) * P + pt) * NT + w) * 256 + lane * 4) =
+      dS;
+}
+
+// S_1 = gamma S_0 + sum_p dS_p (parts in order), one lane of a part's tile
+// layout per thread: fp32 to zT, bf16 to the emitted S_1.
+template <int NT>
+__global__ __launch_bounds__(256) void direct_combine_kernel(DirectArgs a) {
+  constexpr int D = 16 * NT;
+  const long DD = (long)D * D;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long)a.B * a.H * NT * NT * 64) return;
+  const int lane = (int)(e % 64);
+  const int w = (int)((e / 64) % NT);
+  const int rb = (int)((e / (64 * NT)) % NT);
+  const long bh = e / (64 * NT * NT);
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const int g = lane >> 4, li = lane & 15;
+  const int P = a.P;
+  const float* src = a.part + ((bh * NT + rb) * P * NT + w) * 256 + lane * 4;
+  // the parts in order, eight loads in flight at a time
+  f32x4 acc = zero4();
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const f32x4*>(src + (long)min(p0 + j, P - 1) * NT * 256);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j < P) acc += v[j];
+  }
+  const float gm = a.gamma[(long)b * a.T * a.H + h];
+  uint16_t* Sout = static_cast<uint16_t*>(a.emit) + bh * a.T * DD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const long idx = (rb * 16 + 4 * g + r) * D + w * 16 + li;
+    const float z = gm * (a.z0 ? a.z0[bh * DD + idx] : 0.f) + acc[r];
+    if (a.zT) a.zT[bh * DD + idx] = z;
+    Sout[idx] = f32_to_bf16_bits(z);
+  }
+}
+
+template <int NT>
+static hipError_t launch_direct_split_nt(const DirectArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((direct_part_kernel<NT>), dim3(a.B * a.H * NT * a.P), dim3(64 * NT), 0, s, a);
+  const long lanes = (long)a.B * a.H * NT * NT * 64;
+  hipLaunchKernelGGL((direct_combine_kernel<NT>), dim3((unsigned)((lanes + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_direct_split(const DirectArgs& a, int nt, hipStream_t s) {
+  // one frame, parts covering its tokens with none empty
+  if (a.T != 1 || a.N < 1 || a.P < 1 || !a.part || (long)a.P * kDirectPartTokens < a.N ||
+      (long)(a.P - 1) * kDirectPartTokens >= a.N)
+    return hipErrorInvalidValue;
+  switch (nt) {
+    case 1: return launch_direct_split_nt<1>(a, s);
+    case 2: return launch_direct_split_nt<2>(a, s);
+    case 3: return launch_direct_split_nt<3>(a, s);
+    case 4: return launch_direct_split_nt<4>(a, s);
+    case 5: return launch_direct_split_nt<5>(a, s);
+    case 6: return launch_direct_split_nt<6>(a, s);
+    case 7: return launch_direct_split_nt<7>(a, s);
+    case 8: return launch_direct_split_nt<8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int NT>
 static hipError_t launch_direct_nt(const DirectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((direct_kernel<NT>), dim3(a.B * a.H * NT), dim3(64 * NT), 0, s, a);

@@ -182,8 +182,15 @@ struct DirectArgs {
   float* zT;            // [B, H, D, D] fp32 final state or nullptr; may equal z0
   float s;              // key scale
   int B, H, T, N;
+  float* part;          // token-split launches: [B, H, D/16, P] x D/16 x 256 fp32 partials
+  int P;                // token parts (split launches)
 };
 hipError_t launch_direct(const DirectArgs& a, int nt, hipStream_t s);
+// One frame (T == 1) with its tokens split over a.P parts of kDirectPartTokens:
+// every (head, row block, part) forms its part's update in a.part, then a
+// fixed-order sum gives S_1 = gamma S_0 + sum of the parts (emit, zT).
+constexpr int kDirectPartTokens = 128;
+hipError_t launch_direct_split(const DirectArgs& a, int nt, hipStream_t s);
 
 // Token-space forward (frames with few tokens): one workgroup per (b, h),
 // chunks of F frames of N tokens, F N <= TokCfg<io>::CP.

@@ -176,6 +176,12 @@ hipError_t launch_direct(const DirectArgs& a, int nt, hipStream_t) {
   need(a.zT, (int64_t)a.B * a.H * D * D * 4, "direct zT");
   return hipSuccess;
 }
+hipError_t launch_direct_split(const DirectArgs& a, int nt, hipStream_t s) {
+  if (a.T != 1 || !a.part || a.P < 1) return hipErrorInvalidValue;
+  const int64_t D = 16 * nt;
+  need(a.part, (int64_t)a.B * a.H * a.P * D * D * 4, "direct parts");
+  return launch_direct(a, nt, s);   // the same inputs, state and emitted S_1
+}
 hipError_t launch_token(const TokArgs& a, int io, int nt, bool, hipStream_t) {
   ++g_calls;
   const int64_t D = 16 * nt, tok = (int64_t)a.B * a.T * a.N * a.H * D * es_of(io);

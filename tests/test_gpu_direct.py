@@ -65,6 +65,23 @@ def test_direct_matches_oracle(D, N):
     check(inp, N)
 
 
+@pytest.mark.parametrize("D", [16, 48, 112, 128])
+@pytest.mark.parametrize("N", [129, 256, 300, 1000])
+def test_direct_one_frame_token_parts(D, N):
+    # one frame of more than 128 tokens: the tokens in parts of 128 (the last
+    # ragged: 1, 0, 44 and 104 tokens past whole parts), then their ordered sum
+    inp = gin.make_inputs(B=2, H=3, T=1, N=N, D=D, io="bf16", gamma="sigmoid", seed=90 + D,
+                          with_state=True)
+    check(inp, N)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_direct_one_frame_parts_prologue_and_no_state(with_state):
+    inp = gin.make_inputs(B=1, H=4, T=1, N=520, D=64, io="bf16", seed=95,
+                          with_state=with_state, raw=True)
+    check(inp, 520, with_state=with_state, normalize_qk=True, gate_logits=True)
+
+
 @pytest.mark.parametrize("T", [1, 2, 8])
 def test_direct_layer_shape(T):
     # the layer's heads and frame size (20 x 112, 880 tokens)
