@@ -125,11 +125,16 @@ int64_t composite_bytes(const Shape& s) {
 }
 // One-frame launches in direct form split the frame's tokens into parts
 // (when it has more than one part's worth) and keep every part's update of
-// the state in fp32.
+// the state in fp32.  At most kMaxDirectParts parts (frames of up to 4096
+// tokens): the parts' workspace grows with the frame, and longer frames walk
+// their chunks in one workgroup as for several frames.  The parts' grid
+// stays within int32.
+constexpr int64_t kMaxDirectParts = 32;
 int64_t direct_parts(const Shape& s) {
   if (!s.direct || s.T != 1) return 0;
   const int64_t p = (s.N + kDirectPartTokens - 1) / kDirectPartTokens;
-  return p >= 2 ? p : 0;
+  if (p < 2 || p > kMaxDirectParts || s.B * s.H * (s.D / 16) * p > INT32_MAX) return 0;
+  return p;
 }
 int64_t direct_part_bytes(const Shape& s) { return direct_parts(s) * s.B * s.H * s.D * s.D * 4; }
 // The token-split partials (used by the Gram launches), the composites

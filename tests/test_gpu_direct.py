@@ -75,6 +75,14 @@ def test_direct_one_frame_token_parts(D, N):
     check(inp, N)
 
 
+def test_direct_one_frame_beyond_the_parts_cap():
+    # more than 32 parts' worth of tokens (4200): the frame's chunks are
+    # walked in one workgroup per row block instead
+    inp = gin.make_inputs(B=1, H=2, T=1, N=4200, D=48, io="bf16", gamma="sigmoid", seed=97,
+                          with_state=True)
+    check(inp, 4200)
+
+
 @pytest.mark.parametrize("with_state", [False, True])
 def test_direct_one_frame_parts_prologue_and_no_state(with_state):
     inp = gin.make_inputs(B=1, H=4, T=1, N=520, D=64, io="bf16", seed=95,
