@@ -97,7 +97,11 @@ typedef enum { GDN_OP_FORWARD = 0, GDN_OP_STEP = 1, GDN_OP_BACKWARD = 2 } gdn_op
  *                   s^2 S_{t-1} k_n) k_n^T straight from the token rows
  *                   (no A_t, U_t), then O_t = S_t Q^_t for all frames.
  *                   For launches of few frames (streaming steps, short
- *                   windows).  bf16 only; requires saved == NULL.
+ *                   windows).  A launch of one frame of 129 to 4096 tokens
+ *                   splits the frame's tokens into parts of 128, each
+ *                   part's update kept in fp32 in the workspace (B H D^2 4
+ *                   bytes a part) and summed in a fixed order.  bf16 only;
+ *                   requires saved == NULL.
  *   GDN_ALGO_AUTO   the direct form for bf16 launches of at most 2 frames
  *                   (the frame form when a saved buffer is passed), else
  *                   the frame form.
