@@ -187,7 +187,7 @@ def main():
                     help="comma-separated extra legs to run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: libgdn runs on one GPU per process "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
