@@ -1,10 +1,10 @@
 // Host-only stand-ins for libgdn's kernel launchers, for the sanitizer build
 // of the C ABI's host code (gdn_api.hip): nothing is launched.  Every
 // launcher records its call and checks that each device pointer it receives
-// lies inside one of the regions the driver handed to the entry point (the
+// lies inside one of the regions api_driver.cpp handed to the entry point (the
 // caller's tensors and workspace), together with the extent the launch would
 // touch where that follows from its arguments.  Violations are counted and
-// reported by the driver.
+// reported by api_driver.cpp.
 #include <stdint.h>
 #include <stdio.h>
 
