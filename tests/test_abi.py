@@ -58,6 +58,15 @@ def test_workspace_sizes(lib):
     # a streaming step splits each frame's tokens over 8 workgroups and
     # keeps their fp32 partial A_t, U_t in the workspace
     assert _ws(p1, gb.GDN_OP_STEP) == (0, 3 * B * H * D * D * 2 + 8 * B * H * 2 * D * D * 4)
+    # the direct form of one frame splits its tokens into parts of 128 (at most
+    # 32) and keeps each part's fp32 update of the state: beyond the Gram's
+    # partials from 4096 tokens; past 32 parts the frame is not split
+    base = 3 * B * H * D * D * 2
+    gram_parts = 8 * B * H * 2 * D * D * 4
+    p4096 = gb.make_problem(B, H, 1, 4096, D, "bf16")
+    assert _ws(p4096, gb.GDN_OP_STEP) == (0, base + 32 * B * H * D * D * 4)
+    p4097 = gb.make_problem(B, H, 1, 4097, D, "bf16")
+    assert _ws(p4097, gb.GDN_OP_STEP) == (0, base + gram_parts)
     assert gb.saved_size(p) == 2 * mat
     # a chunked scan (8-frame chunks: 16 chunks) keeps -C_w^T, H_w and the
     # entering state of every chunk in fp32
