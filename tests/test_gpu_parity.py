@@ -623,6 +623,27 @@ def test_train_minute_config_all_heads():
     check_grads(gr, ref, N, "bf16")
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_minute_config_other_seeds(seed):
+    # the one-minute configuration repeated at seeds 1 and 2: forward (o,
+    # state) and backward (every gradient), all 20 heads, per-block bars
+    inp = gin.make_config("minute", seed=seed, with_do=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    N = 880
+    plan = gb.ForwardPlan(1, 20, 121, N, 112, "bf16", torch.device(DEV), saved=True)
+    o, st = plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                     saved=plan.saved)
+    torch.cuda.synchronize()
+    f = {k: f64(inp[k]) for k in ("q", "k", "v", "gamma", "beta", "d_o")}
+    ro, rs = oracle.forward(f["q"], f["k"], f["v"], f["gamma"], f["beta"], N)
+    print("minute seed %d, 20 heads:" % seed)
+    check_blocks("o", f64(o.cpu()), ro, N, TOL["bf16"])
+    check_blocks("state", f64(st.cpu()), rs, N, TOL["bf16"])
+    ref = oracle.backward(f["q"], f["k"], f["v"], f["gamma"], f["beta"], N, f["d_o"])
+    check_grads(gr, ref, N, "bf16")
+
+
 def _frag_to_rowmajor(a, D):
     """Undo the bf16 operand order of saved A_t (documented in include/gdn.h):
     element [r][c] of a frame sits at (r / 16) 16 D + (c / 32) 512 +
