@@ -188,9 +188,11 @@ int64_t token_ws(const Shape& s) {
 // backward), q / |q| and k / |k| as [B, L, H, D] io dtype.
 int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
 struct Prologue {
-  int64_t gamma, beta, q, k, end;   // offsets from the region's start; end = bytes
+  int64_t gamma, beta, q, k, iq, ik, end;   // offsets from the region's start; end = bytes
 };
-Prologue prologue_layout(const Shape& s, bool copies) {
+// `inv`: 1 / |q| and 1 / |k| per row beside the copies (the backward's
+// fused chain rule, bf16)
+Prologue prologue_layout(const Shape& s, bool copies, bool inv = false) {
   Prologue r{};
   int64_t o = 0;
   if (s.gates) {
@@ -201,6 +203,11 @@ Prologue prologue_layout(const Shape& s, bool copies) {
     const int64_t tok = round256(s.B * s.L * s.H * s.D * s.es);
     r.q = o; o += tok;
     r.k = o; o += tok;
+    if (inv) {
+      const int64_t rows = round256(s.B * s.L * s.H * 4);
+      r.iq = o; o += rows;
+      r.ik = o; o += rows;
+    }
   }
   r.end = o;
   return r;
@@ -217,8 +224,12 @@ int64_t forward_ws(const Shape& s) {
   const int64_t pro = prologue_layout(s, forward_copies(s)).end;
   return pro ? forward_base(s) + pro : (s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
 }
+// The backward takes dq and dk through the normalisation's chain rule
+// inside its token passes for bf16 (the inverse norms then sit beside the
+// normalised copies), in passes of their own for fp32.
+bool backward_inv(const Shape& s) { return s.norm && s.io == IO_BF16; }
 int64_t backward_ws(const Shape& s) {
-  const int64_t pro = prologue_layout(s, true).end;
+  const int64_t pro = prologue_layout(s, true, backward_inv(s)).end;
   return pro ? backward_base(s) + pro : 6 * s.mat + scratch_bytes(s);
 }
 
@@ -230,6 +241,8 @@ struct Inputs {
   const void* k;
   const float* gamma;
   const float* beta;
+  const float* inv_q;   // 1 / |q| per row, or nullptr
+  const float* inv_k;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -258,9 +271,9 @@ gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_
 
 gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* k,
                         const float* gamma, const float* beta, char* region, Inputs* in,
-                        hipStream_t stream) {
-  const Prologue pl = prologue_layout(s, copies);
-  *in = Inputs{q, k, gamma, beta};
+                        hipStream_t stream, bool inv = false) {
+  const Prologue pl = prologue_layout(s, copies, inv);
+  *in = Inputs{q, k, gamma, beta, nullptr, nullptr};
   hipError_t e = hipSuccess;
   if (s.gates) {
     float* g = reinterpret_cast<float*>(region + pl.gamma);
@@ -273,11 +286,15 @@ gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* 
   if (e == hipSuccess && s.norm && copies) {
     void* qn = region + pl.q;
     void* kn = region + pl.k;
+    float* iq = inv ? reinterpret_cast<float*>(region + pl.iq) : nullptr;
+    float* ik = inv ? reinterpret_cast<float*>(region + pl.ik) : nullptr;
     const int64_t rows = s.B * s.L * s.H;
-    e = launch_rows_normalize(q, qn, rows, (int)s.D, s.io, stream);
-    if (e == hipSuccess) e = launch_rows_normalize(k, kn, rows, (int)s.D, s.io, stream);
+    e = launch_rows_normalize(q, qn, iq, rows, (int)s.D, s.io, stream);
+    if (e == hipSuccess) e = launch_rows_normalize(k, kn, ik, rows, (int)s.D, s.io, stream);
     in->q = qn;
     in->k = kn;
+    in->inv_q = iq;
+    in->inv_k = ik;
   }
   return hip_status(e);
 }
@@ -668,7 +685,8 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   const float* gamma_raw = gamma;
   const float* beta_raw = beta;
   Inputs in;
-  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_);
+  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_,
+                    backward_inv(s));
   if (st != GDN_OK) return st;
   q = in.q; k = in.k; gamma = in.gamma; beta = in.beta;
   const void* A;
@@ -710,6 +728,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   XdqArgs xa{};
   xa.d_o = d_o; xa.q = q; xa.S = S; xa.X = ws + 3 * s.mat; xa.dq = dq;
   xa.B = (int)s.B; xa.H = (int)s.H; xa.T = (int)s.T; xa.N = (int)s.N;
+  xa.inv = in.inv_q;   // with normalised queries: dq of the raw rows
   hipError_t xe = launch_xdq(xa, s.io, nt, stream_);
   if (xe != hipSuccess && xe != hipErrorNotSupported) return GDN_ERR_HIP;
   const bool fused_dq = xe == hipSuccess;
@@ -758,15 +777,18 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
   ba.B = (int)s.B; ba.H = (int)s.H; ba.T = (int)s.T; ba.N = (int)s.N;
   ba.S = S; ba.s0 = state_in; ba.dgamma = dgamma;
+  ba.inv = in.inv_k;   // with normalised keys: dk of the raw rows
   st = hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
   if (st != GDN_OK) return st;
 
-  // Chain rule through the prologue.
+  // Chain rule through the prologue (what the token passes did not take).
   hipError_t e = hipSuccess;
   if (s.norm) {
     const int64_t rows = s.B * s.L * s.H;
-    e = launch_rows_normalize_bwd(q_raw, dq, rows, (int)s.D, s.io, stream_);
-    if (e == hipSuccess) e = launch_rows_normalize_bwd(k_raw, dk, rows, (int)s.D, s.io, stream_);
+    if (!(fused_dq && in.inv_q))
+      e = launch_rows_normalize_bwd(q_raw, dq, rows, (int)s.D, s.io, stream_);
+    if (e == hipSuccess && !in.inv_k)
+      e = launch_rows_normalize_bwd(k_raw, dk, rows, (int)s.D, s.io, stream_);
   }
   if (e == hipSuccess && s.gates) {
     e = launch_sigmoid_bwd(gamma_raw, dgamma, s.B * s.T * s.H, stream_);

@@ -189,13 +189,17 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
 // LDS and stored one chunk later as contiguous 16-byte pieces of token
 // rows; dbeta sums the per-feature-tile partial dot products in a fixed
 // order (deterministic, no atomics).
+// With normalised keys (CHAIN, bf16: k holds k^ = k / |k| and inv 1 / |k|)
+// dK^ goes through the normalisation's chain rule before it is stored, as
+// in the query pass: dk = (dk^ - k^ (k^ . dk^)) / |k|, the dot summed over
+// the feature tiles in a fixed order.
 // Registers bound the shape: at 14 waves per CU a wave has 128 VGPRs, of
 // which its three matrices take 48; chunks of 16 tokens (pairs) two deep
 // fit without spills (at D = 112 the whole backward went from 1.17 to
 // 0.99 ms against the single-head kernel with a ring of direct-to-LDS
 // copies; 32-token chunks or a third chunk in flight spilled and ran
 // slower).
-template <int IO, int NT, int HPW>
+template <int IO, int NT, int HPW, bool CHAIN>
 __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) {
   typedef typename Io<IO>::elem E;
   constexpr bool BF = (IO == IO_BF16);
@@ -231,6 +235,9 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   auto obuf = [&](int i) { return lds + 2 * STAGE + i * OBUF; };
   __shared__ float bstage[2][NB];
   __shared__ float red[2][HPW][NT][CT];                               // dbeta partials
+  static_assert(!CHAIN || BF, "the fused chain rule is for bf16");
+  __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];                  // k^ . dk^ partials
+  __shared__ float istage[CHAIN ? 2 : 1][NB];                         // 1 / |k|
 
   const int HG = a.H / HPW;
   const int total = a.B * a.T * HG;
@@ -373,6 +380,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   struct Ring {
     u32x4 v[PPT];
     float bt;
+    float iv;   // CHAIN: 1 / |k| of the same (token, head) as bt
   };
   // Chunk c: piece p = tid + NTH j of [K rows | V rows] (row p / PR of
   // matrix (p / (CT PR))), rows past the frame re-read its last row.
@@ -392,6 +400,8 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     int tk = c0 + bi / HPW;
     if (tk >= N) tk = N - 1;
     R.bt = bframe[__umul24((unsigned)tk, (unsigned)a.H) + (unsigned)(bi % HPW)];
+    if constexpr (CHAIN)
+      R.iv = a.inv[row0 * a.H + h0 + __umul24((unsigned)tk, (unsigned)a.H) + (unsigned)(bi % HPW)];
   };
   auto commit = [&](const Ring& R, int c) {
     E* st = stage(c & 1);
@@ -403,6 +413,9 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     }
     // tokens past the frame's end get gate 0 (their rows are re-read copies)
     if (tid < NB) bstage[c & 1][tid] = c * CT + tid / HPW < N ? R.bt : 0.f;
+    if constexpr (CHAIN) {
+      if (tid < NB) istage[c & 1][tid] = R.iv;
+    }
   };
   auto load4 = [&](const E* row) -> f32x4 {   // 4 values at this lane's features
     f32x4 r;
@@ -478,6 +491,12 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       if (g == 0) red[c & 1][hp][ft][trow] = part;
+      if constexpr (CHAIN) {
+        float cp = kv[0] * dkv[0] + kv[1] * dkv[1] + kv[2] * dkv[2] + kv[3] * dkv[3];
+        cp += __shfl_xor(cp, 16);
+        cp += __shfl_xor(cp, 32);
+        if (g == 0) cred[c & 1][hp][ft][trow] = cp;
+      }
       put4(ob + trow * LDR + hp * D + ft * 16 + 4 * g, dkv);
       put4(ob + CT * LDR + trow * LDR + hp * D + ft * 16 + 4 * g, dvv);
     }
@@ -492,7 +511,25 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
       const int row = r / PR, pc = r % PR;
       const int tk = c * CT + row;
       const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(pc * 16);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (m * CT + row) * LDR + pc * (16 / ES));
+      u32x4 v = *reinterpret_cast<const u32x4*>(src + (m * CT + row) * LDR + pc * (16 / ES));
+      if constexpr (CHAIN) {
+        if (m == 0) {
+          // dk = (dk^ - k^ (k^ . dk^)) / |k| on this piece of head hm's row
+          const int hm = pc / (D / 8);
+          float dot = 0.f;
+#pragma unroll
+          for (int f = 0; f < NT; ++f) dot += cred[c & 1][hm][f][row];
+          const float iv = istage[c & 1][row * HPW + hm];
+          const u32x4 kx = *reinterpret_cast<const u32x4*>(stage(c & 1) + row * LDR + pc * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g0 = __uint_as_float(v[e] << 16), g1 = __uint_as_float(v[e] & 0xffff0000u);
+            const float k0 = __uint_as_float(kx[e] << 16), k1 = __uint_as_float(kx[e] & 0xffff0000u);
+            v[e] = (uint32_t)f32_to_bf16_bits((g0 - k0 * dot) * iv) |
+                   ((uint32_t)f32_to_bf16_bits((g1 - k1 * dot) * iv) << 16);
+          }
+        }
+      }
       if (full || tk < N) *reinterpret_cast<u32x4*>((m ? dvframe : dkframe) + off) = v;
     }
     if (tid < NB) {
@@ -565,15 +602,28 @@ hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t s) {
   return io == IO_BF16 ? launch_dm_io<IO_BF16>(a, nt, s) : launch_dm_io<IO_F32>(a, nt, s);
 }
 
-template <int IO, int NT>
-static hipError_t launch_bwd_tok_nt(const BwdTokArgs& a, hipStream_t s) {
+template <int IO, int NT, bool CHAIN>
+static void launch_bwd_tok_chain(const BwdTokArgs& a, hipStream_t s) {
   // adjacent head pairs when H is even (bf16: fp32's three D x D operand
   // matrices would not fit the registers of 14 waves per CU)
   if (IO == IO_BF16 && a.H % 2 == 0)
-    hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 2>), dim3(a.B * a.T * (a.H / 2)), dim3(128 * NT), 0,
-                       s, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 2, CHAIN>), dim3(a.B * a.T * (a.H / 2)),
+                       dim3(128 * NT), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 1>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<IO, NT, 1, CHAIN>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0,
+                       s, a);
+}
+template <int IO, int NT>
+static hipError_t launch_bwd_tok_nt(const BwdTokArgs& a, hipStream_t s) {
+  if constexpr (IO == IO_BF16) {
+    if (a.inv) {
+      launch_bwd_tok_chain<IO, NT, true>(a, s);
+      return hipGetLastError();
+    }
+  } else {
+    if (a.inv) return hipErrorInvalidValue;   // the fused chain rule is bf16 only
+  }
+  launch_bwd_tok_chain<IO, NT, false>(a, s);
   return hipGetLastError();
 }
 

@@ -22,6 +22,13 @@
 //       token rows.
 // dO rows past the frame's end are zeroed when staged, so they add nothing
 // to X (their dQ rows are not stored).
+//
+// With normalised queries (CHAIN: q holds q^ = q / |q| and inv 1 / |q|) the
+// pass also takes dQ^ through the normalisation's chain rule before storing
+// it: dq = (dq^ - q^ (q^ . dq^)) / |q| (summary page, 方法步骤详情 module 2,
+// the hats read as per-token normalisation).  Each wave adds q^ . dq^ over
+// its 16 features of a token; the stores sum the tiles' partials in a fixed
+// order (deterministic) and apply the rule to whole 16-byte pieces.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -37,7 +44,7 @@ constexpr int xdq_pad(int rw) {
   return rw;
 }
 
-template <int NT, int HPW>
+template <int NT, int HPW, bool CHAIN>
 __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
   constexpr int D = 16 * NT;
   constexpr int RW = HPW * D;               // elements of a token's row segment
@@ -55,6 +62,9 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
   static_assert(HPW * KR * D <= 2 * STAGE, "S_t of the group must fit the stage");
   __shared__ __attribute__((aligned(16))) uint16_t stage[2][STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t obuf[2][CT * LDO];
+  // CHAIN: q^ . dq^ per (head, tile, token), 1 / |q| per (token, head)
+  __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];
+  __shared__ float istage[CHAIN ? 2 : 1][CT * HPW];
 
   const int HG = a.H / HPW;
   const int total = a.B * a.T * HG;
@@ -102,6 +112,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
 
   struct Ring {
     u32x4 o, q;
+    float iv;   // CHAIN: 1 / |q| of token tid / HPW, head tid % HPW
   };
   auto issue = [&](Ring& R, int c) {
     int tk = (c < nchunks ? c : nchunks - 1) * CT + prow;
@@ -109,12 +120,21 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
     const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(ppc * 16);
     R.o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dob + off));
     R.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qb + off));
+    if constexpr (CHAIN) {
+      const int bi = tid < CT * HPW ? tid : 0;
+      int ti = (c < nchunks ? c : nchunks - 1) * CT + bi / HPW;
+      if (ti >= N) ti = N - 1;
+      R.iv = a.inv[(row0 + ti) * a.H + h0 + bi % HPW];
+    }
   };
   auto commit = [&](const Ring& R, int c) {
     uint16_t* st = stage[c & 1];
     const bool live = c * CT + prow < N;        // rows past the frame: dO zero
     *reinterpret_cast<u32x4*>(st + prow * LDR + ppc * 8) = live ? R.o : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(st + (CT + prow) * LDR + ppc * 8) = R.q;
+    if constexpr (CHAIN) {
+      if (tid < CT * HPW) istage[c & 1][tid] = R.iv;
+    }
   };
 
   f32x4 acc[NT];
@@ -150,11 +170,39 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
       pk[0] = (uint32_t)f32_to_bf16_bits(d[0]) | ((uint32_t)f32_to_bf16_bits(d[1]) << 16);
       pk[1] = (uint32_t)f32_to_bf16_bits(d[2]) | ((uint32_t)f32_to_bf16_bits(d[3]) << 16);
       *reinterpret_cast<u32x2*>(ob + trow * LDO + hp * D + ft * 16 + 4 * g) = pk;
+      if constexpr (CHAIN) {
+        // q^ . dq^ over this wave's 16 features of the token (lanes li,
+        // li + 16, li + 32, li + 48 hold 4 each)
+        const u32x2 qp = *reinterpret_cast<const u32x2*>(qs + trow * LDR + ft * 16 + 4 * g);
+        float part = bf16_bits_to_f32((uint16_t)(qp[0] & 0xffff)) * d[0];
+        part += bf16_bits_to_f32((uint16_t)(qp[0] >> 16)) * d[1];
+        part += bf16_bits_to_f32((uint16_t)(qp[1] & 0xffff)) * d[2];
+        part += bf16_bits_to_f32((uint16_t)(qp[1] >> 16)) * d[3];
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (g == 0) cred[c & 1][hp][ft][trow] = part;
+      }
     }
   };
   auto store = [&](int c, bool full) {
     const int tk = c * CT + prow;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(&obuf[c & 1][prow * LDO + ppc * 8]);
+    u32x4 v = *reinterpret_cast<const u32x4*>(&obuf[c & 1][prow * LDO + ppc * 8]);
+    if constexpr (CHAIN) {
+      // dq = (dq^ - q^ (q^ . dq^)) / |q| on this piece of head hm's row
+      const int hm = ppc / (D / 8);
+      float dot = 0.f;
+#pragma unroll
+      for (int f = 0; f < NT; ++f) dot += cred[c & 1][hm][f][prow];
+      const float iv = istage[c & 1][prow * HPW + hm];
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(&stage[c & 1][(CT + prow) * LDR + ppc * 8]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g0 = __uint_as_float(v[e] << 16), g1 = __uint_as_float(v[e] & 0xffff0000u);
+        const float q0 = __uint_as_float(qv[e] << 16), q1 = __uint_as_float(qv[e] & 0xffff0000u);
+        v[e] = (uint32_t)f32_to_bf16_bits((g0 - q0 * dot) * iv) |
+               ((uint32_t)f32_to_bf16_bits((g1 - q1 * dot) * iv) << 16);
+      }
+    }
     u32x4* dst = reinterpret_cast<u32x4*>(dqb + __umul24((unsigned)tk, rowb) + (unsigned)(ppc * 16));
     if (full || tk < N) __builtin_nontemporal_store(v, dst);
   };
@@ -206,12 +254,20 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
   }
 }
 
+template <int NT, bool CHAIN>
+static void launch_xdq_chain(const XdqArgs& a, hipStream_t s) {
+  if (a.H % 2 == 0)
+    hipLaunchKernelGGL((xdq_kernel<NT, 2, CHAIN>), dim3(a.B * a.T * (a.H / 2)), dim3(128 * NT), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((xdq_kernel<NT, 1, CHAIN>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0, s, a);
+}
 template <int NT>
 static hipError_t launch_xdq_nt(const XdqArgs& a, hipStream_t s) {
-  if (a.H % 2 == 0)
-    hipLaunchKernelGGL((xdq_kernel<NT, 2>), dim3(a.B * a.T * (a.H / 2)), dim3(128 * NT), 0, s, a);
+  if (a.inv)
+    launch_xdq_chain<NT, true>(a, s);
   else
-    hipLaunchKernelGGL((xdq_kernel<NT, 1>), dim3(a.B * a.T * a.H), dim3(64 * NT), 0, s, a);
+    launch_xdq_chain<NT, false>(a, s);
   return hipGetLastError();
 }
 

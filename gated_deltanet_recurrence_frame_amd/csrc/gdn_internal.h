@@ -116,6 +116,10 @@ struct XdqArgs {
   void* X;              // [B, H, T] x D x D tiles bf16
   void* dq;             // [B, L, H, D]
   int B, H, T, N;
+  // With normalised queries (q holds q / |q|): 1 / |q| of the raw rows,
+  // [B, L, H], and dq receives the gradient of the raw rows,
+  // (dq^ - q^ (q^ . dq^)) / |q|, instead of dq^.  nullptr: dq^.
+  const float* inv;
 };
 // hipErrorNotSupported when the launch does not suit the fused pass (fp32,
 // or fewer than 256 (frame, head group) items): the caller then runs the
@@ -151,6 +155,10 @@ struct BwdTokArgs {
   const void* S;        // bf16: states after each frame, row-major
   const float* s0;      // bf16: [B, H, D, D] fp32 initial state or nullptr (zero)
   float* dgamma;        // bf16: [B, T, H]
+  // bf16, with normalised keys (k holds k / |k|): 1 / |k| of the raw rows,
+  // [B, L, H], and dk receives the gradient of the raw rows,
+  // (dk^ - k^ (k^ . dk^)) / |k|.  nullptr: the gradient of k as given.
+  const float* inv;
 };
 hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
 
@@ -158,12 +166,13 @@ hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
 //   sigmoid:        y[i] = 1 / (1 + exp(-x[i])), i < n (fp32)
 //   sigmoid_bwd:    g[i] <- g[i] p (1 - p), p = sigmoid(x[i])
 //   rows_normalize: y[r] = x[r] / |x[r]| for rows of d io elements (0 for a
+//                   zero row); with inv, also inv[r] = 1 / |x[r]| (0 for a
 //                   zero row)
 //   rows_normalize_bwd: g[r] <- (g[r] - x^ (x^ . g[r])) / |x[r]| in place,
 //                   x^ = x[r] / |x[r]| (0 for a zero row)
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s);
 hipError_t launch_sigmoid_bwd(const float* x, float* g, int64_t n, hipStream_t s);
-hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, int io,
+hipError_t launch_rows_normalize(const void* x, void* y, float* inv, int64_t rows, int d, int io,
                                  hipStream_t s);
 hipError_t launch_rows_normalize_bwd(const void* x, void* g, int64_t rows, int d, int io,
                                      hipStream_t s);

@@ -80,6 +80,7 @@ __device__ __forceinline__ float row_sum(float v) {
 
 template <int IO, int LPR>
 __global__ __launch_bounds__(kPrologueThreads) void rows_normalize_kernel(const void* x, void* y,
+                                                                         float* inv_out,
                                                                          int64_t rows, int ph) {
   const int64_t r = (int64_t)blockIdx.x * (kPrologueThreads / LPR) + threadIdx.x / LPR;
   const int pc = threadIdx.x % LPR;
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(kPrologueThreads) void rows_normalize_kernel(const 
   const float ss = row_sum<LPR>(piece_sumsq<IO>(v));
   const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
   if (live) reinterpret_cast<u32x4*>(y)[r * ph + pc] = piece_scale<IO>(v, inv);
+  if (inv_out && r < rows && pc == 0) inv_out[r] = inv;
 }
 
 template <int IO, int LPR>
@@ -145,7 +147,7 @@ hipError_t launch_sigmoid_bwd(const float* x, float* g, int64_t n, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, int io,
+hipError_t launch_rows_normalize(const void* x, void* y, float* inv, int64_t rows, int d, int io,
                                  hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int ph = d * (io == IO_BF16 ? 2 : 4) / 16;
@@ -153,13 +155,13 @@ hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, in
   const dim3 blk(kPrologueThreads);
   if (io == IO_BF16)
     hipLaunchKernelGGL((rows_normalize_kernel<IO_BF16, 16>), grid_rows(rows, 16), blk, 0, s, x, y,
-                       rows, ph);
+                       inv, rows, ph);
   else if (ph <= 16)
     hipLaunchKernelGGL((rows_normalize_kernel<IO_F32, 16>), grid_rows(rows, 16), blk, 0, s, x, y,
-                       rows, ph);
+                       inv, rows, ph);
   else
     hipLaunchKernelGGL((rows_normalize_kernel<IO_F32, 32>), grid_rows(rows, 32), blk, 0, s, x, y,
-                       rows, ph);
+                       inv, rows, ph);
   return hipGetLastError();
 }
 

@@ -43,9 +43,9 @@ KERNELS = {
     "scan": ("scan_kernel<0, 7, 0>", ["gdn_scan.hip", "gdn_device.h", "gdn_internal.h"]),
     "output": ("output_kernel<0, 7, false, 2, false>", ["gdn_output.hip", "gdn_device.h", "gdn_internal.h"]),
     # backward (bf16, head pairs): X_t and dQ; the reverse scan; dK, dV, dbeta, W_t, dgamma
-    "xdq": ("xdq_kernel<7, 2>", ["gdn_bwd_xdq.hip", "gdn_device.h", "gdn_internal.h"]),
+    "xdq": ("xdq_kernel<7, 2, false>", ["gdn_bwd_xdq.hip", "gdn_device.h", "gdn_internal.h"]),
     "scan_rev": ("scan_kernel<0, 7, 1>", ["gdn_scan.hip", "gdn_device.h", "gdn_internal.h"]),
-    "bwd_kv": ("bwd_kv_kernel<0, 7, 2>", ["gdn_backward.hip", "gdn_device.h", "gdn_internal.h"]),
+    "bwd_kv": ("bwd_kv_kernel<0, 7, 2, false>", ["gdn_backward.hip", "gdn_device.h", "gdn_internal.h"]),
 }
 
 

@@ -110,6 +110,7 @@ hipError_t launch_xdq(const XdqArgs& a, int io, int nt, hipStream_t) {
   need(a.S, mats, "xdq S");
   need(a.X, mats, "xdq X");
   need(a.dq, tok, "xdq dq");
+  need(a.inv, (int64_t)a.B * a.T * a.N * a.H * 4, "xdq inv");
   return hipSuccess;
 }
 hipError_t launch_dm(const DmArgs& a, int io, int nt, hipStream_t) {
@@ -137,6 +138,8 @@ hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t) {
   need(a.S, mats, "bwd S");
   need(a.s0, (int64_t)a.B * a.H * D * D * 4, "bwd s0");
   need(a.dgamma, (int64_t)a.B * a.T * a.H * 4, "bwd dgamma");
+  if (a.inv && io != gdn::IO_BF16) return hipErrorInvalidValue;
+  need(a.inv, (int64_t)a.B * a.T * a.N * a.H * 4, "bwd inv");
   return hipSuccess;
 }
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t) {
@@ -151,10 +154,12 @@ hipError_t launch_sigmoid_bwd(const float* x, float* g, int64_t n, hipStream_t) 
   need(g, n * 4, "sigmoid_bwd g");
   return hipSuccess;
 }
-hipError_t launch_rows_normalize(const void* x, void* y, int64_t rows, int d, int io, hipStream_t) {
+hipError_t launch_rows_normalize(const void* x, void* y, float* inv, int64_t rows, int d, int io,
+                                 hipStream_t) {
   ++g_calls;
   need(x, rows * d * es_of(io), "rows_normalize x");
   need(y, rows * d * es_of(io), "rows_normalize y");
+  need(inv, rows * 4, "rows_normalize inv");
   return hipSuccess;
 }
 hipError_t launch_rows_normalize_bwd(const void* x, void* g, int64_t rows, int d, int io,

@@ -192,13 +192,15 @@ def test_prologue_flags(lib):
     need fp32 copies of gamma and beta in the workspace; normalised rows
     need q / |q| and k / |k| copies where the kernels take them as input
     (the backward, the token form), not in the frame form's forward, which
-    takes the norms from the rows it stages."""
+    takes the norms from the rows it stages.  The bf16 backward also keeps
+    1 / |q| and 1 / |k| per row beside the copies (its token passes apply
+    the normalisation's chain rule to dq and dk themselves)."""
     B, H, T, N, D = 1, 20, 121, 880, 112
     L = T * N
     mat = B * H * T * D * D * 2
     r256 = lambda n: (n + 255) // 256 * 256
     gates = r256(B * T * H * 4) + r256(B * L * H * 4)
-    copies = 2 * r256(B * L * H * D * 2)
+    copies = 2 * r256(B * L * H * D * 2) + 2 * r256(B * L * H * 4)
     for flags, fwd, bwd in ((gb.GDN_FLAG_NORMALIZE_QK, 0, copies),
                             (gb.GDN_FLAG_GATE_LOGITS, gates, gates),
                             (3, gates, gates + copies)):

@@ -189,3 +189,57 @@ def test_backward_prologue(io, flags, use_saved):
     inp = gin.make_inputs(B=2, H=3, T=5, N=100, D=112, io=io, seed=66, with_do=True,
                           with_dstate=True, with_state=True, raw=True)
     check_backward(inp, 100, io, nq, gl, use_saved)
+
+
+@pytest.mark.parametrize("H,D", [(4, 112), (3, 48), (2, 128)])
+@pytest.mark.parametrize("use_saved", [False, True])
+def test_backward_prologue_fused_chain_rule(H, D, use_saved):
+    # bf16 with enough frames for the one-pass dO kernel (256 or more
+    # (frame, head group) items): dq and dk leave the token passes already
+    # through the normalisation's chain rule (head pairs for even H, single
+    # heads for odd H, a last 16-column block at D = 48)
+    T = 260 // (H // 2 if H % 2 == 0 else H) + 1
+    inp = gin.make_inputs(B=1, H=H, T=T, N=70, D=D, io="bf16", seed=67, with_do=True,
+                          with_dstate=True, with_state=True, raw=True)
+    check_backward(inp, 70, "bf16", True, True, use_saved)
+
+
+def test_backward_prologue_fused_chain_rule_zero_rows():
+    # a zero query or key row has no direction: its gradient is zero, and
+    # every other row's matches the oracle's on inputs normalised where the
+    # norm is not zero (the zero rows stay zero there), taken through the
+    # chain rule row by row (gates from logits: raw gates outside (0, 1)
+    # would blow the state up over 131 frames)
+    H, D, N, T = 4, 64, 24, 131
+    inp = gin.make_inputs(B=1, H=H, T=T, N=N, D=D, io="bf16", seed=68, with_do=True,
+                          with_dstate=True, with_state=True, raw=True)
+    zq, zk = [(7, 1), (2000, 3)], [(40, 0), (3001, 2)]
+    for tk, h in zq:
+        inp["q"][0, tk, h] = 0.0
+    for tk, h in zk:
+        inp["k"][0, tk, h] = 0.0
+    d = dev(inp)
+    gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                     state_in=d["state"], d_state_out=d["d_state"], normalize_qk=True,
+                     gate_logits=True)
+    torch.cuda.synchronize()
+    qr, kr = f64(inp["q"]), f64(inp["k"])
+    qn, kn = qr.copy(), kr.copy()
+    for x in (qn, kn):
+        nrm = np.linalg.norm(x, axis=-1, keepdims=True)
+        np.divide(x, nrm, out=x, where=nrm > 0)
+    ref = oracle.backward(qn, kn, f64(inp["v"]), f64(inp["gamma"]), f64(inp["beta"]), N,
+                          f64(inp["d_o"]), state_in=f64(inp["state"]),
+                          d_state_out=f64(inp["d_state"]), gate_logits=True)
+    for name, raw, zs in (("dq", qr, zq), ("dk", kr, zk)):
+        g = ref[name]
+        nrm = np.linalg.norm(raw, axis=-1, keepdims=True)
+        xh = np.divide(raw, nrm, out=np.zeros_like(raw), where=nrm > 0)
+        want = np.divide(g - xh * np.sum(xh * g, axis=-1, keepdims=True), nrm,
+                         out=np.zeros_like(g), where=nrm > 0)
+        got = f64(gr[name].cpu())
+        for tk, h in zs:
+            assert np.all(got[0, tk, h] == 0.0), (name, tk, h)
+        e = rel_l2(got, want)
+        print("zero rows: %s rel_l2 %.3e" % (name, e))
+        assert e <= TOL["bf16"], (name, e)
