@@ -188,26 +188,24 @@ int64_t token_ws(const Shape& s) {
 // backward), q / |q| and k / |k| as [B, L, H, D] io dtype.
 int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
 struct Prologue {
-  int64_t gamma, beta, q, k, iq, ik, end;   // offsets from the region's start; end = bytes
+  int64_t gamma, beta, q, k, iq, end;   // offsets from the region's start; end = bytes
 };
-// `inv`: 1 / |q| and 1 / |k| per row beside the copies (the backward's
-// fused chain rule, bf16)
-Prologue prologue_layout(const Shape& s, bool copies, bool inv = false) {
+// `fused`: the backward's token passes normalise the raw rows themselves
+// and take dq, dk through the chain rule; only 1 / |q| per row is kept
+// (no copies)
+Prologue prologue_layout(const Shape& s, bool copies, bool fused = false) {
   Prologue r{};
   int64_t o = 0;
   if (s.gates) {
     r.gamma = o; o += round256(s.B * s.T * s.H * 4);
     r.beta = o;  o += round256(s.B * s.L * s.H * 4);
   }
-  if (s.norm && copies) {
+  if (s.norm && fused) {
+    r.iq = o; o += round256(s.B * s.L * s.H * 4);
+  } else if (s.norm && copies) {
     const int64_t tok = round256(s.B * s.L * s.H * s.D * s.es);
     r.q = o; o += tok;
     r.k = o; o += tok;
-    if (inv) {
-      const int64_t rows = round256(s.B * s.L * s.H * 4);
-      r.iq = o; o += rows;
-      r.ik = o; o += rows;
-    }
   }
   r.end = o;
   return r;
@@ -224,12 +222,16 @@ int64_t forward_ws(const Shape& s) {
   const int64_t pro = prologue_layout(s, forward_copies(s)).end;
   return pro ? forward_base(s) + pro : (s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
 }
-// The backward takes dq and dk through the normalisation's chain rule
-// inside its token passes for bf16 (the inverse norms then sit beside the
-// normalised copies), in passes of their own for fp32.
-bool backward_inv(const Shape& s) { return s.norm && s.io == IO_BF16; }
+// With normalised rows the bf16 backward's token passes (the one-pass dO
+// kernel and the dK/dV pass) take the raw q and k, normalise them as they
+// stage them and apply the chain rule to dq and dk themselves; otherwise
+// (fp32, launches too short for the one-pass dO kernel) the backward runs
+// on normalised copies and the chain rule runs in passes of its own.
+bool backward_fused_norm(const Shape& s) {
+  return s.norm && xdq_supported(s.io, s.B, s.T, s.H);
+}
 int64_t backward_ws(const Shape& s) {
-  const int64_t pro = prologue_layout(s, true, backward_inv(s)).end;
+  const int64_t pro = prologue_layout(s, true, backward_fused_norm(s)).end;
   return pro ? backward_base(s) + pro : 6 * s.mat + scratch_bytes(s);
 }
 
@@ -241,8 +243,7 @@ struct Inputs {
   const void* k;
   const float* gamma;
   const float* beta;
-  const float* inv_q;   // 1 / |q| per row, or nullptr
-  const float* inv_k;
+  const float* inv_q;   // fused: 1 / |q| per row (q, k raw), else nullptr
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -271,9 +272,9 @@ gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_
 
 gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* k,
                         const float* gamma, const float* beta, char* region, Inputs* in,
-                        hipStream_t stream, bool inv = false) {
-  const Prologue pl = prologue_layout(s, copies, inv);
-  *in = Inputs{q, k, gamma, beta, nullptr, nullptr};
+                        hipStream_t stream, bool fused = false) {
+  const Prologue pl = prologue_layout(s, copies, fused);
+  *in = Inputs{q, k, gamma, beta, nullptr};
   hipError_t e = hipSuccess;
   if (s.gates) {
     float* g = reinterpret_cast<float*>(region + pl.gamma);
@@ -283,18 +284,19 @@ gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* 
     in->gamma = g;
     in->beta = b;
   }
-  if (e == hipSuccess && s.norm && copies) {
+  const int64_t rows = s.B * s.L * s.H;
+  if (e == hipSuccess && s.norm && fused) {
+    // 1 / |q| per row only; q and k stay raw
+    float* iq = reinterpret_cast<float*>(region + pl.iq);
+    e = launch_rows_normalize(q, nullptr, iq, rows, (int)s.D, s.io, stream);
+    in->inv_q = iq;
+  } else if (e == hipSuccess && s.norm && copies) {
     void* qn = region + pl.q;
     void* kn = region + pl.k;
-    float* iq = inv ? reinterpret_cast<float*>(region + pl.iq) : nullptr;
-    float* ik = inv ? reinterpret_cast<float*>(region + pl.ik) : nullptr;
-    const int64_t rows = s.B * s.L * s.H;
-    e = launch_rows_normalize(q, qn, iq, rows, (int)s.D, s.io, stream);
-    if (e == hipSuccess) e = launch_rows_normalize(k, kn, ik, rows, (int)s.D, s.io, stream);
+    e = launch_rows_normalize(q, qn, nullptr, rows, (int)s.D, s.io, stream);
+    if (e == hipSuccess) e = launch_rows_normalize(k, kn, nullptr, rows, (int)s.D, s.io, stream);
     in->q = qn;
     in->k = kn;
-    in->inv_q = iq;
-    in->inv_k = ik;
   }
   return hip_status(e);
 }
@@ -685,8 +687,8 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   const float* gamma_raw = gamma;
   const float* beta_raw = beta;
   Inputs in;
-  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_,
-                    backward_inv(s));
+  const bool fused = backward_fused_norm(s);
+  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_, fused);
   if (st != GDN_OK) return st;
   q = in.q; k = in.k; gamma = in.gamma; beta = in.beta;
   const void* A;
@@ -708,6 +710,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
     ga.t0 = 0; ga.Tc = (int)s.T;
     ga.P = gram_splits(s);
     ga.part = reinterpret_cast<float*>(ws + 6 * s.mat);
+    ga.norm = fused;   // raw keys: norms of the staged rows, as in the forward
     st = hip_status(launch_gram(ga, s.io, nt, 2, stream_));
     if (st != GDN_OK) return st;
     if (ga.P > 1 && (st = hip_status(launch_gram_reduce(ga, s.io, nt, 2, stream_))) != GDN_OK)
@@ -728,9 +731,9 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   XdqArgs xa{};
   xa.d_o = d_o; xa.q = q; xa.S = S; xa.X = ws + 3 * s.mat; xa.dq = dq;
   xa.B = (int)s.B; xa.H = (int)s.H; xa.T = (int)s.T; xa.N = (int)s.N;
-  xa.inv = in.inv_q;   // with normalised queries: dq of the raw rows
+  xa.inv = in.inv_q;   // fused: raw queries, dq of the raw rows
   hipError_t xe = launch_xdq(xa, s.io, nt, stream_);
-  if (xe != hipSuccess && xe != hipErrorNotSupported) return GDN_ERR_HIP;
+  if (xe != hipSuccess && (xe != hipErrorNotSupported || fused)) return GDN_ERR_HIP;
   const bool fused_dq = xe == hipSuccess;
   GramArgs gx{};
   gx.x0 = d_o; gx.x1 = nullptr; gx.y = q; gx.w = nullptr; gx.out0 = X; gx.out1 = nullptr;
@@ -777,7 +780,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   ba.dk = dk; ba.dv = dv; ba.dbeta = dbeta; ba.s = s.s;
   ba.B = (int)s.B; ba.H = (int)s.H; ba.T = (int)s.T; ba.N = (int)s.N;
   ba.S = S; ba.s0 = state_in; ba.dgamma = dgamma;
-  ba.inv = in.inv_k;   // with normalised keys: dk of the raw rows
+  ba.norm = fused;   // raw keys normalised in the pass, dk of the raw rows
   st = hip_status(launch_bwd_tok(ba, s.io, nt, stream_));
   if (st != GDN_OK) return st;
 
@@ -785,10 +788,10 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   hipError_t e = hipSuccess;
   if (s.norm) {
     const int64_t rows = s.B * s.L * s.H;
-    if (!(fused_dq && in.inv_q))
+    if (!fused) {
       e = launch_rows_normalize_bwd(q_raw, dq, rows, (int)s.D, s.io, stream_);
-    if (e == hipSuccess && !in.inv_k)
-      e = launch_rows_normalize_bwd(k_raw, dk, rows, (int)s.D, s.io, stream_);
+      if (e == hipSuccess) e = launch_rows_normalize_bwd(k_raw, dk, rows, (int)s.D, s.io, stream_);
+    }
   }
   if (e == hipSuccess && s.gates) {
     e = launch_sigmoid_bwd(gamma_raw, dgamma, s.B * s.T * s.H, stream_);

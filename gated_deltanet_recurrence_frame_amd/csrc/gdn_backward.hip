@@ -189,10 +189,13 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
 // LDS and stored one chunk later as contiguous 16-byte pieces of token
 // rows; dbeta sums the per-feature-tile partial dot products in a fixed
 // order (deterministic, no atomics).
-// With normalised keys (CHAIN, bf16: k holds k^ = k / |k| and inv 1 / |k|)
-// dK^ goes through the normalisation's chain rule before it is stored, as
-// in the query pass: dk = (dk^ - k^ (k^ . dk^)) / |k|, the dot summed over
-// the feature tiles in a fixed order.
+// With normalised keys (CHAIN, bf16) the pass reads the raw key rows: each
+// wave sums the squares of the key fragments it loads (every wave reads all
+// of its head's features of a token), so it has |k| per token; its products
+// with k (per-token columns) and k itself are scaled by 1 / |k| (0 for a zero
+// row), and dK^ goes through the normalisation's chain rule before it is
+// stored, dk = (dk^ - k^ (k^ . dk^)) / |k|, the dot summed over the feature
+// tiles in a fixed order.
 // Registers bound the shape: at 14 waves per CU a wave has 128 VGPRs, of
 // which its three matrices take 48; chunks of 16 tokens (pairs) two deep
 // fit without spills (at D = 112 the whole backward went from 1.17 to
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   __shared__ float red[2][HPW][NT][CT];                               // dbeta partials
   static_assert(!CHAIN || BF, "the fused chain rule is for bf16");
   __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];                  // k^ . dk^ partials
-  __shared__ float istage[CHAIN ? 2 : 1][NB];                         // 1 / |k|
+  __shared__ float istage[CHAIN ? 2 : 1][NB];                         // 1 / |k| per token, head
 
   const int HG = a.H / HPW;
   const int total = a.B * a.T * HG;
@@ -380,7 +383,6 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   struct Ring {
     u32x4 v[PPT];
     float bt;
-    float iv;   // CHAIN: 1 / |k| of the same (token, head) as bt
   };
   // Chunk c: piece p = tid + NTH j of [K rows | V rows] (row p / PR of
   // matrix (p / (CT PR))), rows past the frame re-read its last row.
@@ -400,8 +402,6 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     int tk = c0 + bi / HPW;
     if (tk >= N) tk = N - 1;
     R.bt = bframe[__umul24((unsigned)tk, (unsigned)a.H) + (unsigned)(bi % HPW)];
-    if constexpr (CHAIN)
-      R.iv = a.inv[row0 * a.H + h0 + __umul24((unsigned)tk, (unsigned)a.H) + (unsigned)(bi % HPW)];
   };
   auto commit = [&](const Ring& R, int c) {
     E* st = stage(c & 1);
@@ -413,9 +413,6 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     }
     // tokens past the frame's end get gate 0 (their rows are re-read copies)
     if (tid < NB) bstage[c & 1][tid] = c * CT + tid / HPW < N ? R.bt : 0.f;
-    if constexpr (CHAIN) {
-      if (tid < NB) istage[c & 1][tid] = R.iv;
-    }
   };
   auto load4 = [&](const E* row) -> f32x4 {   // 4 values at this lane's features
     f32x4 r;
@@ -451,6 +448,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     for (int tt = 0; tt < CT / 16; ++tt) {
       const int trow = tt * 16 + li;
       f32x4 ay = zero4(), az = zero4(), aw = zero4();
+      float ss = 0.f;   // CHAIN: this lane's share of |k|^2 for token li
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if constexpr (BF) {
@@ -464,6 +462,13 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
           ay = mfma_bf16(mG[kb], kf, ay);
           az = mfma_bf16(mGT[kb], vf, az);
           aw = mfma_bf16(mW[kb], kf, aw);
+          if constexpr (CHAIN) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = static_cast<float>(kf[e]);
+              ss = fmaf(x, x, ss);
+            }
+          }
           // one block's fragments live at a time (registers)
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -476,8 +481,21 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
         }
       }
       const float bt = bs[trow * HPW + hp];
-      const f32x4 kv = load4(ks + trow * LDR);
+      f32x4 kv = load4(ks + trow * LDR);
       const f32x4 vv = load4(vs + trow * LDR);
+      if constexpr (CHAIN) {
+        // |k|^2 of token li: the four lane groups hold its 32-feature blocks' eighths
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float iv = inv_norm(ss);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ay[r] *= iv;
+          aw[r] *= iv;
+          kv[r] *= iv;
+        }
+        if (ft == 0 && g == 0) istage[c & 1][trow * HPW + hp] = iv;
+      }
       f32x4 dvv, dkv;
       float part = 0.f;
 #pragma unroll
@@ -523,8 +541,10 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
           const u32x4 kx = *reinterpret_cast<const u32x4*>(stage(c & 1) + row * LDR + pc * 8);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            // the staged row is raw: k^ = k / |k|
             const float g0 = __uint_as_float(v[e] << 16), g1 = __uint_as_float(v[e] & 0xffff0000u);
-            const float k0 = __uint_as_float(kx[e] << 16), k1 = __uint_as_float(kx[e] & 0xffff0000u);
+            const float k0 = __uint_as_float(kx[e] << 16) * iv;
+            const float k1 = __uint_as_float(kx[e] & 0xffff0000u) * iv;
             v[e] = (uint32_t)f32_to_bf16_bits((g0 - k0 * dot) * iv) |
                    ((uint32_t)f32_to_bf16_bits((g1 - k1 * dot) * iv) << 16);
           }
@@ -616,12 +636,12 @@ static void launch_bwd_tok_chain(const BwdTokArgs& a, hipStream_t s) {
 template <int IO, int NT>
 static hipError_t launch_bwd_tok_nt(const BwdTokArgs& a, hipStream_t s) {
   if constexpr (IO == IO_BF16) {
-    if (a.inv) {
+    if (a.norm) {
       launch_bwd_tok_chain<IO, NT, true>(a, s);
       return hipGetLastError();
     }
   } else {
-    if (a.inv) return hipErrorInvalidValue;   // the fused chain rule is bf16 only
+    if (a.norm) return hipErrorInvalidValue;   // normalised raw keys: bf16 only
   }
   launch_bwd_tok_chain<IO, NT, false>(a, s);
   return hipGetLastError();

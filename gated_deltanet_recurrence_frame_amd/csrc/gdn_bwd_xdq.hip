@@ -23,11 +23,12 @@
 // dO rows past the frame's end are zeroed when staged, so they add nothing
 // to X (their dQ rows are not stored).
 //
-// With normalised queries (CHAIN: q holds q^ = q / |q| and inv 1 / |q|) the
-// pass also takes dQ^ through the normalisation's chain rule before storing
-// it: dq = (dq^ - q^ (q^ . dq^)) / |q| (summary page, 方法步骤详情 module 2,
-// the hats read as per-token normalisation).  Each wave adds q^ . dq^ over
-// its 16 features of a token; the stores sum the tiles' partials in a fixed
+// With normalised queries (CHAIN) the pass reads the raw query rows and
+// 1 / |q| per row (summary page, 方法步骤详情 module 2, the hats read as
+// per-token normalisation): each thread stages its piece as q^ = q / |q|
+// (bf16), and dQ^ goes through the normalisation's chain rule before it is
+// stored, dq = (dq^ - q^ (q^ . dq^)) / |q|.  Each wave adds q^ . dq^ over its
+// 16 features of a token; the stores sum the tiles' partials in a fixed
 // order (deterministic) and apply the rule to whole 16-byte pieces.
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -62,9 +63,9 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
   static_assert(HPW * KR * D <= 2 * STAGE, "S_t of the group must fit the stage");
   __shared__ __attribute__((aligned(16))) uint16_t stage[2][STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t obuf[2][CT * LDO];
-  // CHAIN: q^ . dq^ per (head, tile, token), 1 / |q| per (token, head)
+  // CHAIN: q^ . dq^ per (head, tile, token); 1 / |q| of each thread's piece
   __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];
-  __shared__ float istage[CHAIN ? 2 : 1][CT * HPW];
+  __shared__ float istage[CHAIN ? 2 : 1][CHAIN ? NTH : 1];
 
   const int HG = a.H / HPW;
   const int total = a.B * a.T * HG;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
 
   struct Ring {
     u32x4 o, q;
-    float iv;   // CHAIN: 1 / |q| of token tid / HPW, head tid % HPW
+    float iv;   // CHAIN: 1 / |q| of this thread's piece (token, head)
   };
   auto issue = [&](Ring& R, int c) {
     int tk = (c < nchunks ? c : nchunks - 1) * CT + prow;
@@ -120,20 +121,17 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
     const unsigned off = __umul24((unsigned)tk, rowb) + (unsigned)(ppc * 16);
     R.o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dob + off));
     R.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qb + off));
-    if constexpr (CHAIN) {
-      const int bi = tid < CT * HPW ? tid : 0;
-      int ti = (c < nchunks ? c : nchunks - 1) * CT + bi / HPW;
-      if (ti >= N) ti = N - 1;
-      R.iv = a.inv[(row0 + ti) * a.H + h0 + bi % HPW];
-    }
+    if constexpr (CHAIN) R.iv = a.inv[(row0 + tk) * a.H + h0 + ppc / (D / 8)];
   };
   auto commit = [&](const Ring& R, int c) {
     uint16_t* st = stage[c & 1];
     const bool live = c * CT + prow < N;        // rows past the frame: dO zero
     *reinterpret_cast<u32x4*>(st + prow * LDR + ppc * 8) = live ? R.o : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(st + (CT + prow) * LDR + ppc * 8) = R.q;
     if constexpr (CHAIN) {
-      if (tid < CT * HPW) istage[c & 1][tid] = R.iv;
+      *reinterpret_cast<u32x4*>(st + (CT + prow) * LDR + ppc * 8) = piece_scale<IO_BF16>(R.q, R.iv);
+      istage[c & 1][tid] = R.iv;   // read back by this thread when it stores the chunk
+    } else {
+      *reinterpret_cast<u32x4*>(st + (CT + prow) * LDR + ppc * 8) = R.q;
     }
   };
 
@@ -193,7 +191,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
       float dot = 0.f;
 #pragma unroll
       for (int f = 0; f < NT; ++f) dot += cred[c & 1][hm][f][prow];
-      const float iv = istage[c & 1][prow * HPW + hm];
+      const float iv = istage[c & 1][tid];
       const u32x4 qv = *reinterpret_cast<const u32x4*>(&stage[c & 1][(CT + prow) * LDR + ppc * 8]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -271,9 +269,12 @@ static hipError_t launch_xdq_nt(const XdqArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool xdq_supported(int io, int64_t B, int64_t T, int64_t H) {
+  return io == IO_BF16 && B * T * (H % 2 == 0 ? H / 2 : H) >= 256;
+}
+
 hipError_t launch_xdq(const XdqArgs& a, int io, int nt, hipStream_t s) {
-  const long items = (long)a.B * a.T * (a.H % 2 == 0 ? a.H / 2 : a.H);
-  if (io != IO_BF16 || items < 256) return hipErrorNotSupported;
+  if (!xdq_supported(io, a.B, a.T, a.H)) return hipErrorNotSupported;
   switch (nt) {
     case 1: return launch_xdq_nt<1>(a, s);
     case 2: return launch_xdq_nt<2>(a, s);

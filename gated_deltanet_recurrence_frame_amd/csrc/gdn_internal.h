@@ -116,11 +116,15 @@ struct XdqArgs {
   void* X;              // [B, H, T] x D x D tiles bf16
   void* dq;             // [B, L, H, D]
   int B, H, T, N;
-  // With normalised queries (q holds q / |q|): 1 / |q| of the raw rows,
-  // [B, L, H], and dq receives the gradient of the raw rows,
-  // (dq^ - q^ (q^ . dq^)) / |q|, instead of dq^.  nullptr: dq^.
+  // Normalised queries taken from the raw rows: q holds the raw queries and
+  // inv 1 / |q| per row, [B, L, H] (0 for a zero row); the pass stages
+  // q^ = q inv and dq receives the gradient of the raw rows,
+  // (dq^ - q^ (q^ . dq^)) / |q|.  nullptr: q is used as given, dq = dq^.
   const float* inv;
 };
+// Whether launch_xdq takes a launch (bf16, 256 or more (frame, head group)
+// items).
+bool xdq_supported(int io, int64_t B, int64_t T, int64_t H);
 // hipErrorNotSupported when the launch does not suit the fused pass (fp32,
 // or fewer than 256 (frame, head group) items): the caller then runs the
 // Gram-mode X pass and the transposed output pass instead.
@@ -155,10 +159,11 @@ struct BwdTokArgs {
   const void* S;        // bf16: states after each frame, row-major
   const float* s0;      // bf16: [B, H, D, D] fp32 initial state or nullptr (zero)
   float* dgamma;        // bf16: [B, T, H]
-  // bf16, with normalised keys (k holds k / |k|): 1 / |k| of the raw rows,
-  // [B, L, H], and dk receives the gradient of the raw rows,
-  // (dk^ - k^ (k^ . dk^)) / |k|.  nullptr: the gradient of k as given.
-  const float* inv;
+  // bf16, normalised keys taken from the raw rows: k holds the raw keys, the
+  // pass forms |k| per row from the rows it stages, uses k^ = k / |k| (0 for
+  // a zero row), and dk receives the gradient of the raw rows,
+  // (dk^ - k^ (k^ . dk^)) / |k|.  0: k is used as given.
+  int norm;
 };
 hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
 
@@ -166,8 +171,8 @@ hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t s);
 //   sigmoid:        y[i] = 1 / (1 + exp(-x[i])), i < n (fp32)
 //   sigmoid_bwd:    g[i] <- g[i] p (1 - p), p = sigmoid(x[i])
 //   rows_normalize: y[r] = x[r] / |x[r]| for rows of d io elements (0 for a
-//                   zero row); with inv, also inv[r] = 1 / |x[r]| (0 for a
-//                   zero row)
+//                   zero row), unless y is nullptr; with inv, also
+//                   inv[r] = 1 / |x[r]| (0 for a zero row)
 //   rows_normalize_bwd: g[r] <- (g[r] - x^ (x^ . g[r])) / |x[r]| in place,
 //                   x^ = x[r] / |x[r]| (0 for a zero row)
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s);

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kPrologueThreads) void rows_normalize_kernel(const 
   if (live) v = reinterpret_cast<const u32x4*>(x)[r * ph + pc];
   const float ss = row_sum<LPR>(piece_sumsq<IO>(v));
   const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-  if (live) reinterpret_cast<u32x4*>(y)[r * ph + pc] = piece_scale<IO>(v, inv);
+  if (live && y) reinterpret_cast<u32x4*>(y)[r * ph + pc] = piece_scale<IO>(v, inv);
   if (inv_out && r < rows && pc == 0) inv_out[r] = inv;
 }
 

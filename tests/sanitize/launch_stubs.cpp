@@ -98,10 +98,12 @@ hipError_t launch_output(const OutArgs& a, int io, int nt, bool, hipStream_t) {
   need(a.out, tok, "output out");
   return hipSuccess;
 }
+bool xdq_supported(int io, int64_t B, int64_t T, int64_t H) {
+  return io == IO_BF16 && B * T * (H % 2 == 0 ? H / 2 : H) >= 256;
+}
 hipError_t launch_xdq(const XdqArgs& a, int io, int nt, hipStream_t) {
   // (the fused pass declines fp32 and launches of few items, like the real one)
-  const long items = (long)a.B * a.T * (a.H % 2 == 0 ? a.H / 2 : a.H);
-  if (io != IO_BF16 || items < 256) return hipErrorNotSupported;
+  if (!xdq_supported(io, a.B, a.T, a.H)) return hipErrorNotSupported;
   ++g_calls;
   const int64_t D = 16 * nt, tok = (int64_t)a.B * a.T * a.N * a.H * D * 2;
   const int64_t mats = (int64_t)a.B * a.H * a.T * D * D * 2;
@@ -138,8 +140,7 @@ hipError_t launch_bwd_tok(const BwdTokArgs& a, int io, int nt, hipStream_t) {
   need(a.S, mats, "bwd S");
   need(a.s0, (int64_t)a.B * a.H * D * D * 4, "bwd s0");
   need(a.dgamma, (int64_t)a.B * a.T * a.H * 4, "bwd dgamma");
-  if (a.inv && io != gdn::IO_BF16) return hipErrorInvalidValue;
-  need(a.inv, (int64_t)a.B * a.T * a.N * a.H * 4, "bwd inv");
+  if (a.norm && io != gdn::IO_BF16) return hipErrorInvalidValue;
   return hipSuccess;
 }
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t) {

@@ -192,21 +192,28 @@ def test_prologue_flags(lib):
     need fp32 copies of gamma and beta in the workspace; normalised rows
     need q / |q| and k / |k| copies where the kernels take them as input
     (the backward, the token form), not in the frame form's forward, which
-    takes the norms from the rows it stages.  The bf16 backward also keeps
-    1 / |q| and 1 / |k| per row beside the copies (its token passes apply
-    the normalisation's chain rule to dq and dk themselves)."""
+    takes the norms from the rows it stages.  The bf16 backward of a launch
+    long enough for its one-pass dO kernel takes the raw rows too and keeps
+    only 1 / |q| per row; shorter launches and fp32 take the copies."""
     B, H, T, N, D = 1, 20, 121, 880, 112
     L = T * N
     mat = B * H * T * D * D * 2
     r256 = lambda n: (n + 255) // 256 * 256
     gates = r256(B * T * H * 4) + r256(B * L * H * 4)
-    copies = 2 * r256(B * L * H * D * 2) + 2 * r256(B * L * H * 4)
-    for flags, fwd, bwd in ((gb.GDN_FLAG_NORMALIZE_QK, 0, copies),
+    inv_q = r256(B * L * H * 4)
+    for flags, fwd, bwd in ((gb.GDN_FLAG_NORMALIZE_QK, 0, inv_q),
                             (gb.GDN_FLAG_GATE_LOGITS, gates, gates),
-                            (3, gates, gates + copies)):
+                            (3, gates, gates + inv_q)):
         p = gb.make_problem(B, H, T, N, D, "bf16", flags=flags)
         assert _ws(p, gb.GDN_OP_FORWARD) == (0, 3 * mat + fwd)
         assert _ws(p, gb.GDN_OP_BACKWARD) == (0, 6 * mat + bwd)
+    # 8 frames of 20 heads: 80 (frame, head pair) items, too few for the
+    # one-pass dO kernel: copies of q and k
+    # (beside the backward's own buffers and the Gram token-split partials
+    # such a short launch takes)
+    ps = gb.make_problem(B, H, 8, N, D, "bf16", flags=1)
+    plain = _ws(gb.make_problem(B, H, 8, N, D, "bf16"), gb.GDN_OP_BACKWARD)[1]
+    assert _ws(ps, gb.GDN_OP_BACKWARD) == (0, r256(plain) + 2 * r256(B * 8 * N * H * D * 2))
     pt = gb.make_problem(1, 2, 4, 8, 32, "bf16", algorithm="token", flags=3)
     base = 2 * (2 * 64 * 64 * 2 + 5 * 64 * 4)
     assert _ws(pt, gb.GDN_OP_FORWARD) == (
