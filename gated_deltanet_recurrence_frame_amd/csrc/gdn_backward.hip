@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     for (int tt = 0; tt < CT / 16; ++tt) {
       const int trow = tt * 16 + li;
       f32x4 ay = zero4(), az = zero4(), aw = zero4();
-      float ss = 0.f;   // CHAIN: this lane's share of |k|^2 for token li
+      f32x4 gram = zero4();   // CHAIN: K K^T of the tile's 16 tokens (its diagonal: |k|^2)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if constexpr (BF) {
@@ -462,13 +462,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
           ay = mfma_bf16(mG[kb], kf, ay);
           az = mfma_bf16(mGT[kb], vf, az);
           aw = mfma_bf16(mW[kb], kf, aw);
-          if constexpr (CHAIN) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = static_cast<float>(kf[e]);
-              ss = fmaf(x, x, ss);
-            }
-          }
+          if constexpr (CHAIN) gram = mfma_bf16(kf, kf, gram);
           // one block's fragments live at a time (registers)
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -484,10 +478,10 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
       f32x4 kv = load4(ks + trow * LDR);
       const f32x4 vv = load4(vs + trow * LDR);
       if constexpr (CHAIN) {
-        // |k|^2 of token li: the four lane groups hold its 32-feature blocks' eighths
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const float iv = inv_norm(ss);
+        // |k|^2 of token li: the diagonal entry (li, li), in lane (li / 4, li)
+        const int rr = li & 3;
+        const float dg = rr == 0 ? gram[0] : rr == 1 ? gram[1] : rr == 2 ? gram[2] : gram[3];
+        const float iv = inv_norm(__shfl(dg, ((li >> 2) << 4) | li));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           ay[r] *= iv;
