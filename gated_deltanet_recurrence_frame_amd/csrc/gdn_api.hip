@@ -215,6 +215,9 @@ int64_t forward_base(const Shape& s) {
   return round256(s.token ? token_ws(s) : 3 * s.mat + scratch_bytes(s));
 }
 int64_t backward_base(const Shape& s) { return round256(6 * s.mat + scratch_bytes(s)); }
+// The saved buffer: A_t, S_t, then with normalised rows 1 / |q| per row
+// (fp32 [B, L, H]), which the output pass computes anyway.
+int64_t saved_bytes(const Shape& s) { return 2 * s.mat + (s.norm ? s.B * s.L * s.H * 4 : 0); }
 // The direct form takes normalised copies of q and k too; it falls back to
 // the frame form (same workspace start) when a saved buffer is asked for.
 bool forward_copies(const Shape& s) { return s.token || s.direct; }
@@ -272,7 +275,8 @@ gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_
 
 gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* k,
                         const float* gamma, const float* beta, char* region, Inputs* in,
-                        hipStream_t stream, bool fused = false) {
+                        hipStream_t stream, bool fused = false,
+                        const float* given_inv_q = nullptr) {
   const Prologue pl = prologue_layout(s, copies, fused);
   *in = Inputs{q, k, gamma, beta, nullptr};
   hipError_t e = hipSuccess;
@@ -286,10 +290,15 @@ gdn_status run_prologue(const Shape& s, bool copies, const void* q, const void* 
   }
   const int64_t rows = s.B * s.L * s.H;
   if (e == hipSuccess && s.norm && fused) {
-    // 1 / |q| per row only; q and k stay raw
-    float* iq = reinterpret_cast<float*>(region + pl.iq);
-    e = launch_rows_normalize(q, nullptr, iq, rows, (int)s.D, s.io, stream);
-    in->inv_q = iq;
+    // 1 / |q| per row only (from the saved buffer when the forward kept
+    // it); q and k stay raw
+    if (given_inv_q) {
+      in->inv_q = given_inv_q;
+    } else {
+      float* iq = reinterpret_cast<float*>(region + pl.iq);
+      e = launch_rows_normalize(q, nullptr, iq, rows, (int)s.D, s.io, stream);
+      in->inv_q = iq;
+    }
   } else if (e == hipSuccess && s.norm && copies) {
     void* qn = region + pl.q;
     void* kn = region + pl.k;
@@ -481,6 +490,7 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
   oa.t0 = 0; oa.Tc = (int)s.T;
   oa.P = out_splits(s);
   oa.norm = s.norm;   // fused: norms of the staged query rows
+  if (saved && s.norm) oa.inv_out = reinterpret_cast<float*>(static_cast<char*>(saved) + 2 * s.mat);
   st = hip_status(launch_output(oa, s.io, nt, false, stream));
   if (st != GDN_OK) return st;
   return record(events, 3, stream);
@@ -559,7 +569,7 @@ gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes) {
   // the token and direct forms keep no A_t, S_t (GDN_ALGO_AUTO's direct
   // form gives way to the frame form when a saved buffer is passed)
   if (s.token || s.algo == GDN_ALGO_DIRECT) return GDN_ERR_UNSUPPORTED;
-  *bytes = (size_t)(2 * s.mat);
+  *bytes = (size_t)saved_bytes(s);
   return GDN_OK;
 }
 
@@ -583,7 +593,7 @@ static gdn_status forward_checked(const gdn_problem* p, const void* q, const voi
   const int64_t stb = s.B * s.H * s.D * s.D * 4;
   const Span ins[] = {{q, tok}, {k, tok}, {v, tok}, {gamma, s.B * s.T * s.H * 4},
                       {beta, s.B * s.L * s.H * 4}, {state_in, stb}};
-  const Span outs[] = {{o, tok}, {saved, saved ? 2 * s.mat : 0},
+  const Span outs[] = {{o, tok}, {saved, saved ? saved_bytes(s) : 0},
                        {workspace, (int64_t)workspace_bytes}};
   if (any_overlap(outs, 3, ins, 6)) return GDN_ERR_ALIASING;
   if (state_out) {
@@ -670,7 +680,7 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   const int64_t stb = s.B * s.H * s.D * s.D * 4;
   const Span ins[] = {{q, tok}, {k, tok}, {v, tok}, {gamma, s.B * s.T * s.H * 4},
                       {beta, s.B * s.L * s.H * 4}, {state_in, stb}, {d_o, tok},
-                      {d_state_out, stb}, {saved, saved ? 2 * s.mat : 0}};
+                      {d_state_out, stb}, {saved, saved ? saved_bytes(s) : 0}};
   const Span outs[] = {{dq, tok}, {dk, tok}, {dv, tok}, {dgamma, s.B * s.T * s.H * 4},
                        {dbeta, s.B * s.L * s.H * 4}, {d_state_in, stb},
                        {workspace, (int64_t)workspace_bytes}};
@@ -688,7 +698,11 @@ gdn_status gdn_backward(const gdn_problem* p, const void* q, const void* k, cons
   const float* beta_raw = beta;
   Inputs in;
   const bool fused = backward_fused_norm(s);
-  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_, fused);
+  const float* saved_inv_q =
+      saved && s.norm ? reinterpret_cast<const float*>(static_cast<const char*>(saved) + 2 * s.mat)
+                      : nullptr;
+  st = run_prologue(s, true, q, k, gamma, beta, ws + backward_base(s), &in, stream_, fused,
+                    saved_inv_q);
   if (st != GDN_OK) return st;
   q = in.q; k = in.k; gamma = in.gamma; beta = in.beta;
   const void* A;

@@ -103,6 +103,7 @@ struct OutArgs {
   int t0, Tc;           // frames t0 .. t0 + Tc - 1
   int P;                // token splits: each frame's chunks over P workgroups
   int norm;             // O_t = S_t (q / |q|) per token (forward only; 0 for a zero row)
+  float* inv_out;       // with norm: 1 / |q| per row, [B, L, H] (0 for a zero row), or nullptr
 };
 hipError_t launch_output(const OutArgs& a, int io, int nt, bool trans, hipStream_t s);
 

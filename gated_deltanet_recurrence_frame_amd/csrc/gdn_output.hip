@@ -28,7 +28,9 @@
 // whose result Q Q^T holds |q_i|^2 on its diagonal (lane (i / 4, i),
 // register i % 4), read back by every lane of token i.  fp32: each lane
 // sums the squares of its quarter of the features, added over the
-// token's four lanes.
+// token's four lanes.  With inv_out the first wave also writes 1 / |q| of
+// every token it scales (the forward keeps it in the saved buffer for the
+// backward).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -191,7 +193,11 @@ __global__ __launch_bounds__(64 * NT, IO == IO_BF16 ? 4 : 1) void output_kernel(
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
           }
-          acc *= inv_norm(ss);
+          const float iv = inv_norm(ss);
+          acc *= iv;
+          // 1 / |q| per row for the backward (every wave has it; the first writes)
+          const int tq = (cbeg + c) * CT + tt * 16 + li;
+          if (a.inv_out && ft == 0 && g == 0 && tq < N) a.inv_out[(row0 + tq) * a.H + h0 + hp] = iv;
         }
         E* dst = ob + (tt * 16 + li) * LDR + hp * D + ft * 16 + 4 * g;
         if constexpr (BF) {

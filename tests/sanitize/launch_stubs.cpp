@@ -96,6 +96,7 @@ hipError_t launch_output(const OutArgs& a, int io, int nt, bool, hipStream_t) {
   need(a.tok, tok, "output tok");
   need(a.mat, (int64_t)a.B * a.H * a.T * D * D * es_of(io), "output mat");
   need(a.out, tok, "output out");
+  need(a.inv_out, (int64_t)a.B * a.T * a.N * a.H * 4, "output inv_out");
   return hipSuccess;
 }
 bool xdq_supported(int io, int64_t B, int64_t T, int64_t H) {

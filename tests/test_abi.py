@@ -79,6 +79,10 @@ def test_workspace_sizes(lib):
     assert _ws(gb.make_problem(B, H, T, N, D, "bf16", scan_chunk=500), gb.GDN_OP_FORWARD) == (0, 3 * mat)
     pf = gb.make_problem(B, H, T, N, D, "fp32")
     assert gb.saved_size(pf) == 2 * B * H * T * D * D * 4
+    # with normalised rows the saved buffer also keeps 1 / |q| per row (fp32)
+    for io, es in (("bf16", 2), ("fp32", 4)):
+        pn = gb.make_problem(B, H, T, N, D, io, flags=gb.GDN_FLAG_NORMALIZE_QK)
+        assert gb.saved_size(pn) == 2 * B * H * T * D * D * es + B * T * N * H * 4
 
 
 @pytest.mark.parametrize("field,value,status", [

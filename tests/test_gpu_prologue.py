@@ -243,3 +243,24 @@ def test_backward_prologue_fused_chain_rule_zero_rows():
         e = rel_l2(got, want)
         print("zero rows: %s rel_l2 %.3e" % (name, e))
         assert e <= TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_saved_inverse_query_norms(io):
+    # with normalised rows the saved buffer ends with 1 / |q| per row (fp32
+    # [B, L, H]), formed by the forward's output pass; a zero row gets 0
+    B, H, T, N, D = 1, 4, 6, 50, 48
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=io, seed=69, raw=True)
+    inp["q"][0, 17, 2] = 0.0
+    d = dev(inp)
+    _, _, saved = gb.forward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N,
+                             return_saved=True, normalize_qk=True, gate_logits=True)
+    torch.cuda.synchronize()
+    es = 2 if io == "bf16" else 4
+    mat = B * H * T * D * D * es
+    assert saved.numel() == 2 * mat + B * T * N * H * 4
+    inv = saved[2 * mat:].view(torch.float32).cpu().numpy().astype(np.float64).reshape(B, T * N, H)
+    nrm = np.linalg.norm(f64(inp["q"]), axis=-1)
+    want = np.divide(1.0, nrm, out=np.zeros_like(nrm), where=nrm > 0)
+    assert inv[0, 17, 2] == 0.0
+    assert np.max(np.abs(inv - want) / np.maximum(want, 1e-30)) < 1e-5
