@@ -34,16 +34,8 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-# Per-file additions.  The one-wave scan keeps its MFMA results in ordinary
-# VGPRs (the state update reads them straight away), not in AGPRs that every
-# VALU read would first have to copy out.
-FILE_FLAGS = {
-    "gdn_scan_wave.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-}
-
-
 def _compile(src, obj):
-    cmd = [_hipcc()] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+    cmd = [_hipcc()] + FLAGS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s" % (src, r.stderr))

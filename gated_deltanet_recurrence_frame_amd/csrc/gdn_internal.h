@@ -23,8 +23,9 @@ namespace gdn {
 //              and then 32 k + 16 + 4 g .. + 3 (8 values).  Inside a
 //              contraction block that order is free (both operands take it),
 //              and it is the order in which two accumulator tiles side by
-//              side hold a row (scan_wave_kernel keeps its state as the next
-//              product's operand that way).  A last block of 16 columns
+//              side hold a row, so a scan that keeps its state in
+//              accumulator tiles could feed it to the next product without
+//              moving data between lanes.  A last block of 16 columns
 //              (D % 32 == 16) is 512 B: lane (g, i), columns 32 k + 4 g .. + 3.
 //              Same size as row-major.
 enum MatLayout { LAYOUT_ROWMAJOR = 0, LAYOUT_TILES = 1, LAYOUT_FRAG = 2 };
@@ -99,10 +100,6 @@ struct ScanArgs {
   float* compH;         // composite output H_w
 };
 hipError_t launch_scan(const ScanArgs& a, int io, int nt, int mode, hipStream_t s);
-// One wave per 16 state rows (bf16, gated SCAN_FWD / SCAN_REV, sequential or
-// chunk replay); launch_scan takes it whenever scan_wave_supported.
-bool scan_wave_supported(const ScanArgs& a, int io, int mode);
-hipError_t launch_scan_wave(const ScanArgs& a, int nt, int mode, hipStream_t s);
 
 // Token-stream product with a per-frame D x D matrix M, one wave per output
 // feature tile: out[n] = M tok[n] (trans = false) or M^T tok[n] (trans =
