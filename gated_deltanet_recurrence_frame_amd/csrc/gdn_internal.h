@@ -17,24 +17,15 @@ namespace gdn {
 //              accumulator layout, so a consumer in the same layout reads
 //              4 contiguous values per lane);
 //   fragments  (bf16 only) the bf16 MFMA operand order of 16-row blocks:
-//              element [R][C] at frag_index(R, C, D).  Rows 16 I .. + 15,
-//              columns 32 k .. + 31 form one contiguous 1 KB piece in which
-//              lane (g, i) holds row 16 I + i, columns 32 k + 4 g .. + 3
-//              and then 32 k + 16 + 4 g .. + 3 (8 values).  Inside a
-//              contraction block that order is free (both operands take it),
-//              and it is the order in which two accumulator tiles side by
-//              side hold a row, so a scan that keeps its state in
-//              accumulator tiles could feed it to the next product without
-//              moving data between lanes.  A last block of 16 columns
-//              (D % 32 == 16) is 512 B: lane (g, i), columns 32 k + 4 g .. + 3.
-//              Same size as row-major.
+//              element [R][C] at frag_index(R, C, D), so that the 64 lanes
+//              of a wave reading rows 16 I .. + 15, columns 32 k .. + 31 as
+//              an operand (lane (g, i): row 16 I + i, columns 32 k + 8 g ..
+//              + 7) read one contiguous 1 KB piece (512 B for the last,
+//              16-column block when D % 32 == 16).  Same size as row-major.
 enum MatLayout { LAYOUT_ROWMAJOR = 0, LAYOUT_TILES = 1, LAYOUT_FRAG = 2 };
 __host__ __device__ inline long frag_index(int R, int C, int D) {
-  const int kb = C >> 5, c = C & 31;
-  const long base = (long)(R >> 4) * 16 * D + kb * 512;
-  const int lane = 16 * ((c & 15) >> 2) + (R & 15);
-  if (kb * 32 + 32 <= D) return base + lane * 8 + (c & 3) + 4 * (c >> 4);
-  return base + lane * 4 + (c & 3);
+  return (long)(R >> 4) * 16 * D + (C >> 5) * 512 + ((((C & 31) >> 3) << 4) + (R & 15)) * 8 +
+         (C & 7);
 }
 
 // Token contraction C_r = scale_r X_r^T diag(w) Y per (b, t, h) frame.

@@ -121,17 +121,18 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     B.gm = gbase[(long)t * gstride];
     if constexpr (BF) {
       // this wave's 16-row block of A_t in the fragment layout: block kb is
-      // 64 lanes x 8 elements (x 4 for a last block of 16 columns, whose
-      // other 4 operand elements are zero, as are the staged rows' there).
+      // 64 lanes x 8 elements (fewer lanes' worth for a last block of 16
+      // columns).  Unconditional loads: a branch around a load would cost
+      // the compiler its count of loads in flight and drain the ring every
+      // frame.  Lanes whose columns run past D re-read another lane's 8
+      // elements of the block (finite); the staged-row operand is zero
+      // there, so they add exact zeros.
       const E* Af = Ab + t * DD + ct * 16 * D;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        if (kb * 32 + 32 <= D) {
-          B.af[kb] = load_bf16x8(Af + kb * 512 + lane * 8);
-        } else {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(Af + kb * 512 + lane * 4);
-          B.af[kb] = __builtin_bit_cast(bf16x8, u32x4{v[0], v[1], 0u, 0u});
-        }
+        const int kw = min(4, (D - kb * 32) / 8);   // 8-column groups inside D
+        const int gc = g < kw ? g : kw - 1;
+        B.af[kb] = load_bf16x8(Af + kb * 512 + (16 * gc + li) * 8);
       }
       B.u = *reinterpret_cast<const u32x2*>(Ub + t * DD + ((rb * NT + ct) * 64 + lane) * 4);
     } else {
@@ -179,12 +180,9 @@ __global__ __launch_bounds__(64 * NT) void scan_kernel(ScanArgs a) {
     if constexpr (BF) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        // columns 32 kb + 4 g .. + 3, then 32 kb + 16 + 4 g .. + 3: the
-        // contraction order of the fragment layout
-        const int k0 = kb * 32 + 4 * g, k1 = k0 + 16;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(zrow + k0);
-        const u32x2 hi = k1 < D ? *reinterpret_cast<const u32x2*>(zrow + k1) : u32x2{0u, 0u};
-        p = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), B.af[kb], p);
+        const int k = kb * 32 + 8 * g;
+        const bf16x8 zf = (k < D) ? load_bf16x8(zrow + k) : zero_bf16x8();
+        p = mfma_bf16(zf, B.af[kb], p);
       }
     } else {
 #pragma unroll

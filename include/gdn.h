@@ -163,10 +163,8 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int op, size_t* bytes);
  * (0 for a zero row), which the output pass forms anyway and the backward
  * reads instead of a pass over q.  fp32 A_t is row-major;
  * bf16 A_t is in the MFMA operand order of the scan: element [r][c] of a
- * frame's A_t at (r / 16) 16 Dk + (c / 32) 512 + L 8 + c % 4 + 4 ((c % 32)
- * / 16) with lane L = 16 ((c % 16) / 4) + r % 16, except in a last block of
- * 16 columns (Dk % 32 == 16, c >= Dk - 16), where it sits at (r / 16) 16 Dk
- * + (c / 32) 512 + L 4 + c % 4.  GDN_ERR_UNSUPPORTED for GDN_ALGO_TOKEN and
+ * frame's A_t at (r / 16) 16 Dk + (c / 32) 512 + (16 ((c % 32) / 8) +
+ * r % 16) 8 + c % 8.  GDN_ERR_UNSUPPORTED for GDN_ALGO_TOKEN and
  * GDN_ALGO_DIRECT, which keep neither. */
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes);
 

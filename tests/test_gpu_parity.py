@@ -646,16 +646,10 @@ def test_minute_config_other_seeds(seed):
 
 def _frag_to_rowmajor(a, D):
     """Undo the bf16 operand order of saved A_t (documented in include/gdn.h):
-    in block b = c / 32 of rows 16 (r / 16) .. + 15, element [r][c] belongs
-    to lane L = 16 ((c % 16) / 4) + r % 16; a full block of 32 columns keeps
-    8 values a lane, columns 32 b + 4 g .. + 3 then 32 b + 16 + 4 g .. + 3
-    (g = L / 16), a last block of 16 columns 4 values a lane."""
+    element [r][c] of a frame sits at (r / 16) 16 D + (c / 32) 512 +
+    (16 ((c % 32) / 8) + r % 16) 8 + c % 8."""
     r, c = np.meshgrid(np.arange(D), np.arange(D), indexing="ij")
-    base = (r // 16) * 16 * D + (c // 32) * 512
-    lane = 16 * ((c % 16) // 4) + r % 16
-    full = (c // 32) * 32 + 32 <= D
-    idx = np.where(full, base + lane * 8 + c % 4 + 4 * ((c % 32) // 16), base + lane * 4 + c % 4)
-    assert np.array_equal(np.sort(idx.ravel()), np.arange(D * D))   # a permutation
+    idx = (r // 16) * 16 * D + (c // 32) * 512 + (16 * ((c % 32) // 8) + r % 16) * 8 + c % 8
     return a[..., idx]
 
 
