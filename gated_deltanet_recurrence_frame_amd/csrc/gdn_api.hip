@@ -438,13 +438,20 @@ gdn_status run_forward(const Shape& s, const void* q, const void* k, const void*
     st = record(events, 1, stream);
     if (st != GDN_OK) return st;
     if (direct_parts(s) >= 2) {
-      // one frame of many tokens: its tokens in parts, then their sum
+      // one frame of many tokens: every part's update, then their sum with
+      // the outputs of each row block's features
       da.part = reinterpret_cast<float*>(ws + 3 * s.mat);
       da.P = (int)direct_parts(s);
-      st = hip_status(launch_direct_split(da, (int)(s.D / 16), stream));
-    } else {
-      st = hip_status(launch_direct(da, (int)(s.D / 16), stream));
+      da.q = q; da.o = o;
+      st = hip_status(launch_direct_parts(da, (int)(s.D / 16), stream));
+      if (st != GDN_OK) return st;
+      st = record(events, 2, stream);
+      if (st != GDN_OK) return st;
+      st = hip_status(launch_direct_out(da, (int)(s.D / 16), stream));
+      if (st != GDN_OK) return st;
+      return record(events, 3, stream);
     }
+    st = hip_status(launch_direct(da, (int)(s.D / 16), stream));
     if (st != GDN_OK) return st;
     st = record(events, 2, stream);
     if (st != GDN_OK) return st;

@@ -17,6 +17,8 @@ namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -95,6 +97,18 @@ __device__ __forceinline__ bf16x8 lds_col_frag_bf16(const uint16_t* M, int ld, i
   i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
   i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
+}
+
+// Four rows of a column of a row-major bf16 matrix M in LDS (row stride ld
+// elements), with the gfx950 transposing read: lane (g, i) receives
+// M[r0 + j][c0 + i], j = 0..3, where r0 may differ between the four groups
+// of 16 lanes.  Lane m of a group addresses row r0 + m / 4, columns
+// c0 + 4 (m % 4) .. + 3.  Needs (ld * 2) and (c0 * 2) to be multiples of 8
+// bytes.
+__device__ __forceinline__ i16x4 lds_rows4_tr(const uint16_t* M, int ld, int r0, int c0) {
+  const int m = lane_id() & 15;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(M + (r0 + (m >> 2)) * ld + c0 + 4 * (m & 3)));
 }
 
 // Sum over the 16 lanes of v's DPP row (lanes 16r .. 16r + 15), returned to

@@ -199,13 +199,17 @@ struct DirectArgs {
   int B, H, T, N;
   float* part;          // token-split launches: [B, H, D/16, P] x D/16 x 256 fp32 partials
   int P;                // token parts (split launches)
+  const void* q;        // split launches: [B, N, H, D] queries (T == 1)
+  void* o;              // split launches: [B, N, H, D] outputs
 };
 hipError_t launch_direct(const DirectArgs& a, int nt, hipStream_t s);
 // One frame (T == 1) with its tokens split over a.P parts of kDirectPartTokens:
-// every (head, row block, part) forms its part's update in a.part, then a
-// fixed-order sum gives S_1 = gamma S_0 + sum of the parts (emit, zT).
+// launch_direct_parts has every (head, part) form its part's update of every
+// row block in a.part; launch_direct_out then sums them in a fixed order,
+// S_1 = gamma S_0 + sum of the parts (zT), and forms the outputs o from q.
 constexpr int kDirectPartTokens = 128;
-hipError_t launch_direct_split(const DirectArgs& a, int nt, hipStream_t s);
+hipError_t launch_direct_parts(const DirectArgs& a, int nt, hipStream_t s);
+hipError_t launch_direct_out(const DirectArgs& a, int nt, hipStream_t s);
 
 // Token-space forward (frames with few tokens): one workgroup per (b, h),
 // chunks of F frames of N tokens, F N <= TokCfg<io>::CP.

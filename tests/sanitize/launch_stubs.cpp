@@ -183,11 +183,28 @@ hipError_t launch_direct(const DirectArgs& a, int nt, hipStream_t) {
   need(a.zT, (int64_t)a.B * a.H * D * D * 4, "direct zT");
   return hipSuccess;
 }
-hipError_t launch_direct_split(const DirectArgs& a, int nt, hipStream_t s) {
+hipError_t launch_direct_parts(const DirectArgs& a, int nt, hipStream_t) {
+  ++g_calls;
   if (a.T != 1 || !a.part || a.P < 1) return hipErrorInvalidValue;
-  const int64_t D = 16 * nt;
+  const int64_t D = 16 * nt, tok = (int64_t)a.B * a.N * a.H * D * 2;
+  need(a.k, tok, "direct parts k");
+  need(a.v, tok, "direct parts v");
+  need(a.beta, (int64_t)a.B * a.N * a.H * 4, "direct parts beta");
+  need(a.z0, (int64_t)a.B * a.H * D * D * 4, "direct parts z0");
   need(a.part, (int64_t)a.B * a.H * a.P * D * D * 4, "direct parts");
-  return launch_direct(a, nt, s);   // the same inputs, state and emitted S_1
+  return hipSuccess;
+}
+hipError_t launch_direct_out(const DirectArgs& a, int nt, hipStream_t) {
+  ++g_calls;
+  if (a.T != 1 || !a.part || a.P < 1 || !a.q || !a.o) return hipErrorInvalidValue;
+  const int64_t D = 16 * nt, tok = (int64_t)a.B * a.N * a.H * D * 2;
+  need(a.q, tok, "direct out q");
+  need(a.o, tok, "direct out o");
+  need(a.gamma, (int64_t)a.B * a.H * 4, "direct out gamma");
+  need(a.z0, (int64_t)a.B * a.H * D * D * 4, "direct out z0");
+  need(a.zT, (int64_t)a.B * a.H * D * D * 4, "direct out zT");
+  need(a.part, (int64_t)a.B * a.H * a.P * D * D * 4, "direct out parts");
+  return hipSuccess;
 }
 hipError_t launch_token(const TokArgs& a, int io, int nt, bool, hipStream_t) {
   ++g_calls;
