@@ -143,6 +143,12 @@ def cpu_baseline(inp, budget_s):
         oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["beta"], N, x["d_o"])
 
     threads = _blas_threads()
+    # dense-equivalent FLOPs per token of one layer (the GPU legs' count)
+    H, D = SHAPE["H"], SHAPE["D"]
+    fwd_ft = H * (3 * 2 * D * D * N + 2 * D ** 3) / N
+    flops_per_token = {"forward_minute": fwd_ft, "forward_minute_1thread": fwd_ft,
+                       "forward_short": fwd_ft, "stream_minute": fwd_ft,
+                       "train_minute": H * (8 * 2 * D * D * N + 3 * 2 * D ** 3) / N}
     legs = {}
     share = {"forward_minute": 0.4, "forward_minute_1thread": 0.15, "forward_short": 0.1,
              "stream_minute": 0.15, "train_minute": 0.2}
@@ -158,11 +164,14 @@ def cpu_baseline(inp, budget_s):
                 v, done, secs = _oracle_heads(inp, fn, budget_s * share[name], frames)
         else:
             v, done, secs = _oracle_heads(inp, fn, budget_s * share[name], frames)
-        legs[name] = {"tokens_per_s": round(v, 1), "head_passes": done,
-                      "seconds": round(secs, 2), "threads": 1 if one else threads}
+        legs[name] = {"tokens_per_s": round(v, 1),
+                      "gflops": round(v * flops_per_token[name] / 1e9, 2),
+                      "head_passes": done, "seconds": round(secs, 2),
+                      "threads": 1 if one else threads}
     main = legs["forward_minute"]
     return {"value": main["tokens_per_s"], "unit": "tokens/s", "cores": threads,
             "nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "kind": "oracle",
             "sample": "float64 oracle (numpy, %d BLAS threads) forward on %d whole heads of the "
                       "1-min shape (121 x 880 tokens each, the 20 heads in turn), %.1f s, scaled "
