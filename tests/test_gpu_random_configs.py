@@ -89,3 +89,52 @@ def test_random_configuration(i):
     print("rel_l2", {k: "%.2e" % v for k, v in errs.items()})
     for k, v in errs.items():
         assert np.isfinite(v) and v <= tol, (k, v, c)
+
+
+NSTEPS = 24
+
+
+def draw_chain(i):
+    rng = np.random.default_rng(8000 + i)
+    io = "bf16" if rng.random() < 0.8 else "fp32"
+    D = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    B, H, T = int(rng.integers(1, 4)), int(rng.integers(1, 9)), int(rng.integers(1, 7))
+    N = int(rng.choice([1, 5, 64, 127, 128, 129, 255, 256, 257, 500, 880, 1000]))
+    algo = str(rng.choice(["auto", "frame"] + (["direct"] if io == "bf16" else [])))
+    return dict(io=io, B=B, H=H, T=T, N=N, D=D, algo=algo, nq=bool(rng.random() < 0.3),
+                gl=bool(rng.random() < 0.3), state=bool(rng.random() < 0.7),
+                plan=bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("i", range(NSTEPS))
+def test_random_step_chain(i):
+    # T gdn_step calls (through a StepPlan or the one-call helper), the state
+    # carried in place, against one oracle forward over the T frames
+    c = draw_chain(i)
+    print("chain", i, c)
+    B, H, T, N, D = c["B"], c["H"], c["T"], c["N"], c["D"]
+    inp = gin.make_inputs(B=B, H=H, T=T, N=N, D=D, io=c["io"], gamma="uniform", seed=8000 + i,
+                          with_state=c["state"], raw=c["nq"])
+    d = {k: v.to(DEV).contiguous() for k, v in inp.items()}
+    st = d["state"].clone() if c["state"] else torch.zeros(B, H, D, D, device=DEV)
+    plan = gb.StepPlan(B, H, N, D, c["io"], torch.device(DEV), algorithm=c["algo"],
+                       flags=gb.flags_of(c["nq"], c["gl"])) if c["plan"] else None
+    outs = []
+    for t in range(T):
+        w = {k: d[k][:, t * N:(t + 1) * N].contiguous() for k in ("q", "k", "v", "beta")}
+        g = d["gamma"][:, t:t + 1].contiguous()
+        if plan is not None:
+            outs.append(plan(w["q"], w["k"], w["v"], g, w["beta"], st).clone())
+        else:
+            outs.append(gb.step(w["q"], w["k"], w["v"], g, w["beta"], st, algorithm=c["algo"],
+                                normalize_qk=c["nq"], gate_logits=c["gl"]))
+    torch.cuda.synchronize()
+    f64 = gin.as_f64
+    ro, rs = oracle.forward(*(f64(inp[k]) for k in ("q", "k", "v", "gamma", "beta")), N,
+                            state_in=f64(inp["state"]) if c["state"] else None,
+                            normalize_qk=c["nq"], gate_logits=c["gl"])
+    tol = 2e-2 if c["io"] == "bf16" else 1e-5
+    eo = rel_l2(f64(torch.cat(outs, dim=1).cpu()), ro)
+    es = rel_l2(f64(st.cpu()), rs)
+    print("rel_l2 o %.2e state %.2e" % (eo, es))
+    assert eo <= tol and es <= tol, (eo, es, c)
