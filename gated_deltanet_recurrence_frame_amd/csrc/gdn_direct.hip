@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * NT) void direct_kernel(DirectArgs a) {
 // O[n][rows] = S_1[rows] q_n: the rounded rows of S_1 are the left operand,
 // the query rows the right one, read straight from memory as 16-byte
 // pieces (8-byte pieces in the tiles' feature order made every load touch
-// 16 lines for 32 bytes each, and the kernel three times slower).  Each
+// 16 lines for 32 bytes each, and the kernel about a third slower).  Each
 // lane stores 4 contiguous output features of one token.
 template <int NT>
 __global__ __launch_bounds__(64 * NT) void direct_part_kernel(DirectArgs a) {
