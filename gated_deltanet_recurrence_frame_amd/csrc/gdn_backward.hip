@@ -189,13 +189,16 @@ __global__ __launch_bounds__(256) void dm_kernel(DmArgs a) {
 // LDS and stored one chunk later as contiguous 16-byte pieces of token
 // rows; dbeta sums the per-feature-tile partial dot products in a fixed
 // order (deterministic, no atomics).
-// With normalised keys (CHAIN, bf16) the pass reads the raw key rows: each
-// wave sums the squares of the key fragments it loads (every wave reads all
-// of its head's features of a token), so it has |k| per token; its products
-// with k (per-token columns) and k itself are scaled by 1 / |k| (0 for a zero
-// row), and dK^ goes through the normalisation's chain rule before it is
-// stored, dk = (dk^ - k^ (k^ . dk^)) / |k|, the dot summed over the feature
-// tiles in a fixed order.
+// With normalised keys (CHAIN, bf16) the pass reads the raw key rows: the
+// thread that commits a 16-byte piece of a key row to LDS also stages the sum
+// of its eight squares, and every wave adds its tokens' piece sums in a fixed
+// order, so it has |k| per token without a K K^T product of its own; its
+// products with k (per-token columns) and k itself are scaled by
+// iv = 1 / |k| (0 for a zero row).  The normalisation's chain rule,
+//   dk = (dk^ - k^ (k^ . dk^)) iv = g - k (iv (k^ . g)),  g = iv dk^,
+// takes g from the compute step (iv folds into its per-token factor), staged
+// in bf16 like dV, and k^ . g summed over the feature tiles in a fixed order;
+// the store then spends one FMA per element.
 // Registers bound the shape: at 14 waves per CU a wave has 128 VGPRs, of
 // which its three matrices take 48; chunks of 16 tokens (pairs) two deep
 // fit without spills (at D = 112 the whole backward went from 1.17 to
@@ -239,8 +242,10 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   __shared__ float bstage[2][NB];
   __shared__ float red[2][HPW][NT][CT];                               // dbeta partials
   static_assert(!CHAIN || BF, "the fused chain rule is for bf16");
-  __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];                  // k^ . dk^ partials
+  __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];                  // k^ . g partials
   __shared__ float istage[CHAIN ? 2 : 1][NB];                         // 1 / |k| per token, head
+  constexpr int KP = D / 8;                                            // key pieces per head row
+  __shared__ float ksq[CHAIN ? 2 : 1][CHAIN ? CT * PR : 1];            // squares per key piece
 
   const int HG = a.H / HPW;
   const int total = a.B * a.T * HG;
@@ -410,6 +415,18 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
       const int p = tid + NTH * j;
       const int m = p / (CT * PR), r = p % (CT * PR);
       *reinterpret_cast<u32x4*>(st + (m * CT + r / PR) * LDR + (r % PR) * (16 / ES)) = R.v[j];
+      if constexpr (CHAIN) {
+        if (m == 0) {
+          float q = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = __uint_as_float(R.v[j][e] << 16);
+            const float x1 = __uint_as_float(R.v[j][e] & 0xffff0000u);
+            q += x0 * x0 + x1 * x1;
+          }
+          ksq[c & 1][r] = q;
+        }
+      }
     }
     // tokens past the frame's end get gate 0 (their rows are re-read copies)
     if (tid < NB) bstage[c & 1][tid] = c * CT + tid / HPW < N ? R.bt : 0.f;
@@ -448,7 +465,6 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
     for (int tt = 0; tt < CT / 16; ++tt) {
       const int trow = tt * 16 + li;
       f32x4 ay = zero4(), az = zero4(), aw = zero4();
-      f32x4 gram = zero4();   // CHAIN: K K^T of the tile's 16 tokens (its diagonal: |k|^2)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if constexpr (BF) {
@@ -462,7 +478,6 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
           ay = mfma_bf16(mG[kb], kf, ay);
           az = mfma_bf16(mGT[kb], vf, az);
           aw = mfma_bf16(mW[kb], kf, aw);
-          if constexpr (CHAIN) gram = mfma_bf16(kf, kf, gram);
           // one block's fragments live at a time (registers)
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -475,36 +490,40 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
         }
       }
       const float bt = bs[trow * HPW + hp];
-      f32x4 kv = load4(ks + trow * LDR);
+      float iv = 1.f;   // CHAIN: 1 / |k| of token trow (the staged k row is raw)
+      const f32x4 kv = load4(ks + trow * LDR);
       const f32x4 vv = load4(vs + trow * LDR);
       if constexpr (CHAIN) {
-        // |k|^2 of token li: the diagonal entry (li, li), in lane (li / 4, li)
-        const int rr = li & 3;
-        const float dg = rr == 0 ? gram[0] : rr == 1 ? gram[1] : rr == 2 ? gram[2] : gram[3];
-        const float iv = inv_norm(__shfl(dg, ((li >> 2) << 4) | li));
+        // |k|^2 of token trow: lane group g adds pieces g, g + 4, ... of the
+        // head's row, then the four groups' sums (the same order in every lane)
+        const float* kq = ksq[c & 1] + trow * PR + hp * KP;
+        float sq = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ay[r] *= iv;
-          aw[r] *= iv;
-          kv[r] *= iv;
-        }
+        for (int q = 0; q < (KP + 3) / 4; ++q)
+          if (g + 4 * q < KP) sq += kq[g + 4 * q];
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        iv = inv_norm(sq);
         if (ft == 0 && g == 0) istage[c & 1][trow * HPW + hp] = iv;
       }
+      // per-token factors: ay, aw and k carry iv under CHAIN (k^ = iv k), and
+      // dK^ = s bt (az - w) is formed as g = iv dK^ there
+      const float sy = s * iv, hk = 0.5f * s * iv, sk = s * bt * iv;
       f32x4 dvv, dkv;
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float y = s * ay[r];          // (G k^)_f
-        const float w = s * aw[r];          // (W k^)_f
+        const float y = sy * ay[r];         // (G k^)_f
+        const float w = sy * aw[r];         // (W k^)_f
         dvv[r] = bt * y;
-        dkv[r] = s * bt * (az[r] - w);
-        part += vv[r] * y - 0.5f * s * kv[r] * w;
+        dkv[r] = sk * (az[r] - w);
+        part += vv[r] * y - hk * kv[r] * w;
       }
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       if (g == 0) red[c & 1][hp][ft][trow] = part;
       if constexpr (CHAIN) {
-        float cp = kv[0] * dkv[0] + kv[1] * dkv[1] + kv[2] * dkv[2] + kv[3] * dkv[3];
+        float cp = iv * (kv[0] * dkv[0] + kv[1] * dkv[1] + kv[2] * dkv[2] + kv[3] * dkv[3]);
         cp += __shfl_xor(cp, 16);
         cp += __shfl_xor(cp, 32);
         if (g == 0) cred[c & 1][hp][ft][trow] = cp;
@@ -526,21 +545,20 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
       u32x4 v = *reinterpret_cast<const u32x4*>(src + (m * CT + row) * LDR + pc * (16 / ES));
       if constexpr (CHAIN) {
         if (m == 0) {
-          // dk = (dk^ - k^ (k^ . dk^)) / |k| on this piece of head hm's row
+          // dk = g - k (iv (k^ . g)) on this piece of head hm's row (k raw)
           const int hm = pc / (D / 8);
           float dot = 0.f;
 #pragma unroll
           for (int f = 0; f < NT; ++f) dot += cred[c & 1][hm][f][row];
-          const float iv = istage[c & 1][row * HPW + hm];
+          const float cf = istage[c & 1][row * HPW + hm] * dot;
           const u32x4 kx = *reinterpret_cast<const u32x4*>(stage(c & 1) + row * LDR + pc * 8);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            // the staged row is raw: k^ = k / |k|
             const float g0 = __uint_as_float(v[e] << 16), g1 = __uint_as_float(v[e] & 0xffff0000u);
-            const float k0 = __uint_as_float(kx[e] << 16) * iv;
-            const float k1 = __uint_as_float(kx[e] & 0xffff0000u) * iv;
-            v[e] = (uint32_t)f32_to_bf16_bits((g0 - k0 * dot) * iv) |
-                   ((uint32_t)f32_to_bf16_bits((g1 - k1 * dot) * iv) << 16);
+            const float k0 = __uint_as_float(kx[e] << 16);
+            const float k1 = __uint_as_float(kx[e] & 0xffff0000u);
+            const f32x2 d = {g0 - k0 * cf, g1 - k1 * cf};
+            v[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));
           }
         }
       }
