@@ -191,14 +191,16 @@ def test_backward_prologue(io, flags, use_saved):
     check_backward(inp, 100, io, nq, gl, use_saved)
 
 
-@pytest.mark.parametrize("B,H,D", [(1, 4, 112), (1, 3, 48), (1, 2, 128), (2, 2, 16)])
+@pytest.mark.parametrize("B,H,D", [(1, 4, 112), (1, 3, 48), (1, 2, 128), (2, 2, 16),
+                                   (1, 5, 32), (1, 2, 64), (1, 4, 80), (1, 1, 96)])
 @pytest.mark.parametrize("use_saved", [False, True])
 def test_backward_prologue_fused_chain_rule(B, H, D, use_saved):
     # bf16 with enough frames for the one-pass dO kernel (256 or more
     # (frame, head group) items): dq and dk leave the token passes already
     # through the normalisation's chain rule (head pairs for even H, single
-    # heads for odd H, a last 16-column block at D = 48 and D = 16, two
-    # sequences)
+    # heads for odd H, a last 16-column block at D = 48, 80, 112 and 16, two
+    # sequences; every head size, so that the key-norm sums' lane split over
+    # D / 8 pieces meets each remainder)
     T = 260 // (B * (H // 2 if H % 2 == 0 else H)) + 1
     inp = gin.make_inputs(B=B, H=H, T=T, N=70, D=D, io="bf16", seed=67, with_do=True,
                           with_dstate=True, with_state=True, raw=True)
