@@ -644,6 +644,31 @@ def test_minute_config_other_seeds(seed):
     check_grads(gr, ref, N, "bf16")
 
 
+def test_train_minute_prologue_all_heads():
+    # the one-minute shape through the block's prologue as the bench's
+    # prologue leg launches it (saved buffer, normalisation and gate logits
+    # fused, the one-pass backward that takes dq and dk through the
+    # normalisation's chain rule), on raw rows (per-row factors exp(N(0, 1)))
+    # and gate logits: forward and every gradient, all 20 heads, per-block bars
+    inp = gin.make_config("minute", seed=3, with_do=True, raw=True)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    N = 880
+    plan = gb.ForwardPlan(1, 20, 121, N, 112, "bf16", torch.device(DEV),
+                          flags=gb.flags_of(True, True), saved=True)
+    o, st = plan(d["q"], d["k"], d["v"], d["gamma"], d["beta"])
+    gr = gb.backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], N, d["d_o"],
+                     saved=plan.saved, normalize_qk=True, gate_logits=True)
+    torch.cuda.synchronize()
+    f = {k: f64(inp[k]) for k in ("q", "k", "v", "gamma", "beta", "d_o")}
+    flags = dict(normalize_qk=True, gate_logits=True)
+    ro, rs = oracle.forward(f["q"], f["k"], f["v"], f["gamma"], f["beta"], N, **flags)
+    print("minute prologue, 20 heads:")
+    check_blocks("o", f64(o.cpu()), ro, N, TOL["bf16"])
+    check_blocks("state", f64(st.cpu()), rs, N, TOL["bf16"])
+    ref = oracle.backward(f["q"], f["k"], f["v"], f["gamma"], f["beta"], N, f["d_o"], **flags)
+    check_grads(gr, ref, N, "bf16")
+
+
 def _frag_to_rowmajor(a, D):
     """Undo the bf16 operand order of saved A_t (documented in include/gdn.h):
     element [r][c] of a frame sits at (r / 16) 16 D + (c / 32) 512 +
