@@ -242,7 +242,9 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
   __shared__ float bstage[2][NB];
   __shared__ float red[2][HPW][NT][CT];                               // dbeta partials
   static_assert(!CHAIN || BF, "the fused chain rule is for bf16");
-  __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];                  // k^ . g partials
+  // k^ . g partials per token, the tiles' side by side (two 16-byte reads)
+  __shared__ __attribute__((aligned(16))) float cred[CHAIN ? 2 : 1][HPW][CT][8];
+  static_assert(NT <= 8, "the partials' row holds eight tiles");
   __shared__ float istage[CHAIN ? 2 : 1][NB];                         // 1 / |k| per token, head
   constexpr int KP = D / 8;                                            // key pieces per head row
   __shared__ float ksq[CHAIN ? 2 : 1][CHAIN ? CT * PR : 1];            // squares per key piece
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
         float cp = iv * (kv[0] * dkv[0] + kv[1] * dkv[1] + kv[2] * dkv[2] + kv[3] * dkv[3]);
         cp += __shfl_xor(cp, 16);
         cp += __shfl_xor(cp, 32);
-        if (g == 0) cred[c & 1][hp][ft][trow] = cp;
+        if (g == 0) cred[c & 1][hp][trow][ft] = cp;
       }
       put4(ob + trow * LDR + hp * D + ft * 16 + 4 * g, dkv);
       put4(ob + CT * LDR + trow * LDR + hp * D + ft * 16 + 4 * g, dvv);
@@ -547,9 +549,12 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void bwd_kv_kernel(BwdTokArgs a) 
         if (m == 0) {
           // dk = g - k (iv (k^ . g)) on this piece of head hm's row (k raw)
           const int hm = pc / (D / 8);
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(&cred[c & 1][hm][row][0]);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(&cred[c & 1][hm][row][4]);
+          const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
           float dot = 0.f;
 #pragma unroll
-          for (int f = 0; f < NT; ++f) dot += cred[c & 1][hm][f][row];
+          for (int f = 0; f < NT; ++f) dot += cv[f];
           const float cf = istage[c & 1][row * HPW + hm] * dot;
           const u32x4 kx = *reinterpret_cast<const u32x4*>(stage(c & 1) + row * LDR + pc * 8);
 #pragma unroll

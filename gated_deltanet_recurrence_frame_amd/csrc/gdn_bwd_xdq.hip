@@ -64,7 +64,10 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stage[2][STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t obuf[2][CT * LDO];
   // CHAIN: q^ . dq^ per (head, tile, token); 1 / |q| of each thread's piece
-  __shared__ float cred[CHAIN ? 2 : 1][HPW][NT][CT];
+  // (per token, the tiles' partials side by side: the store reads them as
+  // two 16-byte pieces)
+  __shared__ __attribute__((aligned(16))) float cred[CHAIN ? 2 : 1][HPW][CT][8];
+  static_assert(NT <= 8, "the partials' row holds eight tiles");
   __shared__ float istage[CHAIN ? 2 : 1][CHAIN ? NTH : 1];
 
   const int HG = a.H / HPW;
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
         part += bf16_bits_to_f32((uint16_t)(qp[1] >> 16)) * d[3];
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
-        if (g == 0) cred[c & 1][hp][ft][trow] = part;
+        if (g == 0) cred[c & 1][hp][trow][ft] = part;
       }
     }
   };
@@ -188,9 +191,12 @@ __global__ __launch_bounds__(64 * NT * HPW, 1) void xdq_kernel(XdqArgs a) {
     if constexpr (CHAIN) {
       // dq = (dq^ - q^ (q^ . dq^)) / |q| on this piece of head hm's row
       const int hm = ppc / (D / 8);
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(&cred[c & 1][hm][prow][0]);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(&cred[c & 1][hm][prow][4]);
+      const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
       float dot = 0.f;
 #pragma unroll
-      for (int f = 0; f < NT; ++f) dot += cred[c & 1][hm][f][prow];
+      for (int f = 0; f < NT; ++f) dot += cv[f];
       const float iv = istage[c & 1][tid];
       const u32x4 qv = *reinterpret_cast<const u32x4*>(&stage[c & 1][(CT + prow) * LDR + ppc * 8]);
 #pragma unroll
